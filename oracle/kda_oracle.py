@@ -1,0 +1,137 @@
+"""Python front end of the float64 KDA oracle (oracle/kda_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Imported by the tests, by the smoke check and by
+the benchmark's CPU-baseline leg; never by the GPU library.  It marshals
+numpy arrays into the C oracle and compiles that C file with gcc when no
+built copy is present.
+
+The C file's header states, with citations, what is computed: per token,
+fade S <- Diag(exp g) S, erase/write S <- S + beta k (v - S^T k)^T, then the
+read o = S^T q from the updated state.  Every function here takes and
+returns float64 arrays in the library's layouts:
+  q, k, g [B, T, H, dk];  v, o [B, T, H, dv];  beta [B, T, H];
+  S0, S_final [B, H, dk, dv]  (decode drops the T axis).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "kda_oracle.c")
+LIBRARY = os.path.join(HERE, "libkda_oracle.so")
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def compile_oracle(source: str = SOURCE, out: str = LIBRARY, extra=()) -> str:
+    """Build the oracle with gcc (IEEE double, no fast-math).  Returns the path."""
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", *extra,
+           "-o", tmp, source, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(_DP)
+
+
+def _c64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+class Oracle:
+    """Handle on one built copy of the C oracle."""
+
+    def __init__(self, lib_path: str = LIBRARY):
+        if lib_path == LIBRARY and (not os.path.exists(LIBRARY)
+                                    or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            compile_oracle()
+        self.path = lib_path
+        self.lib = ctypes.CDLL(lib_path)
+        i = ctypes.c_int
+        self.lib.kda_oracle_fwd.argtypes = [_DP] * 8 + [i] * 6
+        self.lib.kda_oracle_fwd.restype = i
+        self.lib.kda_oracle_decode.argtypes = [_DP] * 7 + [i] * 5
+        self.lib.kda_oracle_decode.restype = i
+        self.lib.kda_oracle_max_threads.argtypes = []
+        self.lib.kda_oracle_max_threads.restype = i
+
+    def max_threads(self) -> int:
+        return int(self.lib.kda_oracle_max_threads())
+
+    def fwd(self, q, k, v, g, beta, S0=None, *, want_state: bool = True,
+            nthreads: int = 0) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+        """Token-by-token forward.  Returns (o [B,T,H,dv], S_final [B,H,dk,dv] or None)."""
+        q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        assert k.shape == q.shape and g.shape == q.shape
+        assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+        if S0 is not None:
+            S0 = _c64(S0)
+            assert S0.shape == (B, H, dk, dv)
+        o = np.zeros((B, T, H, dv), np.float64)
+        Sf = np.zeros((B, H, dk, dv), np.float64) if want_state else None
+        rc = self.lib.kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(S0), _ptr(o), _ptr(Sf), B, T, H, dk, dv,
+                                     int(nthreads))
+        if rc != 0:
+            raise RuntimeError("kda_oracle_fwd failed")
+        return o, Sf
+
+    def decode_step(self, q, k, v, g, beta, S, *, nthreads: int = 0) -> np.ndarray:
+        """One token for every (b, h): S [B,H,dk,dv] float64 updated IN PLACE; returns o [B,H,dv]."""
+        q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+        assert isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
+        B, H, dk = q.shape
+        dv = v.shape[-1]
+        assert S.shape == (B, H, dk, dv)
+        o = np.zeros((B, H, dv), np.float64)
+        rc = self.lib.kda_oracle_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(S), _ptr(o), B, H, dk, dv, int(nthreads))
+        if rc != 0:
+            raise RuntimeError("kda_oracle_decode failed")
+        return o
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT
+
+
+def kda_fwd(q, k, v, g, beta, S0=None, **kw):
+    return default().fwd(q, k, v, g, beta, S0, **kw)
+
+
+def kda_decode_step(q, k, v, g, beta, S, **kw):
+    return default().decode_step(q, k, v, g, beta, S, **kw)
+
+
+def build_variant(source_text: str) -> Oracle:
+    """Compile a modified copy of the oracle source into a temporary library.
+
+    Used by the mutation tests, which plant mistakes into a copy of the oracle
+    on the CPU to show that the pins catch them.
+    """
+    d = tempfile.mkdtemp(prefix="kda_oracle_variant_")
+    src = os.path.join(d, "variant.c")
+    with open(src, "w") as f:
+        f.write(source_text)
+    lib = compile_oracle(src, os.path.join(d, "libvariant.so"))
+    return Oracle(lib)
