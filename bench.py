@@ -1,0 +1,253 @@
+"""Throughput of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step = one kda_chunk_fwd over the training-shape workload
+(B=4, H=32, T=16384, dk=dv=128, bf16 q/k/v/g/beta, fp32 state), inputs
+already resident in HBM.  `value` is tokens/s (B*T tokens per step, each
+token carrying all H heads).  The decode path is timed on its own workload
+(B=256 sequences x H=96, d=128, 64 consecutive steps) and reported under
+"decode" in GB/s.  Each carries a roofline object for its kernel, with the
+kernel's average duration measured by HIP events on the launch stream.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunk-fwd tokens/s + TFLOP/s (H=32,d=128,T=16K); decode GB/s vs roofline"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+CHUNK = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ algorithmic counts
+
+def fwd_bytes(B, T, H, dk, dv, s_qkv, s_g, s_o, s0: bool, sfinal: bool) -> int:
+    """Compulsory HBM bytes of one forward: read q, k, v, g, beta once, write o
+    once; the fp32 state is read (S0) and written (S_final) once when present."""
+    per_tok = s_qkv * (2 * dk + dv) + s_g * (dk + 1) + s_o * dv
+    return B * T * H * per_tok + (int(s0) + int(sfinal)) * 4 * B * H * dk * dv
+
+
+def fwd_flops(B, T, H, dk, dv, C=CHUNK) -> int:
+    """Algorithmic FLOP of the chunkwise form per token-head: three C x d x d
+    products (Gamma.Q S, Gamma.K S, K-bar^T U) = 6 dk dv; the four C x C x d
+    triangular products at their non-zero half = 2 C (dk + dv); the unit-lower
+    inverse ~ C^2 / 3."""
+    return B * T * H * (6 * dk * dv + 2 * C * (dk + dv) + (C * C) // 3)
+
+
+def decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) -> int:
+    """One decode step: fp32 state read + written, q, k, v, g, beta read, o written."""
+    return B * H * (8 * dk * dv + s_qkv * (2 * dk + dv) + s_g * (dk + 1) + s_o * dv)
+
+
+def kernel_source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
+DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
+
+
+def stored_traffic(kernel: str, sources) -> "dict | None":
+    """HBM bytes per launch from the committed counter runs, if the kernel
+    source is unchanged since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(sources):
+        return None
+    return rec
+
+
+# ------------------------------------------------------------------- timing
+
+def time_launches(fn, steps, warmup, stream):
+    """Wall time of `steps` back-to-back calls and the mean kernel duration
+    from HIP events recorded around each launch on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ker = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    return wall, ker
+
+
+def roofline(algo_bytes_per_launch, kernel_s, traffic_rec):
+    achieved = algo_bytes_per_launch / kernel_s / 1e9
+    traffic = None
+    if traffic_rec:
+        traffic = traffic_rec["hbm_bytes_per_launch"]
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+# --------------------------------------------------------------- workloads
+
+def bench_fwd(kda, steps, warmup):
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.TRAIN_BF16
+    log(f"[bench] generating {w.name} on the device")
+    d = gen_torch.fwd_inputs(w)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None, o=o, S_final=Sf)
+
+    log(f"[bench] chunk_fwd: {warmup} warmup + {steps} timed launches")
+    wall, ker = time_launches(step, steps, warmup, stream)
+    nbytes = fwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 4, s0=False, sfinal=True)
+    flops = fwd_flops(w.B, w.T, w.H, w.dk, w.dv)
+    ms = wall / steps * 1e3
+    tok_s = w.B * w.T / (wall / steps)
+    log(f"[bench] chunk_fwd {ms:.3f} ms/step (kernel {ker * 1e3:.3f} ms), {tok_s:.3e} tokens/s")
+    rf = roofline(nbytes, ker, stored_traffic("kda_chunk_fwd", CHUNK_SOURCES))
+    tflops = flops / (wall / steps) / 1e12
+    extra = {
+        "tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "algorithmic_flop_per_step": flops,
+        "algorithmic_bytes_per_step": nbytes,
+        "kernel_ms": round(ker * 1e3, 4),
+    }
+    return w, d, ms, tok_s, rf, extra
+
+
+def bench_decode(kda, reps):
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.DECODE_BF16
+    log(f"[bench] generating {w.name} on the device")
+    S = gen_torch.decode_initial_state(w)
+    xs = [gen_torch.decode_step_inputs(w, s) for s in range(w.steps)]
+    o = torch.empty((w.B, w.H, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    it = {"i": 0}
+
+    def one():
+        x = xs[it["i"] % w.steps]
+        it["i"] += 1
+        kda.kda_decode_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S, o=o)
+
+    log(f"[bench] decode: {w.steps} steps x {reps} repetitions")
+    wall, ker = time_launches(one, w.steps * reps, w.steps, stream)
+    per_step = decode_bytes(w.B, w.H, w.dk, w.dv, 2, 4, 4)
+    n = w.steps * reps
+    gbs = per_step * n / wall / 1e9
+    log(f"[bench] decode {wall / n * 1e3:.3f} ms/step (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
+    return {
+        "workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
+        "ms_per_step": round(wall / n * 1e3, 4), "steps": n,
+        "algorithmic_bytes_per_step": per_step,
+        "roofline": roofline(per_step, ker, stored_traffic("kda_decode_step", DECODE_SOURCES)),
+    }
+
+
+def cpu_baseline(w, d, batch=32):
+    """The float64 oracle on the same workload, every head over the full
+    sequence, on all host threads, `batch` heads per call (only the recurrence
+    is timed, not the copies to float64)."""
+    import numpy as np
+    import torch
+    from oracle import default
+    orc = default()
+    threads = orc.max_threads()
+    n_all = w.B * w.H
+    log(f"[bench] cpu baseline: oracle on {n_all} heads x {w.T} tokens, {threads} threads")
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    dt = 0.0
+    for i0 in range(0, n_all, batch):
+        heads = [(i // w.H, i % w.H) for i in range(i0, min(n_all, i0 + batch))]
+        x = {nm: f64(torch.stack([d[nm][b, :, h] for b, h in heads], dim=1).unsqueeze(0))
+             for nm in ("q", "k", "v", "g", "beta")}
+        t0 = time.perf_counter()
+        orc.fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], None, nthreads=threads)
+        dt += time.perf_counter() - t0
+        del x
+    tok_s = w.B * w.T / dt
+    log(f"[bench] cpu baseline: {dt:.2f} s -> {tok_s:.3e} tokens/s")
+    return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {n_all} heads x {w.T} tokens of {w.name} (the full step), float64 "
+                      f"token recurrence, {batch} heads per call, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the KDA path "
+              "runs one workload per GPU; multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_101_amd as kda
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kda.load_library()
+
+    w, d, ms, tok_s, rf, extra = bench_fwd(kda, args.steps, args.warmup)
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.dk, "dv": w.dv,
+                   "chunk": CHUNK, "tile": 16, "qkv": w.qkv, "gate": w.gate, "out": "f32",
+                   "state": "f32"},
+        **extra,
+        "roofline": rf,
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(kda, args.decode_reps)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, d)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,10 @@
+"""MI355X-native Kimi Delta Attention (KDA): a C-ABI library of HIP kernels
+for gfx950 (libkda.so, declared in include/kda.h) and its Python binding.
+
+    from gated_delta_rule_101_amd import kda_chunk_fwd, kda_decode_step
+"""
+
+from .kda import (  # noqa: F401
+    EXPORTS, KDA_BF16, KDA_ERR_INVALID_ARG, KDA_ERR_LAUNCH, KDA_ERR_UNSUPPORTED, KDA_F32, KDA_OK,
+    KdaError, kda_chunk_fwd, kda_decode_step, load_library, status_string,
+)

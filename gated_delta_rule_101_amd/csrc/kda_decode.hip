@@ -1,0 +1,150 @@
+// Single-token KDA decode for gfx950: one streaming pass over the fp32 state.
+//
+// One workgroup of 256 threads owns one (sequence, head) state S (dk x dv,
+// float32, dv contiguous).  Thread (row group rg, column group cg) holds
+// columns 4cg..4cg+3 of rows rg, rg + NRG, rg + 2 NRG, ...; a wave's two
+// halves read two adjacent full rows per 16-byte load, so every load and
+// store instruction moves whole 512-byte rows.  S is read once and written
+// once with non-temporal hints: the step is bound by HBM bandwidth.
+//
+// With D = Diag(exp g) (fade each key channel first, "Review A - Sequence
+// and depth", Free recall; "K3 Architecture Illustrated", FIG 21):
+//   p = S^T (alpha . k)          what the key retrieves from the faded state
+//   w = beta (v - p)             the correction the delta rule writes
+//   o = S^T (alpha . q) + (q.k) w   the read of the updated state
+//   S <- D S + k w^T
+// which is one token of the recurrence with a single read and write of S.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int NTHREADS = 256;
+
+template <int DK, int DV, bool QBF, bool GBF, bool OBF>
+__global__ void __launch_bounds__(NTHREADS)
+kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
+                  const typename Store<QBF>::type *__restrict__ k,
+                  const typename Store<QBF>::type *__restrict__ v,
+                  const typename Store<GBF>::type *__restrict__ g,
+                  const typename Store<GBF>::type *__restrict__ beta,
+                  float *__restrict__ S, typename Store<OBF>::type *__restrict__ o)
+{
+    typedef typename Store<QBF>::type QT;
+    typedef typename Store<OBF>::type OT;
+    constexpr int NCG = DV / 4;            // column groups of 4
+    constexpr int NRG = NTHREADS / NCG;    // row groups
+    constexpr int RPT = DK / NRG;          // rows per thread
+    static_assert(RPT * NRG == DK, "rows must split evenly");
+
+    __shared__ float s_ak[DK], s_aq[DK], s_k[DK], s_q[DK], s_alpha[DK];
+    __shared__ f32x4 s_p[NRG][NCG], s_r[NRG][NCG];
+    __shared__ float s_qk[NRG];
+
+    const int bh = blockIdx.x;
+    const int cg = threadIdx.x % NCG;
+    const int rg = threadIdx.x / NCG;
+    f32x4 *Sp = reinterpret_cast<f32x4 *>(S + (size_t)bh * DK * DV);
+
+    // issue the whole state slice first: it is the only large transfer
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&Sp[(rg + NRG * i) * NCG + cg]);
+
+    if (threadIdx.x < DK) {
+        const int c = threadIdx.x;
+        const float alpha = __expf(to_f32(g[(size_t)bh * DK + c]));
+        const float kc = to_f32(k[(size_t)bh * DK + c]);
+        const float qc = to_f32(q[(size_t)bh * DK + c]);
+        s_alpha[c] = alpha;
+        s_k[c] = kc;
+        s_q[c] = qc;
+        s_ak[c] = alpha * kc;
+        s_aq[c] = alpha * qc;
+    }
+    const float bt = to_f32(beta[bh]);
+    float vv[4];
+    {
+        const QT *vp = v + (size_t)bh * DV + 4 * cg;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) vv[c] = to_f32(vp[c]);
+    }
+    lds_barrier();
+
+    f32x4 p = {0.f, 0.f, 0.f, 0.f}, rd = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + NRG * i;
+        const float ak = s_ak[row], aq = s_aq[row];
+        p += s[i] * ak;
+        rd += s[i] * aq;
+        if (cg == 0) qk += s_q[row] * s_k[row];   // q.k over this thread's rows
+    }
+    s_p[rg][cg] = p;
+    s_r[rg][cg] = rd;
+    if (cg == 0) s_qk[rg] = qk;
+    lds_barrier();
+
+    f32x4 pt = {0.f, 0.f, 0.f, 0.f}, rt = {0.f, 0.f, 0.f, 0.f};
+    float qkt = 0.f;
+#pragma unroll
+    for (int x = 0; x < NRG; ++x) {
+        pt += s_p[x][cg];
+        rt += s_r[x][cg];
+        qkt += s_qk[x];
+    }
+    f32x4 w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = bt * (vv[c] - pt[c]);
+    if (rg == 0) {
+        OT *op = o + (size_t)bh * DV + 4 * cg;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) op[c] = from_f32<OT>(rt[c] + qkt * w[c]);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + NRG * i;
+        const float a = s_alpha[row], kc = s_k[row];
+        const f32x4 ns = a * s[i] + kc * w;
+        __builtin_nontemporal_store(ns, &Sp[row * NCG + cg]);
+    }
+}
+
+template <int DK, int DV, bool QBF, bool GBF, bool OBF>
+hipError_t launch(const DecodeArgs &a, hipStream_t stream)
+{
+    typedef typename Store<QBF>::type QT;
+    typedef typename Store<GBF>::type GT;
+    typedef typename Store<OBF>::type OT;
+    kda_decode_kernel<DK, DV, QBF, GBF, OBF><<<(unsigned)(a.B * a.H), NTHREADS, 0, stream>>>(
+        (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta,
+        a.S, (OT *)a.o);
+    return hipGetLastError();
+}
+
+template <int DK, int DV, bool QBF, bool GBF>
+hipError_t dispatch_out(const DecodeArgs &a, hipStream_t s)
+{
+    return a.out_bf16 ? launch<DK, DV, QBF, GBF, true>(a, s) : launch<DK, DV, QBF, GBF, false>(a, s);
+}
+
+template <int DK, int DV>
+hipError_t dispatch_dtypes(const DecodeArgs &a, hipStream_t s)
+{
+    if (a.qkv_bf16)
+        return a.gate_bf16 ? dispatch_out<DK, DV, true, true>(a, s) : dispatch_out<DK, DV, true, false>(a, s);
+    return a.gate_bf16 ? dispatch_out<DK, DV, false, true>(a, s) : dispatch_out<DK, DV, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    if (a.dk == 64) return a.dv == 64 ? dispatch_dtypes<64, 64>(a, stream) : dispatch_dtypes<64, 128>(a, stream);
+    return a.dv == 64 ? dispatch_dtypes<128, 64>(a, stream) : dispatch_dtypes<128, 128>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,236 @@
+// Device-side helpers shared by the KDA kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core fragments.  Every contraction in the library is built from
+// 16x16 output tiles of v_mfma_f32_16x16x32_bf16 (bf16 operands) or
+// v_mfma_f32_16x16x4_f32 (fp32 operands), plus the 16x16x16 shapes for the
+// 16-token triangular products.  For all of them lane l holds output rows
+// 4*(l/16)+i (i = 0..3) of column l%16, the A operand's row l%16 and the
+// B operand's column l%16; the items a lane contributes along k are paired
+// identically in A and B.  The kernels rely only on that pairing, never on
+// which logical k an item is: any permutation of k applied to both operands
+// leaves the product unchanged.  That lets an accumulator tile (rows
+// 4*(l/16)+i) serve directly as a B operand whose k index is the
+// accumulator's row, with the A operand read in the matching order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- scalars
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// round-to-nearest-even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// Storage element of a tensor: bfloat16 bit patterns or float32.
+template <bool BF> struct Store;
+template <> struct Store<true> { typedef uint16_t type; };
+template <> struct Store<false> { typedef float type; };
+
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16(x); }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// ------------------------------------------------- 8 consecutive elements
+
+// Raw bits of 8 consecutive storage elements, kept unconverted so a load can
+// be issued early (prefetch) and converted after other work.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    uint4 a;
+    __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void zero() { a = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void to_f32(float (&x)[8]) const {
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void to_f32(float (&x)[8]) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+
+// ------------------------------------------------------ MFMA precisions
+
+template <bool BF> struct Prec;
+
+// bf16 operands, fp32 accumulation.
+template <> struct Prec<true> {
+    typedef uint16_t elem;   // LDS element
+    typedef bf16x8 frag8;    // 8 k-items of a 16x16x32 operand
+    typedef i16x4 frag4;     // 4 k-items of a 16x16x16 operand
+
+    static __device__ __forceinline__ frag8 pack8(const float (&x)[8]) {
+        f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+        return __builtin_convertvector(v, bf16x8);
+    }
+    static __device__ __forceinline__ frag8 pack8(f32x4 lo, f32x4 hi) {
+        f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_convertvector(v, bf16x8);
+    }
+    static __device__ __forceinline__ frag4 pack4(f32x4 x) {
+        return __builtin_bit_cast(i16x4, __builtin_convertvector(x, bf16x4));
+    }
+    // 8 consecutive elements (16-byte aligned)
+    static __device__ __forceinline__ frag8 lds8(const elem *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+    // 4 consecutive elements at p0 then 4 at p1 (each 8-byte aligned)
+    static __device__ __forceinline__ frag8 lds4x2(const elem *p0, const elem *p1) {
+        const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
+        const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p1);
+        return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    static __device__ __forceinline__ frag4 lds4(const elem *p) { return *reinterpret_cast<const i16x4 *>(p); }
+    static __device__ __forceinline__ void unpack8(frag8 f, float (&x)[8]) {
+        const f32x8 v = __builtin_convertvector(f, f32x8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = v[i];
+    }
+    static __device__ __forceinline__ void sts8(elem *p, const float (&x)[8]) {
+        *reinterpret_cast<bf16x8 *>(p) = pack8(x);
+    }
+    static __device__ __forceinline__ elem cvt(float x) { return f32_to_bf16(x); }
+
+    // Two-term split x = hi + lo, both bfloat16 (about 16 significant bits together).
+    static constexpr bool SPLIT = true;
+    static __device__ __forceinline__ void split8(const float (&x)[8], frag8 &hi, frag8 &lo) {
+        const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+        hi = __builtin_convertvector(v, bf16x8);
+        lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
+    }
+    static __device__ __forceinline__ void split8(f32x4 a, f32x4 b, frag8 &hi, frag8 &lo) {
+        const f32x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        hi = __builtin_convertvector(v, bf16x8);
+        lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
+    }
+    static __device__ __forceinline__ void split4(f32x4 x, frag4 &hi, frag4 &lo) {
+        const bf16x4 h = __builtin_convertvector(x, bf16x4);
+        hi = __builtin_bit_cast(i16x4, h);
+        lo = __builtin_bit_cast(i16x4, __builtin_convertvector(x - __builtin_convertvector(h, f32x4), bf16x4));
+    }
+    static __device__ __forceinline__ void split1(float x, elem &hi, elem &lo) {
+        const __bf16 h = (__bf16)x;
+        hi = __builtin_bit_cast(uint16_t, h);
+        lo = f32_to_bf16(x - (float)h);
+    }
+    static __device__ __forceinline__ void split_sts8(elem *hi, elem *lo, const float (&x)[8]) {
+        frag8 h, l;
+        split8(x, h, l);
+        *reinterpret_cast<frag8 *>(hi) = h;
+        *reinterpret_cast<frag8 *>(lo) = l;
+    }
+    static __device__ __forceinline__ f32x4 mma32(frag8 a, frag8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(frag4 a, frag4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+};
+
+// fp32 operands and accumulation (K = 4 per instruction).
+template <> struct Prec<false> {
+    typedef float elem;
+    struct frag8 { f32x4 a, b; };  // items 0..3 and 4..7
+    typedef f32x4 frag4;
+
+    static __device__ __forceinline__ frag8 pack8(const float (&x)[8]) {
+        frag8 f;
+        f.a = f32x4{x[0], x[1], x[2], x[3]};
+        f.b = f32x4{x[4], x[5], x[6], x[7]};
+        return f;
+    }
+    static __device__ __forceinline__ frag8 pack8(f32x4 x, f32x4 y) { return frag8{x, y}; }
+    static __device__ __forceinline__ frag4 pack4(f32x4 x) { return x; }
+    static __device__ __forceinline__ frag8 lds8(const elem *p) {
+        return frag8{*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
+    }
+    static __device__ __forceinline__ frag8 lds4x2(const elem *p0, const elem *p1) {
+        return frag8{*reinterpret_cast<const f32x4 *>(p0), *reinterpret_cast<const f32x4 *>(p1)};
+    }
+    static __device__ __forceinline__ frag4 lds4(const elem *p) { return *reinterpret_cast<const f32x4 *>(p); }
+    static __device__ __forceinline__ void unpack8(frag8 f, float (&x)[8]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = f.a[i]; x[4 + i] = f.b[i]; }
+    }
+    static __device__ __forceinline__ void sts8(elem *p, const float (&x)[8]) {
+        *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+    static __device__ __forceinline__ elem cvt(float x) { return x; }
+
+    // float32 operands are already exact: the "high" part is the value, no low part.
+    static constexpr bool SPLIT = false;
+    static __device__ __forceinline__ void split8(const float (&x)[8], frag8 &hi, frag8 &) { hi = pack8(x); }
+    static __device__ __forceinline__ void split8(f32x4 x, f32x4 y, frag8 &hi, frag8 &) { hi = frag8{x, y}; }
+    static __device__ __forceinline__ void split4(f32x4 x, frag4 &hi, frag4 &) { hi = x; }
+    static __device__ __forceinline__ void split1(float x, elem &hi, elem &) { hi = x; }
+    static __device__ __forceinline__ void split_sts8(elem *hi, elem *, const float (&x)[8]) { sts8(hi, x); }
+    static __device__ __forceinline__ f32x4 mma32(frag8 a, frag8 b, f32x4 c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[i], b.a[i], c, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b[i], b.b[i], c, 0, 0, 0);
+        return c;
+    }
+    static __device__ __forceinline__ f32x4 mma16(frag4 a, frag4 b, f32x4 c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+        return c;
+    }
+};
+
+// ------------------------------------------------------------ wave tools
+
+// Lane i of each 16-lane row receives lane i-N of the same row; lanes i < N get 0.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row.
+__device__ __forceinline__ float row_inclusive_scan(float x) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+
+// Workgroup barrier that orders LDS traffic only: outstanding global loads
+// (prefetches) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads (other
+// lanes of the same wave read what one lane wrote).
+__device__ __forceinline__ void lds_wave_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+}  // namespace kda

@@ -1,0 +1,30 @@
+// Internal interface between the C ABI (kda_api.hip) and the kernel launchers.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkFwdArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float *S0;   // nullable
+    void *o;
+    float *S_final;    // nullable
+    int B, T, H, dk, dv;
+    bool qkv_bf16, gate_bf16, out_bf16;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *S;
+    void *o;
+    int B, H, dk, dv;
+    bool qkv_bf16, gate_bf16, out_bf16;
+};
+
+hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);
+hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kda

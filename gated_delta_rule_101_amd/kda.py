@@ -1,0 +1,166 @@
+"""Python binding of libkda.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(include/kda.h).  PyTorch supplies device memory and the current stream;
+nothing here computes any part of the layer, and there is no fallback: if
+the library is missing or a call fails, an exception is raised.
+
+    o, S_final = kda_chunk_fwd(q, k, v, g, beta, S0=None)
+    o = kda_decode_step(q, k, v, g, beta, S)        # S updated in place
+
+The output is float32 unless out_dtype=torch.bfloat16 is asked for: a
+bfloat16 output carries only 8 significant bits, which for heavy-tailed
+outputs is already a few percent of their RMS.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
+
+# Every symbol include/kda.h declares.
+EXPORTS = ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_abi_version")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libkda.so (built by gated_delta_rule_101_amd.build_lib); raise if absent."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m gated_delta_rule_101_amd.build_lib` "
+                          "(hipcc, gfx950) first")
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [vp] * 8 + [i] * 8 + [vp]
+    lib.kda_chunk_fwd.restype = i
+    lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 7 + [vp]
+    lib.kda_decode_step.restype = i
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = i
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream_handle(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _raise(status: int, what: str):
+    if status != KDA_OK:
+        raise KdaError(status, f"{what}: {status_string(status)}")
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
+                  output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                  S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  stream: Optional[torch.cuda.Stream] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA forward.  Shapes as in include/kda.h:
+    q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; S0 [B,H,dk,dv] float32 or None.
+    Returns (o [B,T,H,dv], S_final [B,H,dk,dv] float32 or None).  o is float32
+    unless out_dtype (or a passed `o`) says bfloat16.  `S_final` may be passed
+    (and may be S0 itself for an in-place continuation)."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch between q, k, v, g, beta")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != g.dtype:
+        raise TypeError("q, k, v share one dtype; g and beta share one dtype")
+    if S0 is not None and (S0.shape != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("S0 must be float32 [B,H,dk,dv]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, T, H, dv):
+        raise ValueError("o must be [B,T,H,dv]")
+    if S_final is None and output_final_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    dev = _check_dev(q, k, v, g, beta, S0, o, S_final)
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                           _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(g),
+                           _dtype_code(o), _stream_handle(stream, dev))
+    _raise(st, "kda_chunk_fwd")
+    return o, S_final
+
+
+def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor, *, o: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One KDA token for every (b, h): q, k, g [B,H,dk]; v [B,H,dv]; beta [B,H];
+    S [B,H,dk,dv] float32 updated IN PLACE.  Returns o [B,H,dv] (float32 unless
+    out_dtype or a passed `o` says bfloat16)."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, H, dv) or beta.shape != (B, H):
+        raise ValueError("shape mismatch between q, k, v, g, beta")
+    if S.shape != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != g.dtype:
+        raise TypeError("q, k, v share one dtype; g and beta share one dtype")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, H, dv):
+        raise ValueError("o must be [B,H,dv]")
+    dev = _check_dev(q, k, v, g, beta, S, o)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                             B, H, dk, dv, _dtype_code(q), _dtype_code(g), _dtype_code(o),
+                             _stream_handle(stream, dev))
+    _raise(st, "kda_decode_step")
+    return o

@@ -1,0 +1,131 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * The layer (one head, state S with dk rows = key channels and dv columns):
+ * for every token t, in order,
+ *     S <- Diag(exp(g_t)) S                       fade each key channel
+ *     S <- S + beta_t k_t (v_t - S^T k_t)^T       erase what k_t retrieves, write v_t
+ *     o_t = S^T q_t                               read from the updated state
+ * ("Review A - Sequence and depth", Free recall, the question on KDA's three
+ * operations; "K3 Architecture Illustrated", section "Combining KDA and MLA",
+ * FIG 21; the erase factor I - beta k k^T from the section "Under what
+ * conditions are RoPE, PaTH, and KDA related?").
+ *
+ * kda_chunk_fwd computes this over a whole sequence in the chunkwise form:
+ * sequential between 64-token chunks, parallel inside a chunk, with the
+ * output split into the inter-chunk term (Gamma . Q) S and the masked
+ * intra-chunk term A V~, and keys rescaled by 1/Gamma inside 16-token tiles
+ * ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the chunkwise diagram and the
+ * paragraphs on the 1/Gamma rescale and on g_min = -5).  The result is the
+ * token recurrence's, up to rounding.
+ *
+ * kda_decode_step advances every (sequence, head) state by one token in place
+ * (the fixed-size state of "Review A", Discriminating between mechanisms).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Tensor pointers are DEVICE pointers to contiguous row-major memory, each
+ *    aligned to 16 bytes.  The caller owns every buffer; the library
+ *    allocates nothing, keeps no state between calls and is reentrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; device-side faults surface at the caller's next
+ *    synchronisation.
+ *  - Arguments are validated on the host before any HIP call.  A non-OK
+ *    status means nothing was enqueued (KDA_ERR_LAUNCH: the launch itself
+ *    was rejected by the runtime).
+ *  - Preconditions that are NOT checked (the data stays on the device):
+ *    every g lies in [-5, 0] (the g_min = -5 floor that bounds 1/Gamma by e^80
+ *    inside a 16-token tile, "Kimi K3 - Lesson 3 of 14", the g_min
+ *    paragraphs); all inputs are finite.  Outside them results are undefined
+ *    (typically inf/NaN), never a fault.
+ *  - Keys and queries are used as given (no normalisation, no scaling).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_F32 = 0,   /* IEEE float32 */
+    KDA_BF16 = 1   /* bfloat16 (round-to-nearest-even when produced) */
+} kda_dtype_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,  /* NULL / misaligned / overlapping pointer, negative size, bad dtype */
+    KDA_ERR_UNSUPPORTED = 2,  /* valid but not provided: dk or dv outside the supported set */
+    KDA_ERR_LAUNCH = 3        /* the HIP runtime rejected the kernel launch */
+} kda_status_t;
+
+/* ABI version of this header; bumped on any incompatible change. */
+#define KDA_ABI_VERSION 1
+
+/*
+ * kda_chunk_fwd -- chunkwise forward over T tokens for B sequences x H heads.
+ *
+ *   q, k   [B, T, H, dk]  qkv_dtype   queries, keys
+ *   v      [B, T, H, dv]  qkv_dtype   values
+ *   g      [B, T, H, dk]  gate_dtype  per-key-channel log-decay, in [-5, 0]
+ *   beta   [B, T, H]      gate_dtype  write strength (any real value)
+ *   S0     [B, H, dk, dv] float32     initial state, or NULL for zeros
+ *   o      [B, T, H, dv]  out_dtype   output (written)
+ *   S_final[B, H, dk, dv] float32     state after token T-1 (written), or NULL
+ *                                     to skip; may be the same pointer as S0
+ *                                     (in-place continuation), must not
+ *                                     overlap it otherwise.
+ *
+ * Supported: dk in {64, 128}; dv a positive multiple of 64, at most 512;
+ * any T >= 0 (a ragged final chunk is padded internally with identity
+ * tokens, which leave the state unchanged); B, H >= 0.  T == 0 copies S0
+ * (or zeros) to S_final.  `o` must not overlap any input; S_final must not
+ * overlap q, k, v, g, beta or o.
+ *
+ * Internal state is float32.  Contractions run on the matrix cores with
+ * float32 accumulation: float32 operands when qkv_dtype == KDA_F32; for
+ * KDA_BF16 inputs, bfloat16 operands, where the products the output is
+ * sensitive to use a two-term (high + low bfloat16) split of both operands,
+ * which carries about 16 significant bits.  out_dtype == KDA_F32 keeps the
+ * output at that precision; KDA_BF16 rounds it once (the output of a
+ * heavy-tailed workload can lose several percent of its RMS to that rounding
+ * alone).
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
+                           const void *g, const void *beta, const float *S0,
+                           void *o, float *S_final,
+                           int B, int T, int H, int dk, int dv,
+                           kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                           kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_decode_step -- one token for every (sequence, head), state updated in place.
+ *
+ *   q, k   [B, H, dk]     qkv_dtype
+ *   v      [B, H, dv]     qkv_dtype
+ *   g      [B, H, dk]     gate_dtype  log-decay in [-5, 0]
+ *   beta   [B, H]         gate_dtype
+ *   S      [B, H, dk, dv] float32     read and written IN PLACE
+ *   o      [B, H, dv]     out_dtype   output (written)
+ *
+ * Supported: dk in {64, 128}, dv in {64, 128}; B, H >= 0.  `o` must not
+ * overlap any input or S; S must not overlap q, k, v, g or beta.
+ * Arithmetic is float32 throughout (the step is bandwidth-bound).
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
+                             const void *g, const void *beta, float *S, void *o,
+                             int B, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                             kda_dtype_t out_dtype, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kda_status_string(kda_status_t status);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
