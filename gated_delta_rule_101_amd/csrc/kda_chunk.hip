@@ -55,9 +55,9 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int WV = 16 * NWAVES;   // value columns per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 
-template <bool UNION, class A, class B> struct MaybeUnion;
-template <class A, class B> struct MaybeUnion<true, A, B> { union { A a; B b; }; };
-template <class A, class B> struct MaybeUnion<false, A, B> { A a; B b; };
+// Off-diagonal tile pairs (m, n), n < m, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+__host__ __device__ constexpr int pair_index(int m, int n) { return m * (m - 1) / 2 + n; }
+constexpr int NPAIRS = NT * (NT - 1) / 2;
 
 template <int DK, bool BF>
 struct ChunkSmem {
@@ -67,19 +67,23 @@ struct ChunkSmem {
     static constexpr int LDK = DK + PAD;             // token x channel rows
     static constexpr int LDC = C + PAD;              // 64-wide rows
     static constexpr int LD16 = TILE + 4;            // 16-wide rows of the inverses
-    // float32 needs the keys of the off-diagonal Gram and its results to share
-    // storage to fit in 160 KB; bfloat16 keeps them apart (one barrier fewer).
-    static constexpr bool UNION = !BF;
-    struct KhBuf { E Kh[NP][(NT - 1) * TILE * LDK]; };  // K decayed to its tile end, tiles 0..2
+    // Keys of tile n decayed to the start of tile m, one 16-row block per
+    // off-diagonal pair (m, n): read only by the Gram products, then the same
+    // storage holds the Gram results.
+    struct KvarBuf { E K[NPAIRS][NP][TILE * LDK]; };
     struct GramBuf {
-        E Aqk[NP][C * LDC];  // A_qk                              [token][token]
-        E L[C * LDC];        // StrictLower(Diag(beta) A_kk)       [token][token]
+        E Aqk[NP][C * LDC];          // A_qk                          [token][token]
+        E L[C * LDC];                // StrictLower(Diag(beta) A_kk)   [token][token]
+        float Ld[NT][TILE][TILE];    // diagonal blocks of L, transposed: [m][col][row]
+    };
+    union U {
+        KvarBuf kv;
+        GramBuf gr;
     };
     E Qt[NP][C * LDK];               // Gamma . Q                  [token][channel]
     E Kt[C * LDK];                   // Gamma . K                  [token][channel]
     E KbT[NP][DK * LDC];             // K decayed to chunk end     [channel][token]
-    MaybeUnion<UNION, KhBuf, GramBuf> mu;
-    float Ld[NT][TILE][TILE];        // diagonal blocks of L, transposed: [m][col][row]
+    U u;
     E Inv[NT][TILE * LD16];          // (I + L_mm)^-1              [m][row][col]
     float D[NT][DK];                 // total decay of each tile
     float GamC[DK];                  // total decay of the chunk
@@ -120,12 +124,15 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
     constexpr int LDK = SM::LDK, LDC = SM::LDC, LD16 = SM::LD16;
 
     __shared__ SM sm;
-    E(&Kh)[SM::NP][(NT - 1) * TILE * LDK] = sm.mu.a.Kh;
-    E(&Aqk)[SM::NP][C * LDC] = sm.mu.b.Aqk;
-    E(&Lm)[C * LDC] = sm.mu.b.L;
+    E(&Kv)[NPAIRS][SM::NP][TILE * LDK] = sm.u.kv.K;
+    E(&Aqk)[SM::NP][C * LDC] = sm.u.gr.Aqk;
+    E(&Lm)[C * LDC] = sm.u.gr.L;
+    float(&Ld)[NT][TILE][TILE] = sm.u.gr.Ld;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // wave index, made explicitly uniform: every branch on it (and the matrix-core
+    // instructions inside those branches, which ignore the exec mask) stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;     // row / column inside a 16x16 tile
     const int gq = lane >> 4;    // lane group: k-items, or output rows 4gq..4gq+3
 
@@ -207,8 +214,10 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
         }
         lds_barrier();
 
-        // Gram operands of the diagonal tile, kept in registers: f-scaled rows
-        // (query: split, key: single) and 1/f-scaled keys (split).
+        // f-scaled rows of tile m (query: split, key: single), kept for the
+        // Gram products, and the 1/f-scaled keys of the diagonal tile.  This
+        // loop issues no matrix-core instruction: every accumulation chain
+        // sits in the straight-line Gram block below.
         F8 aqh[KB], aql[KB], akh[KB], bih[KB], bil[KB];
 
 #pragma unroll
@@ -222,29 +231,52 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { Dt[t][i] = x0[i]; Dt[t][4 + i] = x1[i]; }
             }
-            float qv[8], kv[8];
-            cur.q[j].to_f32(qv);
-            cur.k[j].to_f32(kv);
-            // whole-tile decay before and after tile m (m is uniform per wave)
-            float before[8], after[8], Dm[8];
+            // whole-tile decay before and after tile m (m is uniform per wave), and
+            // from the end of tile m to the starts of tiles m + 2 and m + 3
+            float before[8], after[8], Dm[8], p1[8], p2[8];
             switch (m) {
             case 0:
 #pragma unroll
-                for (int i = 0; i < 8; ++i) { before[i] = 1.f; Dm[i] = Dt[0][i]; after[i] = Dt[1][i] * Dt[2][i] * Dt[3][i]; }
+                for (int i = 0; i < 8; ++i) {
+                    before[i] = 1.f; Dm[i] = Dt[0][i]; p1[i] = Dt[1][i]; p2[i] = Dt[1][i] * Dt[2][i];
+                    after[i] = p2[i] * Dt[3][i];
+                }
                 break;
             case 1:
 #pragma unroll
-                for (int i = 0; i < 8; ++i) { before[i] = Dt[0][i]; Dm[i] = Dt[1][i]; after[i] = Dt[2][i] * Dt[3][i]; }
+                for (int i = 0; i < 8; ++i) {
+                    before[i] = Dt[0][i]; Dm[i] = Dt[1][i]; p1[i] = Dt[2][i]; p2[i] = 1.f;
+                    after[i] = Dt[2][i] * Dt[3][i];
+                }
                 break;
             case 2:
 #pragma unroll
-                for (int i = 0; i < 8; ++i) { before[i] = Dt[0][i] * Dt[1][i]; Dm[i] = Dt[2][i]; after[i] = Dt[3][i]; }
+                for (int i = 0; i < 8; ++i) {
+                    before[i] = Dt[0][i] * Dt[1][i]; Dm[i] = Dt[2][i]; p1[i] = 1.f; p2[i] = 1.f;
+                    after[i] = Dt[3][i];
+                }
                 break;
             default:
 #pragma unroll
-                for (int i = 0; i < 8; ++i) { before[i] = Dt[0][i] * Dt[1][i] * Dt[2][i]; Dm[i] = Dt[3][i]; after[i] = 1.f; }
+                for (int i = 0; i < 8; ++i) {
+                    before[i] = Dt[0][i] * Dt[1][i] * Dt[2][i]; Dm[i] = Dt[3][i]; p1[i] = 1.f; p2[i] = 1.f;
+                    after[i] = 1.f;
+                }
                 break;
             }
+            if (m == 0 && r == 0) {
+                f32x4 g0, g1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    g0[i] = after[i] * Dm[i];
+                    g1[i] = after[4 + i] * Dm[4 + i];
+                }
+                *reinterpret_cast<f32x4 *>(&sm.GamC[ch]) = g0;
+                *reinterpret_cast<f32x4 *>(&sm.GamC[ch + 4]) = g1;
+            }
+            float qv[8], kv[8];
+            cur.q[j].to_f32(qv);
+            cur.k[j].to_f32(kv);
             float qt[8], ktv[8], kh[8], kb[8], qf[8], kf[8], ki[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -262,8 +294,25 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
             P::split8(ki, bih[j], bil[j]);
             P::split_sts8(&sm.Qt[0][(TILE * m + r) * LDK + ch], &sm.Qt[SM::NP - 1][(TILE * m + r) * LDK + ch], qt);
             P::sts8(&sm.Kt[(TILE * m + r) * LDK + ch], ktv);
-            if (m < NT - 1)
-                P::split_sts8(&Kh[0][(TILE * m + r) * LDK + ch], &Kh[SM::NP - 1][(TILE * m + r) * LDK + ch], kh);
+            // keys of tile m decayed to the start of each later tile m + d: pair (m + d, m)
+            if (m + 1 < NT) {
+                const int pi = pair_index(m + 1, m);
+                P::split_sts8(&Kv[pi][0][r * LDK + ch], &Kv[pi][SM::NP - 1][r * LDK + ch], kh);
+            }
+            if (m + 2 < NT) {
+                float kvv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kvv[i] = kh[i] * p1[i];
+                const int pi = pair_index(m + 2, m);
+                P::split_sts8(&Kv[pi][0][r * LDK + ch], &Kv[pi][SM::NP - 1][r * LDK + ch], kvv);
+            }
+            if (m + 3 < NT) {
+                float kvv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kvv[i] = kh[i] * p2[i];
+                const int pi = pair_index(m + 3, m);
+                P::split_sts8(&Kv[pi][0][r * LDK + ch], &Kv[pi][SM::NP - 1][r * LDK + ch], kvv);
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 E hi, lo;
@@ -271,95 +320,95 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
                 sm.KbT[0][(ch + i) * LDC + TILE * m + r] = hi;
                 if constexpr (SPLIT) sm.KbT[1][(ch + i) * LDC + TILE * m + r] = lo;
             }
-            if (m == 0 && r == 0) {
-                f32x4 g0, g1;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    g0[i] = Dt[0][i] * Dt[1][i] * Dt[2][i] * Dt[3][i];
-                    g1[i] = Dt[0][4 + i] * Dt[1][4 + i] * Dt[2][4 + i] * Dt[3][4 + i];
-                }
-                *reinterpret_cast<f32x4 *>(&sm.GamC[ch]) = g0;
-                *reinterpret_cast<f32x4 *>(&sm.GamC[ch + 4]) = g1;
-            }
         }
         if (gq == 0) sm.beta[TILE * m + r] = to_f32(cur.beta);
+        lds_barrier();
+
+        // ====================================================== Gram (wave m = block row m)
+        // Straight-line: the diagonal tile, then the three tiles to its left
+        // (n = m - d); a wave with fewer than three reads a valid stand-in and
+        // discards the result, so no matrix-core chain sits under a branch.
+        f32x4 gq_d = {0.f, 0.f, 0.f, 0.f}, gk_d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            gq_d = P::mma32(aqh[j], bih[j], gq_d);
+            if constexpr (SPLIT) {
+                gq_d = P::mma32(aqh[j], bil[j], gq_d);
+                gq_d = P::mma32(aql[j], bih[j], gq_d);
+            }
+            gk_d = P::mma32(akh[j], bih[j], gk_d);
+        }
+        f32x4 gq_o[NT - 1], gk_o[NT - 1];
+#pragma unroll
+        for (int d = 1; d < NT; ++d) {
+            const int pi = (m - d >= 0) ? pair_index(m, m - d) : 0;
+            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int ch = 32 * j + 8 * gq;
+                F8 bh, bl;
+                bh = P::lds8(&Kv[pi][0][r * LDK + ch]);
+                if constexpr (SPLIT) bl = P::lds8(&Kv[pi][1][r * LDK + ch]);
+                aq = P::mma32(aqh[j], bh, aq);
+                if constexpr (SPLIT) {
+                    aq = P::mma32(aqh[j], bl, aq);
+                    aq = P::mma32(aql[j], bh, aq);
+                }
+                ak = P::mma32(akh[j], bh, ak);
+            }
+            gq_o[d - 1] = aq;
+            gk_o[d - 1] = ak;
+        }
+        const f32x4 bet = *reinterpret_cast<const f32x4 *>(&sm.beta[TILE * m + 4 * gq]);
+        lds_barrier();   // every wave is done reading the key variants (their storage is reused)
+        f32x4 ldiag;
+        {
+            E qh[4], ql[4], kl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * gq + i;   // row inside the tile; the column is r
+                const float aq = (r > row) ? 0.f : gq_d[i];            // keep s <= t
+                const float ak = (r >= row) ? 0.f : gk_d[i] * bet[i];  // keep s <  t
+                ldiag[i] = ak;
+                P::split1(aq, qh[i], ql[i]);
+                kl[i] = P::cvt(ak);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int a = (TILE * m + 4 * gq + i) * LDC + TILE * m + r;
+                Aqk[0][a] = qh[i];
+                if constexpr (SPLIT) Aqk[1][a] = ql[i];
+                Lm[a] = kl[i];
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < NT; ++d) {
+            E qh[4], ql[4], kl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                P::split1(gq_o[d - 1][i], qh[i], ql[i]);
+                kl[i] = P::cvt(gk_o[d - 1][i] * bet[i]);
+            }
+            const int n = m - d;
+            if (n >= 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int a = (TILE * m + 4 * gq + i) * LDC + TILE * n + r;
+                    Aqk[0][a] = qh[i];
+                    if constexpr (SPLIT) Aqk[1][a] = ql[i];
+                    Lm[a] = kl[i];
+                }
+            }
+        }
+        *reinterpret_cast<f32x4 *>(&Ld[m][r][4 * gq]) = ldiag;
+
+        // next chunk's inputs: issued here, they land during the inverse and state parts
         QT vcur[NT][4];
 #pragma unroll
         for (int mm = 0; mm < NT; ++mm)
 #pragma unroll
             for (int i = 0; i < 4; ++i) vcur[mm][i] = cur.v[mm][i];
         if (c + 1 < nchunks) load_chunk(cur, c + 1);
-        lds_barrier();
-
-        // ====================================================== Gram (wave m = block row m)
-        f32x4 accq[NT], acck[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            accq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acck[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (n > m) continue;
-#pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                const int ch = 32 * j + 8 * gq;
-                F8 bh, bl;
-                if (n == m) {
-                    bh = bih[j];
-                    if constexpr (SPLIT) bl = bil[j];
-                } else {
-                    bh = P::lds8(&Kh[0][(TILE * n + r) * LDK + ch]);
-                    if constexpr (SPLIT) bl = P::lds8(&Kh[1][(TILE * n + r) * LDK + ch]);
-                    if (n + 1 < m) {   // decay across the whole tiles strictly between n and m
-                        float x[8], y[8];
-                        P::unpack8(bh, x);
-                        if constexpr (SPLIT) {
-                            P::unpack8(bl, y);
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) x[i] += y[i];
-                        }
-#pragma unroll
-                        for (int t = 1; t < NT - 1; ++t) {
-                            if (t > n && t < m) {
-                                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
-                                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch + 4]);
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) { x[i] *= d0[i]; x[4 + i] *= d1[i]; }
-                            }
-                        }
-                        P::split8(x, bh, bl);
-                    }
-                }
-                accq[n] = P::mma32(aqh[j], bh, accq[n]);
-                if constexpr (SPLIT) {
-                    accq[n] = P::mma32(aqh[j], bl, accq[n]);
-                    accq[n] = P::mma32(aql[j], bh, accq[n]);
-                }
-                acck[n] = P::mma32(akh[j], bh, acck[n]);
-            }
-        }
-        const f32x4 bet = *reinterpret_cast<const f32x4 *>(&sm.beta[TILE * m + 4 * gq]);
-        if constexpr (SM::UNION) lds_barrier();   // every wave is done reading Kh
-        f32x4 ldiag = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            if (n > m) continue;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * gq + i;   // row inside the tile; the column is r
-                float aq = accq[n][i];
-                float ak = acck[n][i] * bet[i];
-                if (n == m) {
-                    aq = (r > row) ? 0.f : aq;    // keep s <= t
-                    ak = (r >= row) ? 0.f : ak;   // keep s <  t
-                    ldiag[i] = ak;
-                }
-                E hi, lo;
-                P::split1(aq, hi, lo);
-                Aqk[0][(TILE * m + row) * LDC + TILE * n + r] = hi;
-                if constexpr (SPLIT) Aqk[1][(TILE * m + row) * LDC + TILE * n + r] = lo;
-                Lm[(TILE * m + row) * LDC + TILE * n + r] = P::cvt(ak);
-            }
-        }
-        *reinterpret_cast<f32x4 *>(&sm.Ld[m][r][4 * gq]) = ldiag;
         lds_wave_sync();
 
         // (I + L_mm)^-1: lane column r, column-oriented forward substitution
@@ -372,7 +421,7 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
                 float Lc[TILE];   // column jj of L_mm
 #pragma unroll
                 for (int i4 = 0; i4 < TILE / 4; ++i4) {
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.Ld[m][jj][4 * i4]);
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&Ld[m][jj][4 * i4]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
                 }

@@ -75,6 +75,7 @@ template <> struct Raw8<float> {
 
 // ------------------------------------------------------ MFMA precisions
 
+
 template <bool BF> struct Prec;
 
 // bf16 operands, fp32 accumulation.
@@ -113,22 +114,36 @@ template <> struct Prec<true> {
     }
     static __device__ __forceinline__ elem cvt(float x) { return f32_to_bf16(x); }
 
-    // Two-term split x = hi + lo, both bfloat16 (about 16 significant bits together).
+    // Two-term split x = hi + lo, both bfloat16 (about 16 significant bits
+    // together): hi = RNE(x); the residual x - hi is exact in float32.
     static constexpr bool SPLIT = true;
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ void split2(float a, float b, bf16x2 &hi, bf16x2 &lo) {
+        hi = bf16x2{(__bf16)a, (__bf16)b};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+        const float ra = a - __uint_as_float(hb << 16);
+        const float rb = b - __uint_as_float(hb & 0xffff0000u);
+        lo = bf16x2{(__bf16)ra, (__bf16)rb};
+    }
     static __device__ __forceinline__ void split8(const float (&x)[8], frag8 &hi, frag8 &lo) {
-        const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-        hi = __builtin_convertvector(v, bf16x8);
-        lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
+        bf16x2 h[4], l[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) split2(x[2 * p], x[2 * p + 1], h[p], l[p]);
+        hi = __builtin_shufflevector(__builtin_shufflevector(h[0], h[1], 0, 1, 2, 3),
+                                     __builtin_shufflevector(h[2], h[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+        lo = __builtin_shufflevector(__builtin_shufflevector(l[0], l[1], 0, 1, 2, 3),
+                                     __builtin_shufflevector(l[2], l[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
     }
     static __device__ __forceinline__ void split8(f32x4 a, f32x4 b, frag8 &hi, frag8 &lo) {
-        const f32x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        hi = __builtin_convertvector(v, bf16x8);
-        lo = __builtin_convertvector(v - __builtin_convertvector(hi, f32x8), bf16x8);
+        const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        split8(x, hi, lo);
     }
     static __device__ __forceinline__ void split4(f32x4 x, frag4 &hi, frag4 &lo) {
-        const bf16x4 h = __builtin_convertvector(x, bf16x4);
-        hi = __builtin_bit_cast(i16x4, h);
-        lo = __builtin_bit_cast(i16x4, __builtin_convertvector(x - __builtin_convertvector(h, f32x4), bf16x4));
+        bf16x2 h0, h1, l0, l1;
+        split2(x[0], x[1], h0, l0);
+        split2(x[2], x[3], h1, l1);
+        hi = __builtin_bit_cast(i16x4, __builtin_shufflevector(h0, h1, 0, 1, 2, 3));
+        lo = __builtin_bit_cast(i16x4, __builtin_shufflevector(l0, l1, 0, 1, 2, 3));
     }
     static __device__ __forceinline__ void split1(float x, elem &hi, elem &lo) {
         const __bf16 h = (__bf16)x;
@@ -221,13 +236,16 @@ __device__ __forceinline__ float row_inclusive_scan(float x) {
 // Workgroup barrier that orders LDS traffic only: outstanding global loads
 // (prefetches) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Orders this wave's earlier LDS writes before its later LDS reads (other
 // lanes of the same wave read what one lane wrote).
 __device__ __forceinline__ void lds_wave_sync() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
