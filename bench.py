@@ -209,6 +209,79 @@ def cpu_baseline(w, d, batch=32):
                       f"token recurrence, {batch} heads per call, {dt:.2f} s wall"}
 
 
+# ------------------------------------------------------------ counter passes
+
+COPY_BYTES = 1 << 30   # the calibration copy moves 1 GiB each way
+
+
+def profile_pass(kda, reps=3):
+    """A short run for `rocprofv3 --pmc`: a plain device copy of known size
+    (calibrates the byte counters), then the chunked forward and the decode
+    step of the benchmark workloads, `reps` launches each."""
+    import torch
+    from kda_workloads import configs, gen_torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    w, d, *_ = bench_fwd(kda, reps, 1)
+    del d
+    torch.cuda.empty_cache()
+    bench_decode(kda, 1)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(directory, counter):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    rows.append(r)
+    return rows
+
+
+def _per_dispatch(rows, name_part):
+    acc = {}
+    for r in rows:
+        if name_part in r["Kernel_Name"]:
+            acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def counters_to_traffic(fetch_dir, write_dir, out=TRAFFIC_FILE):
+    """Turn FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of a profile pass into
+    HBM bytes per launch of each KDA kernel, scaled by what the same counters
+    read for the 1 GiB calibration copy, and store them with the kernels'
+    source hashes."""
+    fr, wr = _counter_rows(fetch_dir, "FETCH_SIZE"), _counter_rows(write_dir, "WRITE_SIZE")
+    copy_f = _per_dispatch(fr, "copyBuffer")   # the runtime's device-to-device copy kernel
+    copy_w = _per_dispatch(wr, "copyBuffer")
+    if not copy_f or not copy_w:
+        raise SystemExit("no calibration copy dispatch found in the counter files")
+    cf = COPY_BYTES / (max(copy_f) * 1024.0)
+    cw = COPY_BYTES / (max(copy_w) * 1024.0)
+    rec = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_KiB": max(copy_f), "write_KiB": max(copy_w),
+                           "fetch_scale": round(cf, 4), "write_scale": round(cw, 4)}}
+    for kernel, part, sources in (("kda_chunk_fwd", "kda_chunk_fwd_kernel", CHUNK_SOURCES),
+                                  ("kda_decode_step", "kda_decode_kernel", DECODE_SOURCES)):
+        f, w_ = _per_dispatch(fr, part), _per_dispatch(wr, part)
+        if not f or not w_:
+            continue
+        fb = sum(f) / len(f) * 1024.0 * cf
+        wb = sum(w_) / len(w_) * 1024.0 * cw
+        rec[kernel] = {"source_hash": kernel_source_hash(sources), "fetch_bytes_per_launch": round(fb),
+                       "write_bytes_per_launch": round(wb), "hbm_bytes_per_launch": round(fb + wb),
+                       "dispatches": len(f)}
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,7 +290,14 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc: calibration copy, then each kernel a few times")
+    ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs of --profile-pass")
     args = ap.parse_args()
+    if args.counters_from:
+        counters_to_traffic(*args.counters_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the KDA path "
               "runs one workload per GPU; multi-GPU runs are not part of this build.", file=sys.stderr)
@@ -229,6 +309,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kda.load_library()
+    if args.profile_pass:
+        profile_pass(kda)
+        return
 
     w, d, ms, tok_s, rf, extra = bench_fwd(kda, args.steps, args.warmup)
     out = {
