@@ -67,7 +67,7 @@ def kernel_source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
+CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk_pipe.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
 DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
 
 
@@ -267,7 +267,7 @@ def counters_to_traffic(fetch_dir, write_dir, out=TRAFFIC_FILE):
     cw = COPY_BYTES / (max(copy_w) * 1024.0)
     rec = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_KiB": max(copy_f), "write_KiB": max(copy_w),
                            "fetch_scale": round(cf, 4), "write_scale": round(cw, 4)}}
-    for kernel, part, sources in (("kda_chunk_fwd", "kda_chunk_fwd_kernel", CHUNK_SOURCES),
+    for kernel, part, sources in (("kda_chunk_fwd", "kda_chunk_pipe_kernel", CHUNK_SOURCES),
                                   ("kda_decode_step", "kda_decode_kernel", DECODE_SOURCES)):
         f, w_ = _per_dispatch(fr, part), _per_dispatch(wr, part)
         if not f or not w_:

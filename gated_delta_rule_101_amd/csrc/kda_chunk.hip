@@ -558,8 +558,6 @@ hipError_t dispatch_out(const ChunkFwdArgs &a, hipStream_t s)
 template <int DK>
 hipError_t dispatch_dtypes(const ChunkFwdArgs &a, hipStream_t s)
 {
-    if (a.qkv_bf16)
-        return a.gate_bf16 ? dispatch_out<DK, true, true>(a, s) : dispatch_out<DK, true, false>(a, s);
     return a.gate_bf16 ? dispatch_out<DK, false, true>(a, s) : dispatch_out<DK, false, false>(a, s);
 }
 
@@ -567,6 +565,7 @@ hipError_t dispatch_dtypes(const ChunkFwdArgs &a, hipStream_t s)
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream)
 {
+    if (a.qkv_bf16) return launch_chunk_fwd_bf16(a, stream);
     (void)hipGetLastError();   // report only this launch's own failure
     if (a.dk == 64) return dispatch_dtypes<64>(a, stream);
     return dispatch_dtypes<128>(a, stream);

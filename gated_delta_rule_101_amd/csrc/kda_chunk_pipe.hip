@@ -1,0 +1,565 @@
+// Chunkwise KDA forward for bfloat16 q, k, v on gfx950: a two-role pipeline
+// inside one workgroup.
+//
+// One workgroup owns one (sequence, head, 64-wide slab of value columns) and
+// walks the head's chunks of 64 tokens in order ("Kimi K3 - Lesson 3 of 14 -
+// Sequence axis": sequential between chunks, parallel within; output =
+// inter-chunk (Gamma . Q) S plus masked intra-chunk A V~; keys rescaled by
+// 1/Gamma inside 16-token tiles, which the g_min = -5 floor keeps below
+// e^80).  Everything a chunk needs that does not depend on the state is
+// prepared one chunk ahead by four producer waves while four consumer waves
+// run the state recurrence of the current chunk; the two sets hand over
+// through a double-buffered LDS stage and meet at one workgroup barrier per
+// chunk.  A SIMD holds one producer and one consumer wave, so the consumer's
+// matrix-core work fills the producer's vector-ALU gaps and the other way
+// round.
+//
+// Producer wave m, tile m (16 tokens, lane row r = token, 8 channels per
+// 32-channel block and lane group):
+//   decays  b = within-tile inclusive cumsum of g (DPP row scan), f = e^b in
+//           [e^-80, 1], 1/f <= e^80, tile totals D_m (to LDS).
+//   keys    K-hat_m: keys decayed to the end of tile m (B operands of the
+//           later tiles' Gram blocks), to LDS.  The four producers then
+//           meet at an LDS counter (the consumers are not involved).
+//   stage   Gamma.Q, Gamma.K (Gamma = decay from the chunk start) and K-bar
+//           (keys decayed to the chunk end), and block row m of
+//             A_qk (s <= t) and L = StrictLower(Diag(beta) A_kk),
+//           A(t, s) = sum_c x_tc k_sc e^{b_tc - b_sc}.  The diagonal tile
+//           pairs f-scaled rows with 1/f-scaled keys in two-term bfloat16
+//           (the 1/f keys exceed fp16 range); a tile n = m - d pairs the
+//           f-scaled rows times the whole tiles strictly between (D_{m-1},
+//           D_{m-1} D_{m-2}) with K-hat_n, in fp16.  Finally (I + L_mm)^-1 by
+//           column-oriented forward substitution in fp32.
+// Consumer wave 4 + w, value columns 16w..16w+15 of the slab, state slab
+// S (dk x 16, fp32) in registers:
+//   X = V - (Gamma.K) S,  U = (I + L)^-1 Diag(beta) X (blocked forward
+//   substitution over the four tiles), O = (Gamma.Q) S + A_qk U,
+//   S <- Diag(Gamma_C) S + K-bar^T U.
+//
+// Operand precision: fp16 single operands for (Gamma.Q) S, (Gamma.K) S, the
+// off-diagonal Gram tiles and L U; fp16 two-term U (and right-hand sides of
+// the diagonal inverses) against single fp16 A_qk, K-bar and inverses; fp32
+// accumulation throughout.  fp16 needs the values, the state and the outputs
+// to stay below 65504 in magnitude, which unit-scale values and L2-normalised
+// queries and keys (as the method prescribes) satisfy.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64;             // tokens per chunk
+constexpr int TILE = 16;          // tokens per tile
+constexpr int NT = C / TILE;      // tiles per chunk
+constexpr int NPROD = NT;         // producer waves: wave m prepares tile m
+constexpr int NCONS = 4;          // consumer waves: 16 value columns each
+constexpr int NTHREADS = 64 * (NPROD + NCONS);
+constexpr int WV = 16 * NCONS;    // value columns per workgroup
+constexpr int LDT = TILE + 4;     // row stride (elements) of a stored 16x16 tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr unsigned SPIN_LIMIT = 1u << 20;   // bound on every producer wait
+
+// Tiles (m, n) of the lower block triangle, n <= m, and of the strict one, n < m.
+__host__ __device__ constexpr int lower_index(int m, int n) { return m * (m + 1) / 2 + n; }
+__host__ __device__ constexpr int strict_index(int m, int n) { return m * (m - 1) / 2 + n; }
+constexpr int NLOWER = NT * (NT + 1) / 2;
+constexpr int NSTRICT = NT * (NT - 1) / 2;
+
+template <int DK>
+struct alignas(16) PipeSmem {
+    static constexpr int LDK = DK + 8;   // token rows, 16 bytes of padding
+    // What the consumers read for one chunk.
+    struct alignas(16) Stage {
+        _Float16 Qt[C * LDK];                   // Gamma . Q               [token][channel]
+        _Float16 Kt[C * LDK];                   // Gamma . K               [token][channel]
+        _Float16 Kb[C * LDK];                   // K decayed to chunk end  [token][channel]
+        _Float16 AqkT[NLOWER][TILE * LDT];      // tiles of A_qk, transposed: [s][t]
+        _Float16 LT[NSTRICT][TILE * LDT];       // tiles of L, transposed
+        _Float16 InvT[NT][TILE * LDT];          // (I + L_mm)^-1, transposed
+        float GamC[DK];                         // total decay of the chunk
+        float beta[C];
+    };
+    Stage stage[2];
+    // Producer scratch.
+    _Float16 Kh[NT - 1][TILE * LDK];            // keys of tiles 0..2 decayed to their tile end
+    float D[NT][DK];                            // total decay of each tile
+    float LdT[NT][TILE][TILE];                  // diagonal blocks of L (fp32): [m][col][row]
+    unsigned arrivals;                          // producer meeting counter
+};
+
+// The q, k, g, beta of one token row of one chunk, as raw storage bits.
+template <int DK, typename GT>
+struct RowIn {
+    static constexpr int KB = DK / 32;
+    Raw8<uint16_t> q[KB], k[KB];   // channels 32j + 8(lane/16) + 0..7
+    Raw8<GT> g[KB];
+    GT beta;
+};
+
+// The four producer waves meet here; LDS writes before it are visible to all
+// four after it.  The wait is bounded, so a wave never spins forever.
+__device__ __forceinline__ void producer_meet(unsigned *arrivals, unsigned target, int lane) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (unsigned it = 0; it < SPIN_LIMIT; ++it) {
+        const unsigned seen = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (seen >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int DK, bool GBF, bool OBF>
+__global__ void __launch_bounds__(NTHREADS, 1)
+kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                      const uint16_t *__restrict__ v, const typename Store<GBF>::type *__restrict__ g,
+                      const typename Store<GBF>::type *__restrict__ beta, const float *S0,
+                      typename Store<OBF>::type *__restrict__ o, float *S_final,
+                      int B, int T, int H, int dv, int nslab)
+{
+    typedef typename Store<GBF>::type GT;
+    typedef typename Store<OBF>::type OT;
+    typedef PipeSmem<DK> SM;
+    typedef typename SM::Stage Stage;
+    typedef Prec<true> BF;
+    constexpr int KB = DK / 32;   // 32-channel blocks
+    constexpr int KT = DK / 16;   // 16-channel tiles
+    constexpr int LDK = SM::LDK;
+
+    __shared__ SM sm;
+
+    const int lane = threadIdx.x & 63;
+    // wave index, made explicitly uniform: every branch on it (and the
+    // matrix-core instructions inside those branches, which ignore the exec
+    // mask) stays scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool producer = wave < NPROD;
+    const int r = lane & 15;     // row / column inside a 16x16 tile
+    const int gq = lane >> 4;    // lane group: k-items, or output rows 4gq..4gq+3
+
+    // Workgroup -> (b, h, slab).  Workgroups are dealt to the 8 XCDs round
+    // robin; the slabs of one head go to the same XCD so they share its L2
+    // for the q, k, g reads they have in common.
+    const int BH = B * H;
+    int bh, slab;
+    if ((BH & 7) == 0) {
+        const int rest = blockIdx.x >> 3;
+        slab = rest % nslab;
+        bh = (rest / nslab) * 8 + (blockIdx.x & 7);
+    } else {
+        bh = blockIdx.x / nslab;
+        slab = blockIdx.x % nslab;
+    }
+    const int b = bh / H, h = bh % H;
+    const int nchunks = (T + C - 1) / C;
+    auto row_qk = [&](int t) -> size_t { return ((size_t)b * T + t) * H + h; };
+
+    // ------------------------------------------------------------ producer state
+    const int m = wave;   // producer: tile
+    RowIn<DK, GT> in;     // inputs of the next chunk to prepare
+    auto load_row = [&](int c) {
+        const int t = c * C + TILE * m + r;
+        if (t < T) {
+            const size_t rr = row_qk(t);
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                in.q[j].load(q + rr * DK + 32 * j + 8 * gq);
+                in.k[j].load(k + rr * DK + 32 * j + 8 * gq);
+                in.g[j].load(g + rr * DK + 32 * j + 8 * gq);
+            }
+            in.beta = beta[rr];
+        } else {   // identity token: no decay, no write, zero read
+#pragma unroll
+            for (int j = 0; j < KB; ++j) { in.q[j].zero(); in.k[j].zero(); in.g[j].zero(); }
+            in.beta = GT(0);
+        }
+    };
+
+    // ------------------------------------------------------------ consumer state
+    const int w = wave - NPROD;                 // consumer: column group
+    const int col0 = slab * WV + 16 * w;        // first value column of this consumer
+    const size_t s_base = (size_t)bh * DK * dv + col0 + r;
+    f32x4 S[KT];                                // rows 16kt + 4gq + i, column r
+    uint16_t vin[NT][4];                        // V rows 16mm + 4gq + i, column r
+    auto load_v = [&](int c) {
+#pragma unroll
+        for (int mm = 0; mm < NT; ++mm)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = c * C + TILE * mm + 4 * gq + i;
+                vin[mm][i] = t < T ? v[row_qk(t) * dv + col0 + r] : uint16_t(0);
+            }
+    };
+
+    // Iteration c: the producers prepare chunk c + 1 into stage (c + 1) & 1
+    // while the consumers run chunk c from stage c & 1.  Both roles run their
+    // own loop; each iteration ends at the same workgroup barrier.
+    if (producer) {
+        if (nchunks > 0) load_row(0);
+        if (threadIdx.x == 0) sm.arrivals = 0;
+        lds_barrier();
+        unsigned meetings = 0;   // producer meetings so far (uniform)
+        for (int c = -1; c < nchunks; ++c) {
+            const int cn = c + 1;
+            if (cn < nchunks) {
+                Stage &st = sm.stage[cn & 1];
+
+                // ---------------------------------------------- decays within tile m
+                float f[KB][8], rf[KB][8];
+#pragma unroll
+                for (int j = 0; j < KB; ++j) {
+                    float gl[8];
+                    in.g[j].to_f32(gl);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        f[j][i] = fast_exp2(row_inclusive_scan(gl[i] * LOG2E));
+                        rf[j][i] = fast_rcp(f[j][i]);
+                    }
+                    if (r == TILE - 1) {
+                        float *d = &sm.D[m][32 * j + 8 * gq];
+                        *reinterpret_cast<f32x4 *>(d) = f32x4{f[j][0], f[j][1], f[j][2], f[j][3]};
+                        *reinterpret_cast<f32x4 *>(d + 4) = f32x4{f[j][4], f[j][5], f[j][6], f[j][7]};
+                    }
+                }
+                lds_wave_sync();
+
+                // ---------------------------------------------- keys decayed to the end of tile m
+                if (m < NT - 1) {
+#pragma unroll
+                    for (int j = 0; j < KB; ++j) {
+                        const int ch = 32 * j + 8 * gq;
+                        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sm.D[m][ch]);
+                        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&sm.D[m][ch + 4]);
+                        float kv[8], kh[8];
+                        in.k[j].to_f32(kv);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            kh[i] = kv[i] * rf[j][i] * d0[i];
+                            kh[4 + i] = kv[4 + i] * rf[j][4 + i] * d1[i];
+                        }
+                        *reinterpret_cast<f16x8 *>(&sm.Kh[m][r * LDK + ch]) = h16::pack8(kh);
+                    }
+                }
+                meetings += 1;
+                producer_meet(&sm.arrivals, NPROD * meetings, lane);
+
+                // ---------------------------------------------- staged operands and block row m of the Gram
+                f32x4 gq_d = {0.f, 0.f, 0.f, 0.f}, gk_d = {0.f, 0.f, 0.f, 0.f};
+                f32x4 gq_o[NT - 1], gk_o[NT - 1];
+#pragma unroll
+                for (int d = 0; d < NT - 1; ++d) {
+                    gq_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    gk_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int j = 0; j < KB; ++j) {
+                    const int ch = 32 * j + 8 * gq;
+                    float Dt[NT][8];
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
+                        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch + 4]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) { Dt[t][i] = x0[i]; Dt[t][4 + i] = x1[i]; }
+                    }
+                    // whole-tile decay before and after tile m (m is uniform per
+                    // wave), and across the tiles strictly between tile m and the
+                    // tiles m - 2, m - 3
+                    float before[8], after[8], Dm[8], v2[8], v3[8];
+                    switch (m) {
+                    case 0:
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            before[i] = 1.f; Dm[i] = Dt[0][i]; after[i] = Dt[1][i] * Dt[2][i] * Dt[3][i];
+                            v2[i] = 1.f; v3[i] = 1.f;
+                        }
+                        break;
+                    case 1:
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            before[i] = Dt[0][i]; Dm[i] = Dt[1][i]; after[i] = Dt[2][i] * Dt[3][i];
+                            v2[i] = 1.f; v3[i] = 1.f;
+                        }
+                        break;
+                    case 2:
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            before[i] = Dt[0][i] * Dt[1][i]; Dm[i] = Dt[2][i]; after[i] = Dt[3][i];
+                            v2[i] = Dt[1][i]; v3[i] = 1.f;
+                        }
+                        break;
+                    default:
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            before[i] = Dt[0][i] * Dt[1][i] * Dt[2][i]; Dm[i] = Dt[3][i]; after[i] = 1.f;
+                            v2[i] = Dt[2][i]; v3[i] = Dt[2][i] * Dt[1][i];
+                        }
+                        break;
+                    }
+                    if (m == 0 && r == 0) {
+                        f32x4 g0, g1;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            g0[i] = after[i] * Dm[i];
+                            g1[i] = after[4 + i] * Dm[4 + i];
+                        }
+                        *reinterpret_cast<f32x4 *>(&st.GamC[ch]) = g0;
+                        *reinterpret_cast<f32x4 *>(&st.GamC[ch + 4]) = g1;
+                    }
+                    float qv[8], kv[8];
+                    in.q[j].to_f32(qv);
+                    in.k[j].to_f32(kv);
+                    float qf[8], kf[8], ki[8], qt[8], kt[8], kb[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        qf[i] = qv[i] * f[j][i];
+                        kf[i] = kv[i] * f[j][i];
+                        ki[i] = kv[i] * rf[j][i];            // 1/f-scaled key, <= e^80 |k|
+                        qt[i] = qf[i] * before[i];
+                        kt[i] = kf[i] * before[i];
+                        kb[i] = ki[i] * (Dm[i] * after[i]);  // decayed to the chunk end, <= |k|
+                    }
+                    const int row = (TILE * m + r) * LDK + ch;
+                    *reinterpret_cast<f16x8 *>(&st.Qt[row]) = h16::pack8(qt);
+                    *reinterpret_cast<f16x8 *>(&st.Kt[row]) = h16::pack8(kt);
+                    *reinterpret_cast<f16x8 *>(&st.Kb[row]) = h16::pack8(kb);
+
+                    // diagonal tile: two-term bfloat16
+                    {
+                        BF::frag8 aqh, aql, bih, bil;
+                        BF::split8(qf, aqh, aql);
+                        BF::split8(ki, bih, bil);
+                        const BF::frag8 akh = BF::pack8(kf);
+                        gq_d = BF::mma32(aqh, bih, gq_d);
+                        gq_d = BF::mma32(aqh, bil, gq_d);
+                        gq_d = BF::mma32(aql, bih, gq_d);
+                        gk_d = BF::mma32(akh, bih, gk_d);
+                    }
+                    // tiles n = m - d to the left: fp16
+                    if (m >= 1) {
+                        const f16x8 bk = h16::lds8(&sm.Kh[m - 1][r * LDK + ch]);
+                        gq_o[0] = h16::mma32(h16::pack8(qf), bk, gq_o[0]);
+                        gk_o[0] = h16::mma32(h16::pack8(kf), bk, gk_o[0]);
+                    }
+                    if (m >= 2) {
+                        const f16x8 bk = h16::lds8(&sm.Kh[m - 2][r * LDK + ch]);
+                        float a[8], e[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v2[i]; e[i] = kf[i] * v2[i]; }
+                        gq_o[1] = h16::mma32(h16::pack8(a), bk, gq_o[1]);
+                        gk_o[1] = h16::mma32(h16::pack8(e), bk, gk_o[1]);
+                    }
+                    if (m >= 3) {
+                        const f16x8 bk = h16::lds8(&sm.Kh[m - 3][r * LDK + ch]);
+                        float a[8], e[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v3[i]; e[i] = kf[i] * v3[i]; }
+                        gq_o[2] = h16::mma32(h16::pack8(a), bk, gq_o[2]);
+                        gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
+                    }
+                }
+                if (gq == 0) st.beta[TILE * m + r] = to_f32(in.beta);
+
+                // q, k, g of chunk cn are consumed: fetch the next chunk's now so the
+                // loads land while the Gram results are stored and inverted
+                if (cn + 1 < nchunks) load_row(cn + 1);
+                lds_wave_sync();
+
+                // ---------------------------------------------- Gram results of block row m
+                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&st.beta[TILE * m + 4 * gq]);
+                {
+                    f32x4 aq, ak;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 4 * gq + i;   // row t inside the tile; the column s is r
+                        aq[i] = (r > row) ? 0.f : gq_d[i];             // keep s <= t
+                        ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
+                    }
+                    *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, m)][r * LDT + 4 * gq]) = h16::pack4(aq);
+                    *reinterpret_cast<f32x4 *>(&sm.LdT[m][r][4 * gq]) = ak;
+                }
+#pragma unroll
+                for (int d = 1; d < NT; ++d) {
+                    if (m >= d) {
+                        const int n = m - d;
+                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, n)][r * LDT + 4 * gq]) =
+                            h16::pack4(gq_o[d - 1]);
+                        *reinterpret_cast<f16x4 *>(&st.LT[strict_index(m, n)][r * LDT + 4 * gq]) =
+                            h16::pack4(gk_o[d - 1] * bet);
+                    }
+                }
+                lds_wave_sync();
+
+                // ---------------------------------------------- (I + L_mm)^-1, lane column r
+                {
+                    // X = e_r; `one` is opaque so the 16 selects are not hoisted out of
+                    // the chunk loop (they would only occupy registers there)
+                    float one = 1.f;
+                    asm volatile("" : "+v"(one));
+                    float X[TILE];
+#pragma unroll
+                    for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < TILE - 1; ++jj) {
+                        float Lc[TILE];   // column jj of L_mm
+#pragma unroll
+                        for (int i4 = 0; i4 < TILE / 4; ++i4) {
+                            const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.LdT[m][jj][4 * i4]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
+                        }
+#pragma unroll
+                        for (int ii = jj + 1; ii < TILE; ++ii) X[ii] -= Lc[ii] * X[jj];
+                    }
+                    // lane group gq stores rows 4gq..4gq+3 of column r
+                    f32x4 part;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
+                    *reinterpret_cast<f16x4 *>(&st.InvT[m][r * LDT + 4 * gq]) = h16::pack4(part);
+                }
+            }
+            lds_barrier();
+        }
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[kt][i] = S0 ? S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
+        if (nchunks > 0) load_v(0);
+        lds_barrier();
+        for (int c = -1; c < nchunks; ++c) {
+            if (c >= 0) {
+                const Stage &st = sm.stage[c & 1];
+
+                uint16_t vc[NT][4];
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vc[mm][i] = vin[mm][i];
+                if (c + 1 < nchunks) load_v(c + 1);
+
+                // state slab as fp16 B operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
+                f16x8 Sh[KB];
+#pragma unroll
+                for (int j = 0; j < KB; ++j) Sh[j] = h16::pack8(S[2 * j], S[2 * j + 1]);
+
+                // (Gamma.Q) S and X = V - (Gamma.K) S, scaled by beta
+                f32x4 accQ[NT], Y[NT];
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm) {
+                    f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
+                    const int row = (TILE * mm + r) * LDK;
+#pragma unroll
+                    for (int j = 0; j < KB; ++j) {
+                        const int ch = row + 32 * j + 4 * gq;
+                        aQ = h16::mma32(h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]), Sh[j], aQ);
+                        aK = h16::mma32(h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]), Sh[j], aK);
+                    }
+                    accQ[mm] = aQ;
+                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(&st.beta[TILE * mm + 4 * gq]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Y[mm][i] = bt[i] * (to_f32(vc[mm][i]) - aK[i]);
+                }
+
+                // U = (I + L)^-1 Diag(beta) X, one tile at a time
+                const int tro = h16::tr_offset(lane, LDT);
+                f16x4 Uh[NT], Ul[NT];
+                f32x4 U[NT];
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int n = 0; n < mm; ++n)
+                        acc = h16::mma16(h16::tr4(&st.LT[strict_index(mm, n)][tro]), Uh[n], acc);
+                    f16x4 rh, rl;
+                    h16::split4(Y[mm] - acc, rh, rl);
+                    const f16x4 inv = h16::tr4(&st.InvT[mm][tro]);
+                    f32x4 u = h16::mma16(inv, rh, f32x4{0.f, 0.f, 0.f, 0.f});
+                    u = h16::mma16(inv, rl, u);
+                    U[mm] = u;
+                    h16::split4(u, Uh[mm], Ul[mm]);
+                }
+
+                // O = (Gamma.Q) S + A_qk U, stored straight from the accumulators
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm) {
+                    f32x4 acc = accQ[mm];
+#pragma unroll
+                    for (int n = 0; n <= mm; ++n) {
+                        const f16x4 a = h16::tr4(&st.AqkT[lower_index(mm, n)][tro]);
+                        acc = h16::mma16(a, Uh[n], acc);
+                        acc = h16::mma16(a, Ul[n], acc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = c * C + TILE * mm + 4 * gq + i;
+                        if (t < T) o[row_qk(t) * dv + col0 + r] = from_f32<OT>(acc[i]);
+                    }
+                }
+
+                // S <- Diag(Gamma_C) S + K-bar^T U; K-bar^T read transposed from its token rows
+                f16x8 Ubh[2], Ubl[2];
+                h16::split8(U[0], U[1], Ubh[0], Ubl[0]);
+                h16::split8(U[2], U[3], Ubh[1], Ubl[1]);
+                const int tk = h16::tr_offset(lane, LDK);
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    const f32x4 gcv = *reinterpret_cast<const f32x4 *>(&st.GamC[16 * kt + 4 * gq]);
+                    f32x4 acc = S[kt] * gcv;
+#pragma unroll
+                    for (int j2 = 0; j2 < 2; ++j2) {
+                        const _Float16 *base = &st.Kb[(32 * j2) * LDK + 16 * kt + tk];
+                        const f16x4 a0 = h16::tr4(base);
+                        const f16x4 a1 = h16::tr4(base + 16 * LDK);
+                        const f16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc = h16::mma32(a, Ubh[j2], acc);
+                        acc = h16::mma32(a, Ubl[j2], acc);
+                    }
+                    S[kt] = acc;
+                }
+            }
+            lds_barrier();
+        }
+        if (S_final) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    S_final[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] = S[kt][i];
+        }
+    }
+}
+
+template <int DK, bool GBF, bool OBF>
+hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
+{
+    typedef typename Store<GBF>::type GT;
+    typedef typename Store<OBF>::type OT;
+    const int nslab = a.dv / WV;
+    const unsigned grid = (unsigned)(a.B * a.H * nslab);
+    kda_chunk_pipe_kernel<DK, GBF, OBF><<<grid, NTHREADS, 0, stream>>>(
+        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const GT *)a.g,
+        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.B, a.T, a.H, a.dv, nslab);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t dispatch(const ChunkFwdArgs &a, hipStream_t s)
+{
+    if (a.gate_bf16) return a.out_bf16 ? launch<DK, true, true>(a, s) : launch<DK, true, false>(a, s);
+    return a.out_bf16 ? launch<DK, false, true>(a, s) : launch<DK, false, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream)
+{
+    (void)hipGetLastError();   // report only this launch's own failure
+    if (a.dk == 64) return dispatch<64>(a, stream);
+    return dispatch<128>(a, stream);
+}
+
+}  // namespace kda

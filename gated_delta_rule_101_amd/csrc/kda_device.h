@@ -216,6 +216,72 @@ template <> struct Prec<false> {
     }
 };
 
+// ------------------------------------------------ fp16 matrix-core operands
+//
+// v_mfma_f32_16x16x32_f16 / 16x16x16_f16 with fp32 accumulation: 11
+// significant bits per operand, for operands bounded by the method (decayed
+// L2-normalised keys and queries) or of unit scale (state, values).
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 fp16x4_v __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) fp16x4_v lds_fp16x4;
+
+namespace h16 {
+
+__device__ __forceinline__ f16x8 pack8(const float (&x)[8]) {
+    const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    return __builtin_convertvector(v, f16x8);   // v_cvt_pk_f16_f32, round to nearest even
+}
+__device__ __forceinline__ f16x8 pack8(f32x4 a, f32x4 b) {
+    const f32x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_convertvector(v, f16x8);
+}
+__device__ __forceinline__ f16x4 pack4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+
+// x = hi + lo with both parts fp16 (about 22 significant bits together).
+__device__ __forceinline__ void split4(f32x4 x, f16x4 &hi, f16x4 &lo) {
+    hi = __builtin_convertvector(x, f16x4);
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), f16x4);
+}
+__device__ __forceinline__ void split8(f32x4 a, f32x4 b, f16x8 &hi, f16x8 &lo) {
+    f16x4 ha, la, hb, lb;
+    split4(a, ha, la);
+    split4(b, hb, lb);
+    hi = __builtin_shufflevector(ha, hb, 0, 1, 2, 3, 4, 5, 6, 7);
+    lo = __builtin_shufflevector(la, lb, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4 mma32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f16x8 lds8(const _Float16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+__device__ __forceinline__ f16x8 lds4x2(const _Float16 *p0, const _Float16 *p1) {
+    const f16x4 a = *reinterpret_cast<const f16x4 *>(p0);
+    const f16x4 b = *reinterpret_cast<const f16x4 *>(p1);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane 4a + b (a, b < 4) supplies an 8-byte address p(a, b); lane i of the
+// group receives, as element a, the 16-bit value (i % 4) of p(a, i / 4).
+// tr_offset gives the per-lane offset (in elements) that makes lane (g, i)
+// (g = lane / 16, i = lane % 16) receive T[4g + a][i], a = 0..3, from a
+// row-major 16-wide block T with row stride ld: an MFMA operand whose row is
+// the block's column and whose k-items are the block's rows.
+__device__ __forceinline__ int tr_offset(int lane, int ld) {
+    return (4 * (lane >> 4) + ((lane & 15) >> 2)) * ld + 4 * (lane & 3);
+}
+__device__ __forceinline__ f16x4 tr4(const _Float16 *p) {
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p));
+}
+
+}  // namespace h16
+
 // ------------------------------------------------------------ wave tools
 
 // Lane i of each 16-lane row receives lane i-N of the same row; lanes i < N get 0.

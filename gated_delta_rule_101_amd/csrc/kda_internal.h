@@ -24,7 +24,8 @@ struct DecodeArgs {
     bool qkv_bf16, gate_bf16, out_bf16;
 };
 
-hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);
+hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        // any dtypes
+hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 
 }  // namespace kda
