@@ -42,6 +42,8 @@
 // accumulation throughout.  fp16 needs the values, the state and the outputs
 // to stay below 65504 in magnitude, which unit-scale values and L2-normalised
 // queries and keys (as the method prescribes) satisfy.
+#include <cstddef>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -75,25 +77,35 @@ struct alignas(16) PipeSmem {
         _Float16 Kb[C * LDK];                   // K decayed to chunk end  [token][channel]
         _Float16 AqkT[NLOWER][TILE * LDT];      // tiles of A_qk, transposed: [s][t]
         _Float16 LT[NSTRICT][TILE * LDT];       // tiles of L, transposed
-        _Float16 InvT[NT][TILE * LDT];          // (I + L_mm)^-1, transposed
+        float LdT[NT][TILE][TILE];              // diagonal blocks of L (fp32): [m][col][row]
         float GamC[DK];                         // total decay of the chunk
-        float beta[C];
     };
     Stage stage[2];
     // Producer scratch.
-    _Float16 Kh[NT - 1][TILE * LDK];            // keys of tiles 0..2 decayed to their tile end
-    float D[NT][DK];                            // total decay of each tile
-    float LdT[NT][TILE][TILE];                  // diagonal blocks of L (fp32): [m][col][row]
+    alignas(16) _Float16 Kh[NT - 1][TILE * LDK];   // keys of tiles 0..2 decayed to their tile end
+    alignas(16) float D[NT][DK];                // total decay of each tile
+    // beta of chunks c, c + 1, c + 2 (slot = chunk mod 3): written by a consumer
+    // two iterations ahead, read by the producers one iteration ahead.
+    alignas(16) float betas[3][C];
+    // Consumer scratch: each consumer's copy of the four (I + L_mm)^-1, transposed.
+    alignas(16) _Float16 inv[NCONS][NT][TILE * LDT];
     unsigned arrivals;                          // producer meeting counter
 };
 
-// The q, k, g, beta of one token row of one chunk, as raw storage bits.
+// Every array above is read with 8- or 16-byte LDS accesses.
+static_assert(sizeof(PipeSmem<64>::Stage) % 16 == 0 && sizeof(PipeSmem<128>::Stage) % 16 == 0, "stage alignment");
+static_assert(offsetof(PipeSmem<128>, betas) % 16 == 0 && offsetof(PipeSmem<128>, inv) % 16 == 0 &&
+              offsetof(PipeSmem<128>, D) % 16 == 0 && offsetof(PipeSmem<128>, Kh) % 16 == 0, "LDS alignment");
+static_assert(offsetof(PipeSmem<64>, betas) % 16 == 0 && offsetof(PipeSmem<64>, inv) % 16 == 0 &&
+              offsetof(PipeSmem<64>, D) % 16 == 0 && offsetof(PipeSmem<64>, Kh) % 16 == 0, "LDS alignment");
+static_assert(sizeof(PipeSmem<128>) <= 160 * 1024, "LDS budget of one workgroup");
+
+// The q, k, g of one token row of one chunk, as raw storage bits.
 template <int DK, typename GT>
 struct RowIn {
     static constexpr int KB = DK / 32;
     Raw8<uint16_t> q[KB], k[KB];   // channels 32j + 8(lane/16) + 0..7
     Raw8<GT> g[KB];
-    GT beta;
 };
 
 // The four producer waves meet here; LDS writes before it are visible to all
@@ -153,50 +165,33 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
     }
     const int b = bh / H, h = bh % H;
     const int nchunks = (T + C - 1) / C;
-    auto row_qk = [&](int t) -> size_t { return ((size_t)b * T + t) * H + h; };
-
-    // ------------------------------------------------------------ producer state
-    const int m = wave;   // producer: tile
-    RowIn<DK, GT> in;     // inputs of the next chunk to prepare
-    auto load_row = [&](int c) {
-        const int t = c * C + TILE * m + r;
-        if (t < T) {
-            const size_t rr = row_qk(t);
-#pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                in.q[j].load(q + rr * DK + 32 * j + 8 * gq);
-                in.k[j].load(k + rr * DK + 32 * j + 8 * gq);
-                in.g[j].load(g + rr * DK + 32 * j + 8 * gq);
-            }
-            in.beta = beta[rr];
-        } else {   // identity token: no decay, no write, zero read
-#pragma unroll
-            for (int j = 0; j < KB; ++j) { in.q[j].zero(); in.k[j].zero(); in.g[j].zero(); }
-            in.beta = GT(0);
-        }
-    };
-
-    // ------------------------------------------------------------ consumer state
-    const int w = wave - NPROD;                 // consumer: column group
-    const int col0 = slab * WV + 16 * w;        // first value column of this consumer
-    const size_t s_base = (size_t)bh * DK * dv + col0 + r;
-    f32x4 S[KT];                                // rows 16kt + 4gq + i, column r
-    uint16_t vin[NT][4];                        // V rows 16mm + 4gq + i, column r
-    auto load_v = [&](int c) {
-#pragma unroll
-        for (int mm = 0; mm < NT; ++mm)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = c * C + TILE * mm + 4 * gq + i;
-                vin[mm][i] = t < T ? v[row_qk(t) * dv + col0 + r] : uint16_t(0);
-            }
-    };
 
     // Iteration c: the producers prepare chunk c + 1 into stage (c + 1) & 1
     // while the consumers run chunk c from stage c & 1.  Both roles run their
     // own loop; each iteration ends at the same workgroup barrier.
     if (producer) {
-        if (nchunks > 0) load_row(0);
+        const int m = wave;   // tile
+        RowIn<DK, GT> in;     // inputs of the next chunk to prepare
+        auto load_row = [&](int c, int r, int gq) {
+            const uint32_t lane_qk = (uint32_t)(r * H * DK + 8 * gq);
+            const size_t row0 = ((size_t)b * T + (size_t)c * C + TILE * m) * H + h;   // token 16m of chunk c
+            const uint16_t *qb = q + row0 * DK;
+            const uint16_t *kb = k + row0 * DK;
+            const GT *gb = g + row0 * DK;
+            if (c * C + TILE * m + r < T) {
+#pragma unroll
+                for (int j = 0; j < KB; ++j) {
+                    in.q[j].load(qb + lane_qk + 32 * j);
+                    in.k[j].load(kb + lane_qk + 32 * j);
+                    in.g[j].load(gb + lane_qk + 32 * j);
+                }
+            } else {   // identity token: no decay, no write, zero read
+#pragma unroll
+                for (int j = 0; j < KB; ++j) { in.q[j].zero(); in.k[j].zero(); in.g[j].zero(); }
+            }
+        };
+
+        if (nchunks > 0) load_row(0, r, gq);
         if (threadIdx.x == 0) sm.arrivals = 0;
         lds_barrier();
         unsigned meetings = 0;   // producer meetings so far (uniform)
@@ -204,6 +199,11 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             const int cn = c + 1;
             if (cn < nchunks) {
                 Stage &st = sm.stage[cn & 1];
+                // Lane coordinates made opaque here, so that no address derived from
+                // them is computed once before the loop and held in a register (or
+                // spilled) through it: every iteration recomputes what it uses.
+                int r = lane & 15, gq = lane >> 4;
+                asm volatile("" : "+v"(r), "+v"(gq));
 
                 // ---------------------------------------------- decays within tile m
                 float f[KB][8], rf[KB][8];
@@ -224,8 +224,22 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 }
                 lds_wave_sync();
 
-                // ---------------------------------------------- keys decayed to the end of tile m
+                // diagonal Gram tile, block (m, m): f-scaled rows against 1/f-scaled
+                // keys of the same tile, two-term bfloat16
+                f32x4 gq_d = {0.f, 0.f, 0.f, 0.f}, gk_d = {0.f, 0.f, 0.f, 0.f};
+                auto diagonal = [&](int j, const float (&qf)[8], const float (&kf)[8], const float (&ki)[8]) {
+                    BF::frag8 aqh, aql, bih, bil;
+                    BF::split8(qf, aqh, aql);
+                    BF::split8(ki, bih, bil);
+                    const BF::frag8 akh = BF::pack8(kf);
+                    gq_d = BF::mma32(aqh, bih, gq_d);
+                    gq_d = BF::mma32(aqh, bil, gq_d);
+                    gq_d = BF::mma32(aql, bih, gq_d);
+                    gk_d = BF::mma32(akh, bih, gk_d);
+                };
+
                 if (m < NT - 1) {
+                    // keys decayed to the end of tile m: B operands of the later tiles' Gram blocks
 #pragma unroll
                     for (int j = 0; j < KB; ++j) {
                         const int ch = 32 * j + 8 * gq;
@@ -240,12 +254,27 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         }
                         *reinterpret_cast<f16x8 *>(&sm.Kh[m][r * LDK + ch]) = h16::pack8(kh);
                     }
+                } else {
+                    // the last tile has no keys to hand on: it does its diagonal tile
+                    // here, while the others write theirs
+#pragma unroll
+                    for (int j = 0; j < KB; ++j) {
+                        float qv[8], kv[8], qf[8], kf[8], ki[8];
+                        in.q[j].to_f32(qv);
+                        in.k[j].to_f32(kv);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            qf[i] = qv[i] * f[j][i];
+                            kf[i] = kv[i] * f[j][i];
+                            ki[i] = kv[i] * rf[j][i];
+                        }
+                        diagonal(j, qf, kf, ki);
+                    }
                 }
                 meetings += 1;
                 producer_meet(&sm.arrivals, NPROD * meetings, lane);
 
                 // ---------------------------------------------- staged operands and block row m of the Gram
-                f32x4 gq_d = {0.f, 0.f, 0.f, 0.f}, gk_d = {0.f, 0.f, 0.f, 0.f};
                 f32x4 gq_o[NT - 1], gk_o[NT - 1];
 #pragma unroll
                 for (int d = 0; d < NT - 1; ++d) {
@@ -325,17 +354,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     *reinterpret_cast<f16x8 *>(&st.Kt[row]) = h16::pack8(kt);
                     *reinterpret_cast<f16x8 *>(&st.Kb[row]) = h16::pack8(kb);
 
-                    // diagonal tile: two-term bfloat16
-                    {
-                        BF::frag8 aqh, aql, bih, bil;
-                        BF::split8(qf, aqh, aql);
-                        BF::split8(ki, bih, bil);
-                        const BF::frag8 akh = BF::pack8(kf);
-                        gq_d = BF::mma32(aqh, bih, gq_d);
-                        gq_d = BF::mma32(aqh, bil, gq_d);
-                        gq_d = BF::mma32(aql, bih, gq_d);
-                        gk_d = BF::mma32(akh, bih, gk_d);
-                    }
+                    if (m < NT - 1) diagonal(j, qf, kf, ki);
                     // tiles n = m - d to the left: fp16
                     if (m >= 1) {
                         const f16x8 bk = h16::lds8(&sm.Kh[m - 1][r * LDK + ch]);
@@ -359,15 +378,13 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
                     }
                 }
-                if (gq == 0) st.beta[TILE * m + r] = to_f32(in.beta);
-
                 // q, k, g of chunk cn are consumed: fetch the next chunk's now so the
-                // loads land while the Gram results are stored and inverted
-                if (cn + 1 < nchunks) load_row(cn + 1);
+                // loads land while the Gram results are stored
+                if (cn + 1 < nchunks) load_row(cn + 1, r, gq);
                 lds_wave_sync();
 
                 // ---------------------------------------------- Gram results of block row m
-                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&st.beta[TILE * m + 4 * gq]);
+                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&sm.betas[cn % 3][TILE * m + 4 * gq]);
                 {
                     f32x4 aq, ak;
 #pragma unroll
@@ -377,7 +394,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
                     }
                     *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, m)][r * LDT + 4 * gq]) = h16::pack4(aq);
-                    *reinterpret_cast<f32x4 *>(&sm.LdT[m][r][4 * gq]) = ak;
+                    *reinterpret_cast<f32x4 *>(&st.LdT[m][r][4 * gq]) = ak;
                 }
 #pragma unroll
                 for (int d = 1; d < NT; ++d) {
@@ -389,40 +406,42 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             h16::pack4(gk_o[d - 1] * bet);
                     }
                 }
-                lds_wave_sync();
-
-                // ---------------------------------------------- (I + L_mm)^-1, lane column r
-                {
-                    // X = e_r; `one` is opaque so the 16 selects are not hoisted out of
-                    // the chunk loop (they would only occupy registers there)
-                    float one = 1.f;
-                    asm volatile("" : "+v"(one));
-                    float X[TILE];
-#pragma unroll
-                    for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
-#pragma unroll
-                    for (int jj = 0; jj < TILE - 1; ++jj) {
-                        float Lc[TILE];   // column jj of L_mm
-#pragma unroll
-                        for (int i4 = 0; i4 < TILE / 4; ++i4) {
-                            const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.LdT[m][jj][4 * i4]);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
-                        }
-#pragma unroll
-                        for (int ii = jj + 1; ii < TILE; ++ii) X[ii] -= Lc[ii] * X[jj];
-                    }
-                    // lane group gq stores rows 4gq..4gq+3 of column r
-                    f32x4 part;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
-                    *reinterpret_cast<f16x4 *>(&st.InvT[m][r * LDT + 4 * gq]) = h16::pack4(part);
-                }
             }
             lds_barrier();
         }
     } else {
+        const int w = wave - NPROD;                 // column group
+        const int col0 = slab * WV + 16 * w;        // first value column of this consumer
+        const size_t s_base = (size_t)bh * DK * dv + col0 + r;
+        const size_t Hdv = (size_t)H * dv;
+        const uint32_t lane_v = (uint32_t)(4 * gq * H * dv + r);   // rows 4gq + i, column r
+        _Float16 (&inv)[NT][TILE * LDT] = sm.inv[w];
+
+        f32x4 S[KT];          // rows 16kt + 4gq + i, column r
+        uint16_t vin[NT][4];  // V rows 16mm + 4gq + i, column r
+        auto load_v = [&](int c) {
+            const uint16_t *vb = v + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0;
+#pragma unroll
+            for (int mm = 0; mm < NT; ++mm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = c * C + TILE * mm + 4 * gq + i;
+                    vin[mm][i] = t < T ? vb[(size_t)(TILE * mm + i) * Hdv + lane_v] : uint16_t(0);
+                }
+        };
+
+        // beta: consumer 0 keeps the slots two chunks ahead, one token per lane
+        auto load_beta = [&](int c) -> GT {
+            const int t = c * C + lane;
+            return t < T ? beta[((size_t)b * T + t) * H + h] : GT(0);
+        };
+        GT bnext = GT(0);   // beta of chunk c + 2, written into its slot in iteration c
+        if (w == 0) {
+            sm.betas[0][lane] = nchunks > 0 ? to_f32(load_beta(0)) : 0.f;
+            sm.betas[1][lane] = nchunks > 1 ? to_f32(load_beta(1)) : 0.f;
+            if (nchunks > 2) bnext = load_beta(2);
+        }
+
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -440,6 +459,39 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                     for (int i = 0; i < 4; ++i) vc[mm][i] = vin[mm][i];
                 if (c + 1 < nchunks) load_v(c + 1);
+                if (w == 0 && c + 2 < nchunks) {
+                    sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
+                    if (c + 3 < nchunks) bnext = load_beta(c + 3);
+                }
+
+                // (I + L_mm)^-1 for all four tiles: lane group gq inverts block gq,
+                // lane r computes its column r by column-oriented forward substitution
+                {
+                    // X = e_r; `one` is opaque so the 16 selects are not hoisted out
+                    // of the chunk loop (they would only occupy registers there)
+                    float one = 1.f;
+                    asm volatile("" : "+v"(one));
+                    float X[TILE];
+#pragma unroll
+                    for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
+#pragma unroll
+                    for (int jj = 0; jj < TILE - 1; ++jj) {
+                        float Lc[TILE];   // column jj of L_gq
+#pragma unroll
+                        for (int i4 = 0; i4 < TILE / 4; ++i4) {
+                            const f32x4 x = *reinterpret_cast<const f32x4 *>(&st.LdT[gq][jj][4 * i4]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
+                        }
+#pragma unroll
+                        for (int ii = jj + 1; ii < TILE; ++ii) X[ii] -= Lc[ii] * X[jj];
+                    }
+                    // column r of the inverse is row r of its transpose
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        *reinterpret_cast<f16x4 *>(&inv[gq][r * LDT + 4 * a]) =
+                            h16::pack4(f32x4{X[4 * a], X[4 * a + 1], X[4 * a + 2], X[4 * a + 3]});
+                }
 
                 // state slab as fp16 B operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
                 f16x8 Sh[KB];
@@ -459,10 +511,11 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         aK = h16::mma32(h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]), Sh[j], aK);
                     }
                     accQ[mm] = aQ;
-                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(&st.beta[TILE * mm + 4 * gq]);
+                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(&sm.betas[c % 3][TILE * mm + 4 * gq]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) Y[mm][i] = bt[i] * (to_f32(vc[mm][i]) - aK[i]);
                 }
+                lds_wave_sync();   // the inverses written above are read below
 
                 // U = (I + L)^-1 Diag(beta) X, one tile at a time
                 const int tro = h16::tr_offset(lane, LDT);
@@ -476,14 +529,15 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         acc = h16::mma16(h16::tr4(&st.LT[strict_index(mm, n)][tro]), Uh[n], acc);
                     f16x4 rh, rl;
                     h16::split4(Y[mm] - acc, rh, rl);
-                    const f16x4 inv = h16::tr4(&st.InvT[mm][tro]);
-                    f32x4 u = h16::mma16(inv, rh, f32x4{0.f, 0.f, 0.f, 0.f});
-                    u = h16::mma16(inv, rl, u);
+                    const f16x4 a = h16::tr4(&inv[mm][tro]);
+                    f32x4 u = h16::mma16(a, rh, f32x4{0.f, 0.f, 0.f, 0.f});
+                    u = h16::mma16(a, rl, u);
                     U[mm] = u;
                     h16::split4(u, Uh[mm], Ul[mm]);
                 }
 
                 // O = (Gamma.Q) S + A_qk U, stored straight from the accumulators
+                OT *ob = o + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0;
 #pragma unroll
                 for (int mm = 0; mm < NT; ++mm) {
                     f32x4 acc = accQ[mm];
@@ -496,7 +550,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int t = c * C + TILE * mm + 4 * gq + i;
-                        if (t < T) o[row_qk(t) * dv + col0 + r] = from_f32<OT>(acc[i]);
+                        if (t < T) ob[(size_t)(TILE * mm + i) * Hdv + lane_v] = from_f32<OT>(acc[i]);
                     }
                 }
 
