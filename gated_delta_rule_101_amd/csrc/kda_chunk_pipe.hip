@@ -57,7 +57,8 @@ constexpr int NPROD = NT;         // producer waves: wave m prepares tile m
 constexpr int NCONS = 4;          // consumer waves: 16 value columns each
 constexpr int NTHREADS = 64 * (NPROD + NCONS);
 constexpr int WV = 16 * NCONS;    // value columns per workgroup
-constexpr int LDT = TILE + 4;     // row stride (elements) of a stored 16x16 tile
+constexpr int LDT = TILE;         // row stride (elements) of a stored 16x16 tile
+constexpr int LDL = TILE * TILE + 4;   // stride (floats) between the fp32 diagonal blocks of L
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr unsigned SPIN_LIMIT = 1u << 20;   // bound on every producer wait
 
@@ -69,15 +70,20 @@ constexpr int NSTRICT = NT * (NT - 1) / 2;
 
 template <int DK>
 struct alignas(16) PipeSmem {
-    static constexpr int LDK = DK + 8;   // token rows, 16 bytes of padding
+    // Row strides (elements).  Token rows read four-at-a-time along channels
+    // (Qt, Kt, Kh) are 16 bytes longer than a multiple of 256, so the 32 rows
+    // x 8 bytes of a half-wave read fall in distinct banks; K-bar is read
+    // transposed, four rows per 32-byte segment, and wants 32 bytes instead.
+    static constexpr int LDK = DK + 8;
+    static constexpr int LDKB = DK + 16;
     // What the consumers read for one chunk.
     struct alignas(16) Stage {
         _Float16 Qt[C * LDK];                   // Gamma . Q               [token][channel]
         _Float16 Kt[C * LDK];                   // Gamma . K               [token][channel]
-        _Float16 Kb[C * LDK];                   // K decayed to chunk end  [token][channel]
+        _Float16 Kb[C * LDKB];                  // K decayed to chunk end  [token][channel]
         _Float16 AqkT[NLOWER][TILE * LDT];      // tiles of A_qk, transposed: [s][t]
         _Float16 LT[NSTRICT][TILE * LDT];       // tiles of L, transposed
-        float LdT[NT][TILE][TILE];              // diagonal blocks of L (fp32): [m][col][row]
+        float LdT[NT * LDL];                    // diagonal blocks of L (fp32): [m][col][row]
         float GamC[DK];                         // total decay of the chunk
     };
     Stage stage[2];
@@ -100,12 +106,13 @@ static_assert(offsetof(PipeSmem<64>, betas) % 16 == 0 && offsetof(PipeSmem<64>, 
               offsetof(PipeSmem<64>, D) % 16 == 0 && offsetof(PipeSmem<64>, Kh) % 16 == 0, "LDS alignment");
 static_assert(sizeof(PipeSmem<128>) <= 160 * 1024, "LDS budget of one workgroup");
 
-// The q, k, g of one token row of one chunk, as raw storage bits.
+// The q, k, g of one token row of one chunk, as raw storage bits.  A producer
+// lane (g, r) holds token r of its tile, channels 16 blk + 4 g + (0..3).
 template <int DK, typename GT>
 struct RowIn {
-    static constexpr int KB = DK / 32;
-    Raw8<uint16_t> q[KB], k[KB];   // channels 32j + 8(lane/16) + 0..7
-    Raw8<GT> g[KB];
+    static constexpr int KT = DK / 16;
+    Raw4<uint16_t> q[KT], k[KT];
+    Raw4<GT> g[KT];
 };
 
 // The four producer waves meet here; LDS writes before it are visible to all
@@ -137,7 +144,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
     typedef Prec<true> BF;
     constexpr int KB = DK / 32;   // 32-channel blocks
     constexpr int KT = DK / 16;   // 16-channel tiles
-    constexpr int LDK = SM::LDK;
+    constexpr int LDK = SM::LDK, LDKB = SM::LDKB;
 
     __shared__ SM sm;
 
@@ -166,68 +173,112 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
     const int b = bh / H, h = bh % H;
     const int nchunks = (T + C - 1) / C;
 
-    // Iteration c: the producers prepare chunk c + 1 into stage (c + 1) & 1
-    // while the consumers run chunk c from stage c & 1.  Both roles run their
-    // own loop; each iteration ends at the same workgroup barrier.
+    // Between two workgroup barriers the producers prepare chunk c + 1 into
+    // stage (c + 1) & 1 while the consumers run chunk c from stage c & 1.  Each
+    // role runs its own loop; both pass the same nchunks + 2 barriers.
     if (producer) {
         const int m = wave;   // tile
         RowIn<DK, GT> in;     // inputs of the next chunk to prepare
-        auto load_row = [&](int c, int r, int gq) {
-            const uint32_t lane_qk = (uint32_t)(r * H * DK + 8 * gq);
-            const size_t row0 = ((size_t)b * T + (size_t)c * C + TILE * m) * H + h;   // token 16m of chunk c
-            const uint16_t *qb = q + row0 * DK;
-            const uint16_t *kb = k + row0 * DK;
-            const GT *gb = g + row0 * DK;
-            if (c * C + TILE * m + r < T) {
+        // Loads of chunk c: g as soon as the scan has consumed the previous
+        // chunk's, q and k once the staging has consumed theirs.  Every load
+        // is issued unconditionally (a token past the end reads the last
+        // token; its g is zeroed when used, and its zero beta keeps it from
+        // writing), so the loads in flight are always the same ones and
+        // waiting for g never waits for the younger q and k loads.
+        auto token_row = [&](int c, int r) -> size_t {
+            const int t = min(c * C + TILE * m + r, T - 1);
+            return ((size_t)b * T + t) * H + h;
+        };
+        auto load_g = [&](int c, int r, int gq) {
+            const GT *gb = g + token_row(c, r) * DK + 4 * gq;
 #pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    in.q[j].load(qb + lane_qk + 32 * j);
-                    in.k[j].load(kb + lane_qk + 32 * j);
-                    in.g[j].load(gb + lane_qk + 32 * j);
-                }
-            } else {   // identity token: no decay, no write, zero read
+            for (int blk = 0; blk < KT; ++blk) in.g[blk].load(gb + 16 * blk);
+        };
+        auto load_qk = [&](int c, int r, int gq) {
+            const size_t off = token_row(c, r) * DK + 4 * gq;
 #pragma unroll
-                for (int j = 0; j < KB; ++j) { in.q[j].zero(); in.k[j].zero(); in.g[j].zero(); }
+            for (int blk = 0; blk < KT; ++blk) {
+                in.q[blk].load(q + off + 16 * blk);
+                in.k[blk].load(k + off + 16 * blk);
             }
         };
 
-        if (nchunks > 0) load_row(0, r, gq);
         if (threadIdx.x == 0) sm.arrivals = 0;
+        if (nchunks == 0) {
+            lds_barrier();
+            lds_barrier();
+            return;
+        }
+        load_g(0, r, gq);
+        load_qk(0, r, gq);
         lds_barrier();
         unsigned meetings = 0;   // producer meetings so far (uniform)
-        for (int c = -1; c < nchunks; ++c) {
-            const int cn = c + 1;
-            if (cn < nchunks) {
+        for (int cn = 0; cn < nchunks; ++cn) {
+            {
                 Stage &st = sm.stage[cn & 1];
                 // Lane coordinates made opaque here, so that no address derived from
                 // them is computed once before the loop and held in a register (or
                 // spilled) through it: every iteration recomputes what it uses.
                 int r = lane & 15, gq = lane >> 4;
                 asm volatile("" : "+v"(r), "+v"(gq));
+                const bool live = cn * C + TILE * m + r < T;   // else: identity token
+                const int cnext = min(cn + 1, nchunks - 1);    // the last chunk reloads itself
 
                 // ---------------------------------------------- decays within tile m
-                float f[KB][8], rf[KB][8];
+                // b = inclusive cumsum of g over the tile's 16 tokens, per channel
+                float f[KT][4], rf[KT][4];   // f = e^b in [e^-80, 1], and 1/f
+                if constexpr (GBF) {
+                    // as a matrix-core product: b^T = g^T Tri, Tri(s, t) = [s <= t].
+                    // g goes through this tile's rows of the Qt staging area (rewritten
+                    // below), read back transposed: channels as rows, tokens as k-items.
+                    uint16_t *gs = reinterpret_cast<uint16_t *>(&st.Qt[TILE * m * LDK]);
 #pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    float gl[8];
-                    in.g[j].to_f32(gl);
+                    for (int blk = 0; blk < KT; ++blk)
+                        *reinterpret_cast<uint2 *>(&gs[r * LDK + 16 * blk + 4 * gq]) =
+                            live ? in.g[blk].a : make_uint2(0, 0);
+                    lds_wave_sync();
+                    i16x4 tri;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        f[j][i] = fast_exp2(row_inclusive_scan(gl[i] * LOG2E));
-                        rf[j][i] = fast_rcp(f[j][i]);
+                    for (int i = 0; i < 4; ++i) tri[i] = (4 * gq + i <= r) ? (short)0x3F80 : (short)0;   // bf16 1.0
+                    const int tro = h16::tr_offset(lane, LDK);
+#pragma unroll
+                    for (int blk = 0; blk < KT; ++blk) {
+                        const i16x4 gt = __builtin_bit_cast(
+                            i16x4, h16::tr4(reinterpret_cast<const _Float16 *>(&gs[16 * blk + tro])));
+                        const f32x4 bsum = BF::mma16(gt, tri, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            f[blk][i] = fast_exp2(bsum[i] * LOG2E);
+                            rf[blk][i] = fast_rcp(f[blk][i]);
+                        }
                     }
-                    if (r == TILE - 1) {
-                        float *d = &sm.D[m][32 * j + 8 * gq];
-                        *reinterpret_cast<f32x4 *>(d) = f32x4{f[j][0], f[j][1], f[j][2], f[j][3]};
-                        *reinterpret_cast<f32x4 *>(d + 4) = f32x4{f[j][4], f[j][5], f[j][6], f[j][7]};
+                } else {
+                    // float32 gates: a DPP scan across the 16 lanes of each row
+#pragma unroll
+                    for (int blk = 0; blk < KT; ++blk) {
+                        float gl[4];
+                        in.g[blk].to_f32(gl);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            f[blk][i] = fast_exp2(row_inclusive_scan(live ? gl[i] * LOG2E : 0.f));
+                            rf[blk][i] = fast_rcp(f[blk][i]);
+                        }
                     }
                 }
+                if (r == TILE - 1) {
+#pragma unroll
+                    for (int blk = 0; blk < KT; ++blk)
+                        *reinterpret_cast<f32x4 *>(&sm.D[m][16 * blk + 4 * gq]) =
+                            f32x4{f[blk][0], f[blk][1], f[blk][2], f[blk][3]};
+                }
+                load_g(cnext, r, gq);
                 lds_wave_sync();
 
                 // diagonal Gram tile, block (m, m): f-scaled rows against 1/f-scaled
-                // keys of the same tile, two-term bfloat16
+                // keys of the same tile, two-term bfloat16.  k-items of block pair p:
+                // channels 32p + 4gq + (0..3) and 32p + 16 + 4gq + (0..3).
                 f32x4 gq_d = {0.f, 0.f, 0.f, 0.f}, gk_d = {0.f, 0.f, 0.f, 0.f};
-                auto diagonal = [&](int j, const float (&qf)[8], const float (&kf)[8], const float (&ki)[8]) {
+                auto diagonal = [&](const float (&qf)[8], const float (&kf)[8], const float (&ki)[8]) {
                     BF::frag8 aqh, aql, bih, bil;
                     BF::split8(qf, aqh, aql);
                     BF::split8(ki, bih, bil);
@@ -241,34 +292,35 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 if (m < NT - 1) {
                     // keys decayed to the end of tile m: B operands of the later tiles' Gram blocks
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) {
-                        const int ch = 32 * j + 8 * gq;
-                        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&sm.D[m][ch]);
-                        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&sm.D[m][ch + 4]);
-                        float kv[8], kh[8];
-                        in.k[j].to_f32(kv);
+                    for (int blk = 0; blk < KT; ++blk) {
+                        const int ch = 16 * blk + 4 * gq;
+                        const f32x4 dm = *reinterpret_cast<const f32x4 *>(&sm.D[m][ch]);
+                        float kv[4];
+                        in.k[blk].to_f32(kv);
+                        f32x4 kh;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            kh[i] = kv[i] * rf[j][i] * d0[i];
-                            kh[4 + i] = kv[4 + i] * rf[j][4 + i] * d1[i];
-                        }
-                        *reinterpret_cast<f16x8 *>(&sm.Kh[m][r * LDK + ch]) = h16::pack8(kh);
+                        for (int i = 0; i < 4; ++i) kh[i] = kv[i] * rf[blk][i] * dm[i];
+                        *reinterpret_cast<f16x4 *>(&sm.Kh[m][r * LDK + ch]) = h16::pack4(kh);
                     }
                 } else {
                     // the last tile has no keys to hand on: it does its diagonal tile
                     // here, while the others write theirs
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) {
-                        float qv[8], kv[8], qf[8], kf[8], ki[8];
-                        in.q[j].to_f32(qv);
-                        in.k[j].to_f32(kv);
+                    for (int p = 0; p < KB; ++p) {
+                        float qf[8], kf[8], ki[8];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            qf[i] = qv[i] * f[j][i];
-                            kf[i] = kv[i] * f[j][i];
-                            ki[i] = kv[i] * rf[j][i];
+                        for (int hh = 0; hh < 2; ++hh) {
+                            float qv[4], kv[4];
+                            in.q[2 * p + hh].to_f32(qv);
+                            in.k[2 * p + hh].to_f32(kv);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                qf[4 * hh + i] = qv[i] * f[2 * p + hh][i];
+                                kf[4 * hh + i] = kv[i] * f[2 * p + hh][i];
+                                ki[4 * hh + i] = kv[i] * rf[2 * p + hh][i];
+                            }
                         }
-                        diagonal(j, qf, kf, ki);
+                        diagonal(qf, kf, ki);
                     }
                 }
                 meetings += 1;
@@ -282,87 +334,61 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     gk_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    const int ch = 32 * j + 8 * gq;
-                    float Dt[NT][8];
+                for (int p = 0; p < KB; ++p) {
+                    float qf[8], kf[8], ki[8], v2[8], v3[8];
 #pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
-                        const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch + 4]);
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int blk = 2 * p + hh;
+                        const int ch = 16 * blk + 4 * gq;
+                        f32x4 Dt[NT];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) { Dt[t][i] = x0[i]; Dt[t][4 + i] = x1[i]; }
-                    }
-                    // whole-tile decay before and after tile m (m is uniform per
-                    // wave), and across the tiles strictly between tile m and the
-                    // tiles m - 2, m - 3
-                    float before[8], after[8], Dm[8], v2[8], v3[8];
-                    switch (m) {
-                    case 0:
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            before[i] = 1.f; Dm[i] = Dt[0][i]; after[i] = Dt[1][i] * Dt[2][i] * Dt[3][i];
-                            v2[i] = 1.f; v3[i] = 1.f;
+                        for (int t = 0; t < NT; ++t) Dt[t] = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
+                        // whole-tile decay before and after tile m (m is uniform per
+                        // wave), and across the tiles strictly between tile m and the
+                        // tiles m - 2, m - 3
+                        f32x4 before, after, Dm, w2, w3;
+                        const f32x4 one = {1.f, 1.f, 1.f, 1.f};
+                        switch (m) {
+                        case 0: before = one; Dm = Dt[0]; after = Dt[1] * Dt[2] * Dt[3]; w2 = one; w3 = one; break;
+                        case 1: before = Dt[0]; Dm = Dt[1]; after = Dt[2] * Dt[3]; w2 = one; w3 = one; break;
+                        case 2: before = Dt[0] * Dt[1]; Dm = Dt[2]; after = Dt[3]; w2 = Dt[1]; w3 = one; break;
+                        default: before = Dt[0] * Dt[1] * Dt[2]; Dm = Dt[3]; after = one; w2 = Dt[2]; w3 = Dt[2] * Dt[1]; break;
                         }
-                        break;
-                    case 1:
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            before[i] = Dt[0][i]; Dm[i] = Dt[1][i]; after[i] = Dt[2][i] * Dt[3][i];
-                            v2[i] = 1.f; v3[i] = 1.f;
-                        }
-                        break;
-                    case 2:
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            before[i] = Dt[0][i] * Dt[1][i]; Dm[i] = Dt[2][i]; after[i] = Dt[3][i];
-                            v2[i] = Dt[1][i]; v3[i] = 1.f;
-                        }
-                        break;
-                    default:
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            before[i] = Dt[0][i] * Dt[1][i] * Dt[2][i]; Dm[i] = Dt[3][i]; after[i] = 1.f;
-                            v2[i] = Dt[2][i]; v3[i] = Dt[2][i] * Dt[1][i];
-                        }
-                        break;
-                    }
-                    if (m == 0 && r == 0) {
-                        f32x4 g0, g1;
+                        const f32x4 dma = Dm * after;   // from the tile start to the chunk end
+                        if (m == 0 && r == 0) *reinterpret_cast<f32x4 *>(&st.GamC[ch]) = dma;
+                        float qv[4], kv[4];
+                        in.q[blk].to_f32(qv);
+                        in.k[blk].to_f32(kv);
+                        f32x4 qt, kt, kb;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            g0[i] = after[i] * Dm[i];
-                            g1[i] = after[4 + i] * Dm[4 + i];
+                            const float fq = qv[i] * f[blk][i], fk = kv[i] * f[blk][i];
+                            const float ik = kv[i] * rf[blk][i];   // 1/f-scaled key, <= e^80 |k|
+                            qf[4 * hh + i] = fq;
+                            kf[4 * hh + i] = fk;
+                            ki[4 * hh + i] = ik;
+                            v2[4 * hh + i] = w2[i];
+                            v3[4 * hh + i] = w3[i];
+                            qt[i] = fq * before[i];
+                            kt[i] = fk * before[i];
+                            kb[i] = ik * dma[i];   // decayed to the chunk end, <= |k|
                         }
-                        *reinterpret_cast<f32x4 *>(&st.GamC[ch]) = g0;
-                        *reinterpret_cast<f32x4 *>(&st.GamC[ch + 4]) = g1;
+                        const int row = (TILE * m + r) * LDK + ch;
+                        *reinterpret_cast<f16x4 *>(&st.Qt[row]) = h16::pack4(qt);
+                        *reinterpret_cast<f16x4 *>(&st.Kt[row]) = h16::pack4(kt);
+                        *reinterpret_cast<f16x4 *>(&st.Kb[(TILE * m + r) * LDKB + ch]) = h16::pack4(kb);
                     }
-                    float qv[8], kv[8];
-                    in.q[j].to_f32(qv);
-                    in.k[j].to_f32(kv);
-                    float qf[8], kf[8], ki[8], qt[8], kt[8], kb[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        qf[i] = qv[i] * f[j][i];
-                        kf[i] = kv[i] * f[j][i];
-                        ki[i] = kv[i] * rf[j][i];            // 1/f-scaled key, <= e^80 |k|
-                        qt[i] = qf[i] * before[i];
-                        kt[i] = kf[i] * before[i];
-                        kb[i] = ki[i] * (Dm[i] * after[i]);  // decayed to the chunk end, <= |k|
-                    }
-                    const int row = (TILE * m + r) * LDK + ch;
-                    *reinterpret_cast<f16x8 *>(&st.Qt[row]) = h16::pack8(qt);
-                    *reinterpret_cast<f16x8 *>(&st.Kt[row]) = h16::pack8(kt);
-                    *reinterpret_cast<f16x8 *>(&st.Kb[row]) = h16::pack8(kb);
 
-                    if (m < NT - 1) diagonal(j, qf, kf, ki);
-                    // tiles n = m - d to the left: fp16
+                    if (m < NT - 1) diagonal(qf, kf, ki);
+                    // tiles n = m - d to the left: fp16, B = K-hat of tile n
+                    const int kh_off = r * LDK + 32 * p + 4 * gq;
                     if (m >= 1) {
-                        const f16x8 bk = h16::lds8(&sm.Kh[m - 1][r * LDK + ch]);
+                        const f16x8 bk = h16::lds4x2(&sm.Kh[m - 1][kh_off], &sm.Kh[m - 1][kh_off + 16]);
                         gq_o[0] = h16::mma32(h16::pack8(qf), bk, gq_o[0]);
                         gk_o[0] = h16::mma32(h16::pack8(kf), bk, gk_o[0]);
                     }
                     if (m >= 2) {
-                        const f16x8 bk = h16::lds8(&sm.Kh[m - 2][r * LDK + ch]);
+                        const f16x8 bk = h16::lds4x2(&sm.Kh[m - 2][kh_off], &sm.Kh[m - 2][kh_off + 16]);
                         float a[8], e[8];
 #pragma unroll
                         for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v2[i]; e[i] = kf[i] * v2[i]; }
@@ -370,7 +396,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         gk_o[1] = h16::mma32(h16::pack8(e), bk, gk_o[1]);
                     }
                     if (m >= 3) {
-                        const f16x8 bk = h16::lds8(&sm.Kh[m - 3][r * LDK + ch]);
+                        const f16x8 bk = h16::lds4x2(&sm.Kh[m - 3][kh_off], &sm.Kh[m - 3][kh_off + 16]);
                         float a[8], e[8];
 #pragma unroll
                         for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v3[i]; e[i] = kf[i] * v3[i]; }
@@ -378,9 +404,9 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
                     }
                 }
-                // q, k, g of chunk cn are consumed: fetch the next chunk's now so the
-                // loads land while the Gram results are stored
-                if (cn + 1 < nchunks) load_row(cn + 1, r, gq);
+
+                // q and k of chunk cn are consumed: fetch the next chunk's
+                load_qk(cnext, r, gq);
                 lds_wave_sync();
 
                 // ---------------------------------------------- Gram results of block row m
@@ -394,7 +420,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
                     }
                     *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, m)][r * LDT + 4 * gq]) = h16::pack4(aq);
-                    *reinterpret_cast<f32x4 *>(&st.LdT[m][r][4 * gq]) = ak;
+                    *reinterpret_cast<f32x4 *>(&st.LdT[m * LDL + r * TILE + 4 * gq]) = ak;
                 }
 #pragma unroll
                 for (int d = 1; d < NT; ++d) {
@@ -409,6 +435,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             }
             lds_barrier();
         }
+        lds_barrier();   // the consumers' last chunk
     } else {
         const int w = wave - NPROD;                 // column group
         const int col0 = slab * WV + 16 * w;        // first value column of this consumer
@@ -453,16 +480,6 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             if (c >= 0) {
                 const Stage &st = sm.stage[c & 1];
 
-                uint16_t vc[NT][4];
-#pragma unroll
-                for (int mm = 0; mm < NT; ++mm)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) vc[mm][i] = vin[mm][i];
-                if (c + 1 < nchunks) load_v(c + 1);
-                if (w == 0 && c + 2 < nchunks) {
-                    sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
-                    if (c + 3 < nchunks) bnext = load_beta(c + 3);
-                }
 
                 // (I + L_mm)^-1 for all four tiles: lane group gq inverts block gq,
                 // lane r computes its column r by column-oriented forward substitution
@@ -479,7 +496,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         float Lc[TILE];   // column jj of L_gq
 #pragma unroll
                         for (int i4 = 0; i4 < TILE / 4; ++i4) {
-                            const f32x4 x = *reinterpret_cast<const f32x4 *>(&st.LdT[gq][jj][4 * i4]);
+                            const f32x4 x = *reinterpret_cast<const f32x4 *>(&st.LdT[gq * LDL + jj * TILE + 4 * i4]);
 #pragma unroll
                             for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
                         }
@@ -488,9 +505,10 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     }
                     // column r of the inverse is row r of its transpose
 #pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        *reinterpret_cast<f16x4 *>(&inv[gq][r * LDT + 4 * a]) =
-                            h16::pack4(f32x4{X[4 * a], X[4 * a + 1], X[4 * a + 2], X[4 * a + 3]});
+                    for (int a = 0; a < 2; ++a)
+                        *reinterpret_cast<f16x8 *>(&inv[gq][r * LDT + 8 * a]) = h16::pack8(
+                            f32x4{X[8 * a], X[8 * a + 1], X[8 * a + 2], X[8 * a + 3]},
+                            f32x4{X[8 * a + 4], X[8 * a + 5], X[8 * a + 6], X[8 * a + 7]});
                 }
 
                 // state slab as fp16 B operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
@@ -513,8 +531,9 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     accQ[mm] = aQ;
                     const f32x4 bt = *reinterpret_cast<const f32x4 *>(&sm.betas[c % 3][TILE * mm + 4 * gq]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) Y[mm][i] = bt[i] * (to_f32(vc[mm][i]) - aK[i]);
+                    for (int i = 0; i < 4; ++i) Y[mm][i] = bt[i] * (to_f32(vin[mm][i]) - aK[i]);
                 }
+                if (w == 0 && c + 2 < nchunks) sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
                 lds_wave_sync();   // the inverses written above are read below
 
                 // U = (I + L)^-1 Diag(beta) X, one tile at a time
@@ -558,22 +577,28 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 f16x8 Ubh[2], Ubl[2];
                 h16::split8(U[0], U[1], Ubh[0], Ubl[0]);
                 h16::split8(U[2], U[3], Ubh[1], Ubl[1]);
-                const int tk = h16::tr_offset(lane, LDK);
+                const int tk = h16::tr_offset(lane, LDKB);
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
                     const f32x4 gcv = *reinterpret_cast<const f32x4 *>(&st.GamC[16 * kt + 4 * gq]);
                     f32x4 acc = S[kt] * gcv;
 #pragma unroll
                     for (int j2 = 0; j2 < 2; ++j2) {
-                        const _Float16 *base = &st.Kb[(32 * j2) * LDK + 16 * kt + tk];
+                        const _Float16 *base = &st.Kb[(32 * j2) * LDKB + 16 * kt + tk];
                         const f16x4 a0 = h16::tr4(base);
-                        const f16x4 a1 = h16::tr4(base + 16 * LDK);
+                        const f16x4 a1 = h16::tr4(base + 16 * LDKB);
                         const f16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                         acc = h16::mma32(a, Ubh[j2], acc);
                         acc = h16::mma32(a, Ubl[j2], acc);
                     }
                     S[kt] = acc;
                 }
+
+                // Next loads go out only now, after this chunk's output stores:
+                // vector-memory loads and stores complete out of order, so a wait
+                // for a load issued before a store is a wait for the store as well.
+                if (c + 1 < nchunks) load_v(c + 1);
+                if (w == 0 && c + 3 < nchunks) bnext = load_beta(c + 3);
             }
             lds_barrier();
         }

@@ -73,6 +73,26 @@ template <> struct Raw8<float> {
     }
 };
 
+// Raw bits of 4 consecutive storage elements.
+template <typename T> struct Raw4;
+template <> struct Raw4<uint16_t> {
+    uint2 a;
+    __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint2 *>(p); }
+    __device__ __forceinline__ void zero() { a = make_uint2(0, 0); }
+    __device__ __forceinline__ void to_f32(float (&x)[4]) const {
+        x[0] = __uint_as_float(a.x << 16);
+        x[1] = __uint_as_float(a.x & 0xffff0000u);
+        x[2] = __uint_as_float(a.y << 16);
+        x[3] = __uint_as_float(a.y & 0xffff0000u);
+    }
+};
+template <> struct Raw4<float> {
+    float4 a;
+    __device__ __forceinline__ void load(const float *p) { a = *reinterpret_cast<const float4 *>(p); }
+    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void to_f32(float (&x)[4]) const { x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; }
+};
+
 // ------------------------------------------------------ MFMA precisions
 
 
