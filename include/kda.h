@@ -84,12 +84,15 @@ typedef enum {
  *
  * Internal state is float32.  Contractions run on the matrix cores with
  * float32 accumulation: float32 operands when qkv_dtype == KDA_F32; for
- * KDA_BF16 inputs, bfloat16 operands, where the products the output is
- * sensitive to use a two-term (high + low bfloat16) split of both operands,
- * which carries about 16 significant bits.  out_dtype == KDA_F32 keeps the
- * output at that precision; KDA_BF16 rounds it once (the output of a
- * heavy-tailed workload can lose several percent of its RMS to that rounding
- * alone).
+ * KDA_BF16 inputs, fp16 operands (11 significant bits), with the state-update
+ * operand U and the right-hand sides of the diagonal solves carried as two
+ * fp16 terms, and two-term bfloat16 for the diagonal 16-token Gram tiles,
+ * whose 1/decay factor reaches e^80.  The fp16 operands need |v|, |S| and
+ * |o| below 65504 (true for unit-scale values and L2-normalised q and k, as
+ * the method uses them); beyond that the KDA_BF16 path produces inf.
+ * out_dtype == KDA_F32 keeps the output at accumulator precision; KDA_BF16
+ * rounds it once (the output of a heavy-tailed workload can lose several
+ * percent of its RMS to that rounding alone).
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
                            const void *g, const void *beta, const float *S0,
