@@ -14,13 +14,16 @@
 // matrix-core work fills the producer's vector-ALU gaps and the other way
 // round.
 //
-// Producer wave m, tile m (16 tokens, lane row r = token, 8 channels per
-// 32-channel block and lane group):
-//   decays  b = within-tile inclusive cumsum of g (DPP row scan), f = e^b in
-//           [e^-80, 1], 1/f <= e^80, tile totals D_m (to LDS).
+// Producer wave m, tile m (16 tokens; lane (g, r) holds token r and channels
+// 16 blk + 4g + 0..3):
+//   decays  b = within-tile inclusive cumsum of g (for bf16 gates one
+//           matrix-core product per 16 channels with a constant triangle, g
+//           read back transposed from LDS; for fp32 gates a DPP row scan),
+//           f = e^b in [e^-80, 1], tile totals D_m (to LDS).
 //   keys    K-hat_m: keys decayed to the end of tile m (B operands of the
-//           later tiles' Gram blocks), to LDS.  The four producers then
-//           meet at an LDS counter (the consumers are not involved).
+//           later tiles' Gram blocks), to LDS; the last tile does its
+//           diagonal Gram block meanwhile.  The four producers then meet at
+//           an LDS counter (the consumers are not involved).
 //   stage   Gamma.Q, Gamma.K (Gamma = decay from the chunk start) and K-bar
 //           (keys decayed to the chunk end), and block row m of
 //             A_qk (s <= t) and L = StrictLower(Diag(beta) A_kk),
@@ -58,7 +61,6 @@ constexpr int NCONS = 4;          // consumer waves: 16 value columns each
 constexpr int NTHREADS = 64 * (NPROD + NCONS);
 constexpr int WV = 16 * NCONS;    // value columns per workgroup
 constexpr int LDT = TILE;         // row stride (elements) of a stored 16x16 tile
-constexpr int LDL = TILE * TILE + 4;   // stride (floats) between the fp32 diagonal blocks of L
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr unsigned SPIN_LIMIT = 1u << 20;   // bound on every producer wait
 
@@ -83,7 +85,7 @@ struct alignas(16) PipeSmem {
         _Float16 Kb[C * LDKB];                  // K decayed to chunk end  [token][channel]
         _Float16 AqkT[NLOWER][TILE * LDT];      // tiles of A_qk, transposed: [s][t]
         _Float16 LT[NSTRICT][TILE * LDT];       // tiles of L, transposed
-        float LdT[NT * LDL];                    // diagonal blocks of L (fp32): [m][col][row]
+        _Float16 InvT[NT][TILE * LDT];          // (I + L_mm)^-1, transposed
         float GamC[DK];                         // total decay of the chunk
     };
     Stage stage[2];
@@ -93,16 +95,15 @@ struct alignas(16) PipeSmem {
     // beta of chunks c, c + 1, c + 2 (slot = chunk mod 3): written by a consumer
     // two iterations ahead, read by the producers one iteration ahead.
     alignas(16) float betas[3][C];
-    // Consumer scratch: each consumer's copy of the four (I + L_mm)^-1, transposed.
-    alignas(16) _Float16 inv[NCONS][NT][TILE * LDT];
+    alignas(16) float LdT[NT][TILE][TILE];      // diagonal blocks of L (fp32): [m][col][row]
     unsigned arrivals;                          // producer meeting counter
 };
 
 // Every array above is read with 8- or 16-byte LDS accesses.
 static_assert(sizeof(PipeSmem<64>::Stage) % 16 == 0 && sizeof(PipeSmem<128>::Stage) % 16 == 0, "stage alignment");
-static_assert(offsetof(PipeSmem<128>, betas) % 16 == 0 && offsetof(PipeSmem<128>, inv) % 16 == 0 &&
+static_assert(offsetof(PipeSmem<128>, betas) % 16 == 0 && offsetof(PipeSmem<128>, LdT) % 16 == 0 &&
               offsetof(PipeSmem<128>, D) % 16 == 0 && offsetof(PipeSmem<128>, Kh) % 16 == 0, "LDS alignment");
-static_assert(offsetof(PipeSmem<64>, betas) % 16 == 0 && offsetof(PipeSmem<64>, inv) % 16 == 0 &&
+static_assert(offsetof(PipeSmem<64>, betas) % 16 == 0 && offsetof(PipeSmem<64>, LdT) % 16 == 0 &&
               offsetof(PipeSmem<64>, D) % 16 == 0 && offsetof(PipeSmem<64>, Kh) % 16 == 0, "LDS alignment");
 static_assert(sizeof(PipeSmem<128>) <= 160 * 1024, "LDS budget of one workgroup");
 
@@ -226,7 +227,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 
                 // ---------------------------------------------- decays within tile m
                 // b = inclusive cumsum of g over the tile's 16 tokens, per channel
-                float f[KT][4], rf[KT][4];   // f = e^b in [e^-80, 1], and 1/f
+                float f[KT][4];   // f = e^b in [e^-80, 1] (1/f, up to e^80, is recomputed where used)
                 if constexpr (GBF) {
                     // as a matrix-core product: b^T = g^T Tri, Tri(s, t) = [s <= t].
                     // g goes through this tile's rows of the Qt staging area (rewritten
@@ -247,10 +248,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             i16x4, h16::tr4(reinterpret_cast<const _Float16 *>(&gs[16 * blk + tro])));
                         const f32x4 bsum = BF::mma16(gt, tri, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            f[blk][i] = fast_exp2(bsum[i] * LOG2E);
-                            rf[blk][i] = fast_rcp(f[blk][i]);
-                        }
+                        for (int i = 0; i < 4; ++i) f[blk][i] = fast_exp2(bsum[i] * LOG2E);
                     }
                 } else {
                     // float32 gates: a DPP scan across the 16 lanes of each row
@@ -259,10 +257,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         float gl[4];
                         in.g[blk].to_f32(gl);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
+                        for (int i = 0; i < 4; ++i)
                             f[blk][i] = fast_exp2(row_inclusive_scan(live ? gl[i] * LOG2E : 0.f));
-                            rf[blk][i] = fast_rcp(f[blk][i]);
-                        }
                     }
                 }
                 if (r == TILE - 1) {
@@ -299,7 +295,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         in.k[blk].to_f32(kv);
                         f32x4 kh;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) kh[i] = kv[i] * rf[blk][i] * dm[i];
+                        for (int i = 0; i < 4; ++i) kh[i] = kv[i] * fast_rcp(f[blk][i]) * dm[i];
                         *reinterpret_cast<f16x4 *>(&sm.Kh[m][r * LDK + ch]) = h16::pack4(kh);
                     }
                 } else {
@@ -317,7 +313,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             for (int i = 0; i < 4; ++i) {
                                 qf[4 * hh + i] = qv[i] * f[2 * p + hh][i];
                                 kf[4 * hh + i] = kv[i] * f[2 * p + hh][i];
-                                ki[4 * hh + i] = kv[i] * rf[2 * p + hh][i];
+                                ki[4 * hh + i] = kv[i] * fast_rcp(f[2 * p + hh][i]);
                             }
                         }
                         diagonal(qf, kf, ki);
@@ -363,7 +359,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float fq = qv[i] * f[blk][i], fk = kv[i] * f[blk][i];
-                            const float ik = kv[i] * rf[blk][i];   // 1/f-scaled key, <= e^80 |k|
+                            const float ik = kv[i] * fast_rcp(f[blk][i]);   // 1/f-scaled key, <= e^80 |k|
                             qf[4 * hh + i] = fq;
                             kf[4 * hh + i] = fk;
                             ki[4 * hh + i] = ik;
@@ -420,7 +416,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
                     }
                     *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, m)][r * LDT + 4 * gq]) = h16::pack4(aq);
-                    *reinterpret_cast<f32x4 *>(&st.LdT[m * LDL + r * TILE + 4 * gq]) = ak;
+                    *reinterpret_cast<f32x4 *>(&sm.LdT[m][r][4 * gq]) = ak;
                 }
 #pragma unroll
                 for (int d = 1; d < NT; ++d) {
@@ -432,6 +428,32 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             h16::pack4(gk_o[d - 1] * bet);
                     }
                 }
+                lds_wave_sync();
+
+                // ------------------------------------------ (I + L_mm)^-1, lane column r
+                {
+                    // column r of L_mm, and X = e_r; `one` is opaque so the 16 selects
+                    // are not hoisted out of the chunk loop
+                    float Lc[TILE];
+#pragma unroll
+                    for (int i4 = 0; i4 < TILE / 4; ++i4) {
+                        const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.LdT[m][r][4 * i4]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
+                    }
+                    float one = 1.f;
+                    asm volatile("" : "+v"(one));
+                    float X[TILE];
+#pragma unroll
+                    for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
+                    unit_lower_inverse_steps<0>(X, Lc);
+                    // lane group gq stores rows 4gq..4gq+3 of column r (row r of the transpose)
+                    f32x4 part;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
+                    *reinterpret_cast<f16x4 *>(&st.InvT[m][r * LDT + 4 * gq]) = h16::pack4(part);
+                }
             }
             lds_barrier();
         }
@@ -442,19 +464,28 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         const size_t s_base = (size_t)bh * DK * dv + col0 + r;
         const size_t Hdv = (size_t)H * dv;
         const uint32_t lane_v = (uint32_t)(4 * gq * H * dv + r);   // rows 4gq + i, column r
-        _Float16 (&inv)[NT][TILE * LDT] = sm.inv[w];
 
         f32x4 S[KT];          // rows 16kt + 4gq + i, column r
         uint16_t vin[NT][4];  // V rows 16mm + 4gq + i, column r
+        // V of chunk c.  A token past the end reads the last token instead (its
+        // beta is zero, so its value never enters U); a full chunk needs no
+        // clamping and addresses every row from one uniform base.
         auto load_v = [&](int c) {
-            const uint16_t *vb = v + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0;
+            if ((c + 1) * C <= T) {
+                const uint16_t *vb = v + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0 + lane_v;
 #pragma unroll
-            for (int mm = 0; mm < NT; ++mm)
+                for (int mm = 0; mm < NT; ++mm)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = c * C + TILE * mm + 4 * gq + i;
-                    vin[mm][i] = t < T ? vb[(size_t)(TILE * mm + i) * Hdv + lane_v] : uint16_t(0);
-                }
+                    for (int i = 0; i < 4; ++i) vin[mm][i] = vb[(size_t)(TILE * mm + i) * Hdv];
+            } else {
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = min(c * C + TILE * mm + 4 * gq + i, T - 1);
+                        vin[mm][i] = v[(((size_t)b * T + t) * H + h) * dv + col0 + r];
+                    }
+            }
         };
 
         // beta: consumer 0 keeps the slots two chunks ahead, one token per lane
@@ -481,36 +512,6 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 const Stage &st = sm.stage[c & 1];
 
 
-                // (I + L_mm)^-1 for all four tiles: lane group gq inverts block gq,
-                // lane r computes its column r by column-oriented forward substitution
-                {
-                    // X = e_r; `one` is opaque so the 16 selects are not hoisted out
-                    // of the chunk loop (they would only occupy registers there)
-                    float one = 1.f;
-                    asm volatile("" : "+v"(one));
-                    float X[TILE];
-#pragma unroll
-                    for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
-#pragma unroll
-                    for (int jj = 0; jj < TILE - 1; ++jj) {
-                        float Lc[TILE];   // column jj of L_gq
-#pragma unroll
-                        for (int i4 = 0; i4 < TILE / 4; ++i4) {
-                            const f32x4 x = *reinterpret_cast<const f32x4 *>(&st.LdT[gq * LDL + jj * TILE + 4 * i4]);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
-                        }
-#pragma unroll
-                        for (int ii = jj + 1; ii < TILE; ++ii) X[ii] -= Lc[ii] * X[jj];
-                    }
-                    // column r of the inverse is row r of its transpose
-#pragma unroll
-                    for (int a = 0; a < 2; ++a)
-                        *reinterpret_cast<f16x8 *>(&inv[gq][r * LDT + 8 * a]) = h16::pack8(
-                            f32x4{X[8 * a], X[8 * a + 1], X[8 * a + 2], X[8 * a + 3]},
-                            f32x4{X[8 * a + 4], X[8 * a + 5], X[8 * a + 6], X[8 * a + 7]});
-                }
-
                 // state slab as fp16 B operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
                 f16x8 Sh[KB];
 #pragma unroll
@@ -534,7 +535,6 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     for (int i = 0; i < 4; ++i) Y[mm][i] = bt[i] * (to_f32(vin[mm][i]) - aK[i]);
                 }
                 if (w == 0 && c + 2 < nchunks) sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
-                lds_wave_sync();   // the inverses written above are read below
 
                 // U = (I + L)^-1 Diag(beta) X, one tile at a time
                 const int tro = h16::tr_offset(lane, LDT);
@@ -548,7 +548,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         acc = h16::mma16(h16::tr4(&st.LT[strict_index(mm, n)][tro]), Uh[n], acc);
                     f16x4 rh, rl;
                     h16::split4(Y[mm] - acc, rh, rl);
-                    const f16x4 a = h16::tr4(&inv[mm][tro]);
+                    const f16x4 a = h16::tr4(&st.InvT[mm][tro]);
                     f32x4 u = h16::mma16(a, rh, f32x4{0.f, 0.f, 0.f, 0.f});
                     u = h16::mma16(a, rl, u);
                     U[mm] = u;
@@ -556,7 +556,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 }
 
                 // O = (Gamma.Q) S + A_qk U, stored straight from the accumulators
-                OT *ob = o + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0;
+                OT *ob = o + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0 + lane_v;
+                const bool full = (c + 1) * C <= T;   // uniform: every row of the chunk is real
 #pragma unroll
                 for (int mm = 0; mm < NT; ++mm) {
                     f32x4 acc = accQ[mm];
@@ -569,7 +570,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int t = c * C + TILE * mm + 4 * gq + i;
-                        if (t < T) ob[(size_t)(TILE * mm + i) * Hdv + lane_v] = from_f32<OT>(acc[i]);
+                        if (full || t < T) ob[(size_t)(TILE * mm + i) * Hdv] = from_f32<OT>(acc[i]);
                     }
                 }
 

@@ -334,6 +334,24 @@ __device__ __forceinline__ void lds_wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Forward substitution for the inverse of a unit lower-triangular 16x16 block,
+// one column per lane: on entry lane i of each 16-lane row holds column i of
+// the strictly lower part (Lc[ii] = L[ii][i]) and X = e_i; on exit X is column
+// i of (I + L)^-1.  Step JJ needs L[ii][JJ] in every lane of the row: that is
+// lane JJ's Lc[ii], taken by a DPP row broadcast fused into the FMA
+// (v_fmac_f32 with row_newbcast:JJ).  The broadcast sources are only ever
+// written by loads, never by a vector-ALU instruction, so no DPP read follows
+// a VALU write of its source.
+template <int JJ>
+__device__ __forceinline__ void unit_lower_inverse_steps(float (&X)[16], const float (&Lc)[16]) {
+    const float nx = -X[JJ];
+#pragma unroll
+    for (int ii = JJ + 1; ii < 16; ++ii)
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(X[ii]) : "v"(Lc[ii]), "v"(nx), "i"(JJ));
+    if constexpr (JJ + 2 < 16) unit_lower_inverse_steps<JJ + 1>(X, Lc);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
