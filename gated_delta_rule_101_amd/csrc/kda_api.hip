@@ -19,13 +19,16 @@ bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
-                           const void *beta, const float *S0, void *o, float *S_final,
-                           int B, int T, int H, int dk, int dv,
-                           kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
-                           void *stream)
+// Host-side checks shared by every chunked entry point.  `o` and `q` may be
+// absent only where the caller says so (commit writes no output and reads no
+// query).  Returns KDA_OK when the launch may proceed.
+kda_status_t check_chunk(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                         const float *S0, const void *o, const float *S_final, const float *A_log,
+                         const int *lengths, int B, int T, int H, int dk, int dv,
+                         kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                         bool need_q, bool need_o)
 {
     if (B < 0 || T < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
@@ -34,34 +37,51 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     if (dv % 64 != 0 || dv > 512) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)B * T >= ((int64_t)1 << 31) || (int64_t)B * H * (dv / 64) >= ((int64_t)1 << 31))
         return KDA_ERR_UNSUPPORTED;
-    if (B == 0 || H == 0) return KDA_OK;   // nothing to compute
+    if (B == 0 || H == 0) return KDA_OK;
 
     const size_t tok = (size_t)B * T * H;
     const size_t sq = dsize(qkv_dtype), sg = dsize(gate_dtype), so = dsize(out_dtype);
-    const Span sp_q = span(q, tok * dk * sq), sp_k = span(k, tok * dk * sq);
-    const Span sp_v = span(v, tok * dv * sq), sp_o = span(o, tok * dv * so);
+    const Span sp_q = span(need_q ? q : nullptr, need_q ? tok * dk * sq : 0), sp_k = span(k, tok * dk * sq);
+    const Span sp_v = span(v, tok * dv * sq), sp_o = span(need_o ? o : nullptr, need_o ? tok * dv * so : 0);
     const Span sp_g = span(g, tok * dk * sg), sp_b = span(beta, tok * sg);
+    const Span sp_a = span(A_log, A_log ? (size_t)H * sizeof(float) : 0);
+    const Span sp_l = span(lengths, lengths ? (size_t)B * sizeof(int) : 0);
     const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
     const Span sp_s0 = span(S0, S0 ? state_bytes : 0), sp_sf = span(S_final, S_final ? state_bytes : 0);
 
     if (T > 0) {
-        if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o))
+        if ((need_q && !q) || !k || !v || !g || !beta || (need_o && !o)) return KDA_ERR_INVALID_ARG;
+        if ((need_q && !aligned16(q)) || !aligned16(k) || !aligned16(v) || !aligned16(g) || (need_o && !aligned16(o)))
             return KDA_ERR_INVALID_ARG;
-        const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b, sp_s0, sp_sf};
-        for (const Span &s : ins)
-            if (overlap(sp_o, s)) return KDA_ERR_INVALID_ARG;
+        if (need_o) {
+            const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b, sp_s0, sp_sf, sp_a, sp_l};
+            for (const Span &s : ins)
+                if (overlap(sp_o, s)) return KDA_ERR_INVALID_ARG;
+        }
     }
     if ((S0 && !aligned16(S0)) || (S_final && !aligned16(S_final))) return KDA_ERR_INVALID_ARG;
+    if ((A_log && ((uintptr_t)A_log & 3u)) || (lengths && ((uintptr_t)lengths & 3u))) return KDA_ERR_INVALID_ARG;
     if (S_final) {
-        const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b};
+        const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b, sp_a, sp_l};
         if (T > 0)
             for (const Span &s : ins)
                 if (overlap(sp_sf, s)) return KDA_ERR_INVALID_ARG;
         if (S0 && S0 != S_final && overlap(sp_sf, sp_s0)) return KDA_ERR_INVALID_ARG;
     }
-    if (T == 0 && !S_final) return KDA_OK;
+    return KDA_OK;
+}
 
+kda_status_t run_chunk(kda::ChunkFwdArgs &a, void *stream)
+{
+    if (a.B == 0 || a.H == 0) return KDA_OK;
+    if (a.T == 0 && !a.S_final) return KDA_OK;
+    return kda::launch_chunk_fwd(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda::ChunkFwdArgs chunk_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                             const float *S0, void *o, float *S_final, int B, int T, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype)
+{
     kda::ChunkFwdArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
     a.S0 = S0; a.o = o; a.S_final = S_final;
@@ -69,13 +89,12 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const vo
     a.qkv_bf16 = qkv_dtype == KDA_BF16;
     a.gate_bf16 = gate_dtype == KDA_BF16;
     a.out_bf16 = out_dtype == KDA_BF16;
-    return kda::launch_chunk_fwd(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return a;
 }
 
-kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,
-                             const void *beta, float *S, void *o, int B, int H, int dk, int dv,
-                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
-                             void *stream)
+kda_status_t decode(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                    const float *A_log, float *S, void *o, int B, int H, int dk, int dv,
+                    kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype, void *stream)
 {
     if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
@@ -85,24 +104,110 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     if (B == 0 || H == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
     if (!aligned16(S)) return KDA_ERR_INVALID_ARG;
+    if (A_log && ((uintptr_t)A_log & 3u)) return KDA_ERR_INVALID_ARG;
 
     const size_t n = (size_t)B * H;
     const size_t sq = dsize(qkv_dtype), sg = dsize(gate_dtype), so = dsize(out_dtype);
     const Span sp_q = span(q, n * dk * sq), sp_k = span(k, n * dk * sq), sp_v = span(v, n * dv * sq);
     const Span sp_g = span(g, n * dk * sg), sp_b = span(beta, n * sg);
+    const Span sp_a = span(A_log, A_log ? (size_t)H * sizeof(float) : 0);
     const Span sp_s = span(S, n * dk * dv * sizeof(float)), sp_o = span(o, n * dv * so);
-    const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b};
+    const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b, sp_a};
     for (const Span &s : ins)
         if (overlap(sp_o, s) || overlap(sp_s, s)) return KDA_ERR_INVALID_ARG;
     if (overlap(sp_o, sp_s)) return KDA_ERR_INVALID_ARG;
 
     kda::DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o; a.A_log = A_log;
     a.B = B; a.H = H; a.dk = dk; a.dv = dv;
     a.qkv_bf16 = qkv_dtype == KDA_BF16;
     a.gate_bf16 = gate_dtype == KDA_BF16;
     a.out_bf16 = out_dtype == KDA_BF16;
     return kda::launch_decode_step(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g,
+                           const void *beta, const float *S0, void *o, float *S_final,
+                           int B, int T, int H, int dk, int dv,
+                           kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                           void *stream)
+{
+    const kda_status_t st = check_chunk(q, k, v, g, beta, S0, o, S_final, nullptr, nullptr, B, T, H, dk, dv,
+                                        qkv_dtype, gate_dtype, out_dtype, true, true);
+    if (st != KDA_OK) return st;
+    kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S0, o, S_final, B, T, H, dk, dv,
+                                     qkv_dtype, gate_dtype, out_dtype);
+    return run_chunk(a, stream);
+}
+
+kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v, const void *z,
+                                const float *A_log, const void *beta, const float *S0, void *o,
+                                float *S_final, int B, int T, int H, int dk, int dv,
+                                kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                void *stream)
+{
+    if (!A_log && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
+    const kda_status_t st = check_chunk(q, k, v, z, beta, S0, o, S_final, A_log, nullptr, B, T, H, dk, dv,
+                                        qkv_dtype, gate_dtype, out_dtype, true, true);
+    if (st != KDA_OK) return st;
+    kda::ChunkFwdArgs a = chunk_args(q, k, v, z, beta, S0, o, S_final, B, T, H, dk, dv,
+                                     qkv_dtype, gate_dtype, out_dtype);
+    a.A_log = A_log;
+    return run_chunk(a, stream);
+}
+
+kda_status_t kda_verify_step(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, const float *S, void *o,
+                             int B, int K, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                             void *stream)
+{
+    if (!S && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
+    const kda_status_t st = check_chunk(q, k, v, g, beta, S, o, nullptr, nullptr, nullptr, B, K, H, dk, dv,
+                                        qkv_dtype, gate_dtype, out_dtype, true, true);
+    if (st != KDA_OK) return st;
+    if (K == 0) return KDA_OK;
+    kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S, o, nullptr, B, K, H, dk, dv,
+                                     qkv_dtype, gate_dtype, out_dtype);
+    return run_chunk(a, stream);
+}
+
+kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const void *beta,
+                             const int *accepted, float *S, int B, int K, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, void *stream)
+{
+    if ((!S || !accepted) && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
+    const kda_status_t st = check_chunk(nullptr, k, v, g, beta, S, nullptr, S, nullptr, accepted, B, K, H,
+                                        dk, dv, qkv_dtype, gate_dtype, KDA_F32, false, false);
+    if (st != KDA_OK) return st;
+    if (K == 0) return KDA_OK;
+    // the kernels read a query row for every token; the keys stand in (no output is written)
+    kda::ChunkFwdArgs a = chunk_args(k, k, v, g, beta, S, nullptr, S, B, K, H, dk, dv,
+                                     qkv_dtype, gate_dtype, KDA_F32);
+    a.lengths = accepted;
+    return run_chunk(a, stream);
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const void *g,
+                             const void *beta, float *S, void *o, int B, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                             void *stream)
+{
+    return decode(q, k, v, g, beta, nullptr, S, o, B, H, dk, dv, qkv_dtype, gate_dtype, out_dtype, stream);
+}
+
+kda_status_t kda_decode_step_gate(const void *q, const void *k, const void *v, const void *z,
+                                  const float *A_log, const void *beta, float *S, void *o,
+                                  int B, int H, int dk, int dv,
+                                  kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                  void *stream)
+{
+    if (!A_log && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
+    return decode(q, k, v, z, beta, A_log, S, o, B, H, dk, dv, qkv_dtype, gate_dtype, out_dtype, stream);
 }
 
 const char *kda_status_string(kda_status_t status)

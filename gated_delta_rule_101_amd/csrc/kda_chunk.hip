@@ -100,7 +100,7 @@ struct ChunkIn {
     QT v[NT][4];             // rows 16m + 4(lane/16) + i, column 16*wave + lane%16 of the slab
 };
 
-template <int DK, bool QBF, bool GBF, bool OBF>
+template <int DK, bool QBF, bool GBF, bool OBF, bool GL>
 __global__ void __launch_bounds__(NTHREADS, 1)
 kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
                      const typename Store<QBF>::type *__restrict__ k,
@@ -108,7 +108,8 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
                      const typename Store<GBF>::type *__restrict__ g,
                      const typename Store<GBF>::type *__restrict__ beta,
                      const float *S0, typename Store<OBF>::type *__restrict__ o,
-                     float *S_final, int B, int T, int H, int dv, int nslab)
+                     float *S_final, const int *__restrict__ lengths, const float *__restrict__ A_log,
+                     int B, int T, int H, int dv, int nslab)
 {
     typedef Prec<QBF> P;
     typedef typename P::elem E;
@@ -152,6 +153,9 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
     const int b = bh / H, h = bh % H;
     const int col0 = slab * WV + 16 * wave;   // first value column owned by this wave
     const int nchunks = (T + C - 1) / C;
+    // tokens from `len` on are identity tokens (no decay, no write)
+    const int len = lengths ? max(0, min(lengths[b], T)) : T;
+    const float gate_scale = GL ? __expf(A_log[h]) : 1.f;   // exp(A_h), gate logits only
 
     auto row_qk = [&](int t) -> size_t { return ((size_t)b * T + t) * H + h; };
 
@@ -166,7 +170,7 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
 
     auto load_chunk = [&](ChunkIn<DK, QT, GT> &in, int c) {
         const int t = c * C + TILE * wave + r;
-        if (t < T) {
+        if (t < len) {
             const size_t rr = row_qk(t);
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
@@ -204,6 +208,11 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
         for (int j = 0; j < KB; ++j) {
             float gl[8];
             cur.g[j].to_f32(gl);
+            if constexpr (GL) {   // an identity token keeps g = 0, not the gate of logit 0
+                const bool live = c * C + TILE * m + r < len;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) gl[i] = live ? gate_from_logit(gl[i], gate_scale) : 0.f;
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 fdec[j][i] = fast_exp2(row_inclusive_scan(gl[i] * LOG2E));
@@ -498,7 +507,7 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = c * C + TILE * mm + 4 * gq + i;
-                if (t < T) o[row_qk(t) * dv + col0 + r] = from_f32<OT>(acc[i]);
+                if (o && t < T) o[row_qk(t) * dv + col0 + r] = from_f32<OT>(acc[i]);
             }
         }
 
@@ -535,7 +544,7 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
     }
 }
 
-template <int DK, bool QBF, bool GBF, bool OBF>
+template <int DK, bool QBF, bool GBF, bool OBF, bool GL>
 hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
 {
     typedef typename Store<QBF>::type QT;
@@ -543,16 +552,22 @@ hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
     typedef typename Store<OBF>::type OT;
     const int nslab = a.dv / WV;
     const unsigned grid = (unsigned)(a.B * a.H * nslab);
-    kda_chunk_fwd_kernel<DK, QBF, GBF, OBF><<<grid, NTHREADS, 0, stream>>>(
+    kda_chunk_fwd_kernel<DK, QBF, GBF, OBF, GL><<<grid, NTHREADS, 0, stream>>>(
         (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta,
-        a.S0, (OT *)a.o, a.S_final, a.B, a.T, a.H, a.dv, nslab);
+        a.S0, (OT *)a.o, a.S_final, a.lengths, a.A_log, a.B, a.T, a.H, a.dv, nslab);
     return hipGetLastError();
+}
+
+template <int DK, bool QBF, bool GBF, bool GL>
+hipError_t dispatch_gate(const ChunkFwdArgs &a, hipStream_t s)
+{
+    return a.out_bf16 ? launch<DK, QBF, GBF, true, GL>(a, s) : launch<DK, QBF, GBF, false, GL>(a, s);
 }
 
 template <int DK, bool QBF, bool GBF>
 hipError_t dispatch_out(const ChunkFwdArgs &a, hipStream_t s)
 {
-    return a.out_bf16 ? launch<DK, QBF, GBF, true>(a, s) : launch<DK, QBF, GBF, false>(a, s);
+    return a.A_log ? dispatch_gate<DK, QBF, GBF, true>(a, s) : dispatch_gate<DK, QBF, GBF, false>(a, s);
 }
 
 template <int DK>

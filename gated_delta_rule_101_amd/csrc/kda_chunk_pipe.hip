@@ -130,12 +130,13 @@ __device__ __forceinline__ void producer_meet(unsigned *arrivals, unsigned targe
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int DK, bool GBF, bool OBF>
+template <int DK, bool GBF, bool OBF, bool GL>
 __global__ void __launch_bounds__(NTHREADS, 1)
 kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                       const uint16_t *__restrict__ v, const typename Store<GBF>::type *__restrict__ g,
                       const typename Store<GBF>::type *__restrict__ beta, const float *S0,
                       typename Store<OBF>::type *__restrict__ o, float *S_final,
+                      const int *__restrict__ lengths, const float *__restrict__ A_log,
                       int B, int T, int H, int dv, int nslab)
 {
     typedef typename Store<GBF>::type GT;
@@ -173,12 +174,15 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
     }
     const int b = bh / H, h = bh % H;
     const int nchunks = (T + C - 1) / C;
+    // tokens from `len` on are identity tokens (no decay, no write)
+    const int len = lengths ? max(0, min(lengths[b], T)) : T;
 
     // Between two workgroup barriers the producers prepare chunk c + 1 into
     // stage (c + 1) & 1 while the consumers run chunk c from stage c & 1.  Each
     // role runs its own loop; both pass the same nchunks + 2 barriers.
     if (producer) {
         const int m = wave;   // tile
+        const float gate_scale = GL ? __expf(A_log[h]) : 1.f;   // exp(A_h), gate logits only
         RowIn<DK, GT> in;     // inputs of the next chunk to prepare
         // Loads of chunk c: g as soon as the scan has consumed the previous
         // chunk's, q and k once the staging has consumed theirs.  Every load
@@ -222,13 +226,13 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 // spilled) through it: every iteration recomputes what it uses.
                 int r = lane & 15, gq = lane >> 4;
                 asm volatile("" : "+v"(r), "+v"(gq));
-                const bool live = cn * C + TILE * m + r < T;   // else: identity token
+                const bool live = cn * C + TILE * m + r < len;   // else: identity token
                 const int cnext = min(cn + 1, nchunks - 1);    // the last chunk reloads itself
 
                 // ---------------------------------------------- decays within tile m
                 // b = inclusive cumsum of g over the tile's 16 tokens, per channel
                 float f[KT][4];   // f = e^b in [e^-80, 1] (1/f, up to e^80, is recomputed where used)
-                if constexpr (GBF) {
+                if constexpr (GBF && !GL) {
                     // as a matrix-core product: b^T = g^T Tri, Tri(s, t) = [s <= t].
                     // g goes through this tile's rows of the Qt staging area (rewritten
                     // below), read back transposed: channels as rows, tokens as k-items.
@@ -251,14 +255,17 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         for (int i = 0; i < 4; ++i) f[blk][i] = fast_exp2(bsum[i] * LOG2E);
                     }
                 } else {
-                    // float32 gates: a DPP scan across the 16 lanes of each row
+                    // float32 gates, or gates computed here from logits: a DPP scan
+                    // across the 16 lanes of each row
 #pragma unroll
                     for (int blk = 0; blk < KT; ++blk) {
                         float gl[4];
                         in.g[blk].to_f32(gl);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (GL) gl[i] = gate_from_logit(gl[i], gate_scale);
                             f[blk][i] = fast_exp2(row_inclusive_scan(live ? gl[i] * LOG2E : 0.f));
+                        }
                     }
                 }
                 if (r == TILE - 1) {
@@ -491,7 +498,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         // beta: consumer 0 keeps the slots two chunks ahead, one token per lane
         auto load_beta = [&](int c) -> GT {
             const int t = c * C + lane;
-            return t < T ? beta[((size_t)b * T + t) * H + h] : GT(0);
+            return t < len ? beta[((size_t)b * T + t) * H + h] : GT(0);
         };
         GT bnext = GT(0);   // beta of chunk c + 2, written into its slot in iteration c
         if (w == 0) {
@@ -570,7 +577,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int t = c * C + TILE * mm + 4 * gq + i;
-                        if (full || t < T) ob[(size_t)(TILE * mm + i) * Hdv] = from_f32<OT>(acc[i]);
+                        if (o && (full || t < T)) ob[(size_t)(TILE * mm + i) * Hdv] = from_f32<OT>(acc[i]);
                     }
                 }
 
@@ -613,24 +620,30 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
     }
 }
 
-template <int DK, bool GBF, bool OBF>
+template <int DK, bool GBF, bool OBF, bool GL>
 hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
 {
     typedef typename Store<GBF>::type GT;
     typedef typename Store<OBF>::type OT;
     const int nslab = a.dv / WV;
     const unsigned grid = (unsigned)(a.B * a.H * nslab);
-    kda_chunk_pipe_kernel<DK, GBF, OBF><<<grid, NTHREADS, 0, stream>>>(
+    kda_chunk_pipe_kernel<DK, GBF, OBF, GL><<<grid, NTHREADS, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const GT *)a.g,
-        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.B, a.T, a.H, a.dv, nslab);
+        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.lengths, a.A_log, a.B, a.T, a.H, a.dv, nslab);
     return hipGetLastError();
+}
+
+template <int DK, bool GL>
+hipError_t dispatch_gate(const ChunkFwdArgs &a, hipStream_t s)
+{
+    if (a.gate_bf16) return a.out_bf16 ? launch<DK, true, true, GL>(a, s) : launch<DK, true, false, GL>(a, s);
+    return a.out_bf16 ? launch<DK, false, true, GL>(a, s) : launch<DK, false, false, GL>(a, s);
 }
 
 template <int DK>
 hipError_t dispatch(const ChunkFwdArgs &a, hipStream_t s)
 {
-    if (a.gate_bf16) return a.out_bf16 ? launch<DK, true, true>(a, s) : launch<DK, true, false>(a, s);
-    return a.out_bf16 ? launch<DK, false, true>(a, s) : launch<DK, false, false>(a, s);
+    return a.A_log ? dispatch_gate<DK, true>(a, s) : dispatch_gate<DK, false>(a, s);
 }
 
 }  // namespace

@@ -22,14 +22,15 @@ namespace {
 
 constexpr int NTHREADS = 256;
 
-template <int DK, int DV, bool QBF, bool GBF, bool OBF>
+template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL>
 __global__ void __launch_bounds__(NTHREADS)
 kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
                   const typename Store<QBF>::type *__restrict__ k,
                   const typename Store<QBF>::type *__restrict__ v,
                   const typename Store<GBF>::type *__restrict__ g,
                   const typename Store<GBF>::type *__restrict__ beta,
-                  float *__restrict__ S, typename Store<OBF>::type *__restrict__ o)
+                  float *__restrict__ S, typename Store<OBF>::type *__restrict__ o,
+                  const float *__restrict__ A_log, int H)
 {
     typedef typename Store<QBF>::type QT;
     typedef typename Store<OBF>::type OT;
@@ -54,7 +55,9 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
 
     if (threadIdx.x < DK) {
         const int c = threadIdx.x;
-        const float alpha = __expf(to_f32(g[(size_t)bh * DK + c]));
+        float gc = to_f32(g[(size_t)bh * DK + c]);
+        if constexpr (GL) gc = gate_from_logit(gc, __expf(A_log[bh % H]));
+        const float alpha = __expf(gc);
         const float kc = to_f32(k[(size_t)bh * DK + c]);
         const float qc = to_f32(q[(size_t)bh * DK + c]);
         s_alpha[c] = alpha;
@@ -112,22 +115,28 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
     }
 }
 
-template <int DK, int DV, bool QBF, bool GBF, bool OBF>
+template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream)
 {
     typedef typename Store<QBF>::type QT;
     typedef typename Store<GBF>::type GT;
     typedef typename Store<OBF>::type OT;
-    kda_decode_kernel<DK, DV, QBF, GBF, OBF><<<(unsigned)(a.B * a.H), NTHREADS, 0, stream>>>(
+    kda_decode_kernel<DK, DV, QBF, GBF, OBF, GL><<<(unsigned)(a.B * a.H), NTHREADS, 0, stream>>>(
         (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta,
-        a.S, (OT *)a.o);
+        a.S, (OT *)a.o, a.A_log, a.H);
     return hipGetLastError();
+}
+
+template <int DK, int DV, bool QBF, bool GBF, bool GL>
+hipError_t dispatch_gate(const DecodeArgs &a, hipStream_t s)
+{
+    return a.out_bf16 ? launch<DK, DV, QBF, GBF, true, GL>(a, s) : launch<DK, DV, QBF, GBF, false, GL>(a, s);
 }
 
 template <int DK, int DV, bool QBF, bool GBF>
 hipError_t dispatch_out(const DecodeArgs &a, hipStream_t s)
 {
-    return a.out_bf16 ? launch<DK, DV, QBF, GBF, true>(a, s) : launch<DK, DV, QBF, GBF, false>(a, s);
+    return a.A_log ? dispatch_gate<DK, DV, QBF, GBF, true>(a, s) : dispatch_gate<DK, DV, QBF, GBF, false>(a, s);
 }
 
 template <int DK, int DV>

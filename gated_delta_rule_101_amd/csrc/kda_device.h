@@ -355,4 +355,13 @@ __device__ __forceinline__ void unit_lower_inverse_steps(float (&X)[16], const f
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Log-decay from a gate logit z: g = g_min * sigmoid(s z) with g_min = -5 and s
+// the head's scale exp(A_h) ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the
+// scaled-sigmoid mapping that replaced the unbounded -softplus one).  In
+// [-5, 0] for every z: exp2 of a huge argument is inf and 1/inf is 0.
+__device__ __forceinline__ float gate_from_logit(float z, float s) {
+    constexpr float LOG2E_ = 1.4426950408889634f;
+    return -5.0f * fast_rcp(1.0f + fast_exp2(-s * z * LOG2E_));
+}
+
 }  // namespace kda

@@ -9,9 +9,11 @@ namespace kda {
 
 struct ChunkFwdArgs {
     const void *q, *k, *v, *g, *beta;
-    const float *S0;   // nullable
-    void *o;
-    float *S_final;    // nullable
+    const float *S0 = nullptr;        // nullable: zero initial state
+    void *o = nullptr;                // nullable: outputs not written
+    float *S_final = nullptr;         // nullable: final state not written
+    const int *lengths = nullptr;     // nullable: per sequence, tokens from lengths[b] on are identity tokens
+    const float *A_log = nullptr;     // non-null: g holds gate logits z, log-decay = -5 sigmoid(exp(A_log[h]) z)
     int B, T, H, dk, dv;
     bool qkv_bf16, gate_bf16, out_bf16;
 };
@@ -20,6 +22,7 @@ struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
     float *S;
     void *o;
+    const float *A_log = nullptr;     // as in ChunkFwdArgs
     int B, H, dk, dv;
     bool qkv_bf16, gate_bf16, out_bf16;
 };

@@ -28,7 +28,8 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 
 # Every symbol include/kda.h declares.
-EXPORTS = ("kda_chunk_fwd", "kda_decode_step", "kda_status_string", "kda_abi_version")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_verify_step", "kda_commit_step",
+           "kda_decode_step", "kda_decode_step_gate", "kda_status_string", "kda_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -53,6 +54,14 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = i
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 7 + [vp]
     lib.kda_decode_step.restype = i
+    lib.kda_chunk_fwd_gate.argtypes = [vp] * 9 + [i] * 8 + [vp]
+    lib.kda_chunk_fwd_gate.restype = i
+    lib.kda_decode_step_gate.argtypes = [vp] * 8 + [i] * 7 + [vp]
+    lib.kda_decode_step_gate.restype = i
+    lib.kda_verify_step.argtypes = [vp] * 7 + [i] * 8 + [vp]
+    lib.kda_verify_step.restype = i
+    lib.kda_commit_step.argtypes = [vp] * 6 + [i] * 7 + [vp]
+    lib.kda_commit_step.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -164,3 +173,113 @@ def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.
                              _stream_handle(stream, dev))
     _raise(st, "kda_decode_step")
     return o
+
+
+def _check_chunk_shapes(q, k, v, g, beta):
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    if (q is not None and q.shape != k.shape) or g.shape != k.shape or v.shape != (B, T, H, dv) \
+            or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch between q, k, v, g, beta")
+    if (q is not None and q.dtype != k.dtype) or v.dtype != k.dtype or beta.dtype != g.dtype:
+        raise TypeError("q, k, v share one dtype; g and beta share one dtype")
+    return B, T, H, dk, dv
+
+
+def _check_head_scale(A_log: torch.Tensor, H: int):
+    if A_log.shape != (H,) or A_log.dtype != torch.float32:
+        raise ValueError("A_log must be float32 [H]")
+
+
+def kda_chunk_fwd_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
+                       A_log: torch.Tensor, beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
+                       output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                       S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                       stream: Optional[torch.cuda.Stream] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd with the log-decay formed in the kernel from gate logits:
+    g = -5 sigmoid(exp(A_log[h]) z).  z [B,T,H,dk] (gate dtype), A_log [H] float32."""
+    lib = load_library()
+    B, T, H, dk, dv = _check_chunk_shapes(q, k, v, z, beta)
+    _check_head_scale(A_log, H)
+    if S0 is not None and (S0.shape != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("S0 must be float32 [B,H,dk,dv]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, T, H, dv):
+        raise ValueError("o must be [B,T,H,dv]")
+    if S_final is None and output_final_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    dev = _check_dev(q, k, v, z, A_log, beta, S0, o, S_final)
+    st = lib.kda_chunk_fwd_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(beta), _ptr(S0),
+                                _ptr(o), _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(z),
+                                _dtype_code(o), _stream_handle(stream, dev))
+    _raise(st, "kda_chunk_fwd_gate")
+    return o, S_final
+
+
+def kda_decode_step_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
+                         A_log: torch.Tensor, beta: torch.Tensor, S: torch.Tensor, *,
+                         o: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """kda_decode_step with g = -5 sigmoid(exp(A_log[h]) z) formed in the kernel."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or z.shape != q.shape or v.shape != (B, H, dv) or beta.shape != (B, H):
+        raise ValueError("shape mismatch between q, k, v, z, beta")
+    if S.shape != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != z.dtype:
+        raise TypeError("q, k, v share one dtype; z and beta share one dtype")
+    _check_head_scale(A_log, H)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, H, dv):
+        raise ValueError("o must be [B,H,dv]")
+    dev = _check_dev(q, k, v, z, A_log, beta, S, o)
+    st = lib.kda_decode_step_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(beta), _ptr(S),
+                                  _ptr(o), B, H, dk, dv, _dtype_code(q), _dtype_code(z), _dtype_code(o),
+                                  _stream_handle(stream, dev))
+    _raise(st, "kda_decode_step_gate")
+    return o
+
+
+def kda_verify_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, S: torch.Tensor, *, o: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Outputs of K draft tokens per sequence ([B,K,H,*] inputs) through the
+    state S [B,H,dk,dv], which is left unchanged.  Returns o [B,K,H,dv]."""
+    lib = load_library()
+    B, K, H, dk, dv = _check_chunk_shapes(q, k, v, g, beta)
+    if S.shape != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if o is None:
+        o = torch.empty((B, K, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, K, H, dv):
+        raise ValueError("o must be [B,K,H,dv]")
+    dev = _check_dev(q, k, v, g, beta, S, o)
+    st = lib.kda_verify_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), _ptr(o),
+                             B, K, H, dk, dv, _dtype_code(q), _dtype_code(g), _dtype_code(o),
+                             _stream_handle(stream, dev))
+    _raise(st, "kda_verify_step")
+    return o
+
+
+def kda_commit_step(k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                    accepted: torch.Tensor, S: torch.Tensor, *,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Advance S [B,H,dk,dv] IN PLACE by the first accepted[b] (int32 [B],
+    clamped to [0, K]) of the K draft tokens of each sequence.  Returns S."""
+    lib = load_library()
+    B, K, H, dk, dv = _check_chunk_shapes(None, k, v, g, beta)
+    if S.shape != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if accepted.shape != (B,) or accepted.dtype != torch.int32:
+        raise ValueError("accepted must be int32 [B]")
+    dev = _check_dev(k, v, g, beta, accepted, S)
+    st = lib.kda_commit_step(_ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(accepted), _ptr(S),
+                             B, K, H, dk, dv, _dtype_code(k), _dtype_code(g), _stream_handle(stream, dev))
+    _raise(st, "kda_commit_step")
+    return S

@@ -22,6 +22,20 @@
  * kda_decode_step advances every (sequence, head) state by one token in place
  * (the fixed-size state of "Review A", Discriminating between mechanisms).
  *
+ * kda_verify_step and kda_commit_step serve speculative decoding ("K3
+ * Architecture Illustrated", the section on speculative decoding: the
+ * recurrent state needs rollback handling after rejected proposals): verify
+ * runs K draft tokens through the current state without changing it, commit
+ * then advances the state by each sequence's accepted prefix only.
+ *
+ * kda_chunk_fwd_gate and kda_decode_step_gate take raw gate logits z and a
+ * per-head log-scale A_h instead of g, and form g = -5 sigmoid(exp(A_h) z)
+ * inside the kernels ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the
+ * scaled-sigmoid gate with g_min = -5 and A_h a learnable per-head log-scale
+ * initialised to 0).  The page shows the mapping without its formula; the
+ * scale is read as acting on the logit inside the sigmoid, which keeps every
+ * g in [-5, 0] for any A_h and is the plain -5 sigmoid(z) at A_h = 0.
+ *
  * Conventions for every entry point
  * ---------------------------------
  *  - Tensor pointers are DEVICE pointers to contiguous row-major memory, each
@@ -60,7 +74,7 @@ typedef enum {
 } kda_status_t;
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /*
  * kda_chunk_fwd -- chunkwise forward over T tokens for B sequences x H heads.
@@ -120,6 +134,70 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              int B, int H, int dk, int dv,
                              kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
                              kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_chunk_fwd_gate -- kda_chunk_fwd with the log-decay formed in the kernel.
+ *
+ *   z      [B, T, H, dk]  gate_dtype  gate logits (any real value)
+ *   A_log  [H]            float32     per-head log-scale A_h (device pointer,
+ *                                     4-byte aligned)
+ *   g = -5 sigmoid(exp(A_log[h]) z), in [-5, 0] for every z.  Everything
+ *   else, including supported sizes and errors, as kda_chunk_fwd; A_log must
+ *   not be NULL and must not overlap o or S_final.
+ */
+kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
+                                const void *z, const float *A_log, const void *beta,
+                                const float *S0, void *o, float *S_final,
+                                int B, int T, int H, int dk, int dv,
+                                kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                                kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_decode_step_gate -- kda_decode_step with g = -5 sigmoid(exp(A_log[h]) z)
+ * formed in the kernel (z [B, H, dk] gate_dtype, A_log [H] float32).
+ */
+kda_status_t kda_decode_step_gate(const void *q, const void *k, const void *v,
+                                  const void *z, const float *A_log, const void *beta,
+                                  float *S, void *o, int B, int H, int dk, int dv,
+                                  kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                                  kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_verify_step -- K draft tokens per sequence through the current state,
+ * outputs only.
+ *
+ *   q, k, g [B, K, H, dk], v [B, K, H, dv], beta [B, K, H]: the draft tokens
+ *   S       [B, H, dk, dv] float32   the state before the drafts; READ ONLY
+ *   o       [B, K, H, dv]  out_dtype o[:, j] is the output token j would get
+ *                                    after tokens 0..j-1 of its draft
+ *
+ * Equivalent to kda_chunk_fwd(q, k, v, g, beta, S0 = S, o, S_final = NULL)
+ * over T = K tokens; same sizes, dtypes and errors.  S must not be NULL and
+ * must not overlap o.
+ */
+kda_status_t kda_verify_step(const void *q, const void *k, const void *v,
+                             const void *g, const void *beta, const float *S, void *o,
+                             int B, int K, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                             kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_commit_step -- advance S in place by the accepted prefix of each draft.
+ *
+ *   k, g [B, K, H, dk], v [B, K, H, dv], beta [B, K, H]: the same draft tokens
+ *   accepted [B] int32 (device): tokens 0..accepted[b]-1 of sequence b are
+ *                   applied, the rest are treated as identity tokens (values
+ *                   are clamped to [0, K])
+ *   S        [B, H, dk, dv] float32, read and written IN PLACE
+ *
+ * Afterwards S is the state kda_chunk_fwd would reach over the first
+ * accepted[b] tokens of each sequence.  No output is written.  S must not
+ * overlap k, v, g, beta or accepted.
+ */
+kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const void *beta,
+                             const int *accepted, float *S,
+                             int B, int K, int H, int dk, int dv,
+                             kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status_t status);

@@ -94,8 +94,8 @@ def _sigmoid_f64(z: np.ndarray) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def _log_decay(rng: np.random.Generator, shape, w: Workload, chan_axis_bh) -> np.ndarray:
-    """g = -5 * sigmoid(z) with the workload's logit distribution, float32."""
+def _gate_logits(rng: np.random.Generator, shape, w: Workload, chan_axis_bh) -> np.ndarray:
+    """The workload's gate logits z (float32), forced channels included."""
     z = rng.standard_normal(size=shape, dtype=np.float32)
     if w.z_sd != 1.0 or w.z_mu != 0.0:
         z *= np.float32(w.z_sd)
@@ -109,6 +109,12 @@ def _log_decay(rng: np.random.Generator, shape, w: Workload, chan_axis_bh) -> np
                     z[b, :, h, pick[b, h]] = np.float32(w.forced_z)
                 else:                    # [B, H, dk]
                     z[b, h, pick[b, h]] = np.float32(w.forced_z)
+    return z
+
+
+def _log_decay(rng: np.random.Generator, shape, w: Workload, chan_axis_bh) -> np.ndarray:
+    """g = -5 * sigmoid(z) with the workload's logit distribution, float32."""
+    z = _gate_logits(rng, shape, w, chan_axis_bh)
     out = np.empty(shape, dtype=np.float32)
     zf = z.reshape(-1)
     of = out.reshape(-1)
@@ -146,6 +152,37 @@ def fwd_tensor(w: Workload, name: str, seed: int = 0) -> Optional[HostTensor]:
 
 def fwd_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[HostTensor]]:
     return {n: fwd_tensor(w, n, seed) for n in ("q", "k", "v", "g", "beta", "S0")}
+
+
+_HEAD_SCALE_STREAM = 7
+
+
+def head_log_scales(H: int, sd: float = 0.5, seed: int = 0) -> HostTensor:
+    """Per-head gate log-scales A_h ~ N(0, sd), float32 [H] (A_h = 0 at initialisation)."""
+    return HostTensor(_normal_f32(_rng(seed, _HEAD_SCALE_STREAM), (H,)) * np.float32(sd), "f32")
+
+
+def gate_logit_inputs(w: Workload, seed: int = 0) -> Dict[str, Optional[HostTensor]]:
+    """fwd_inputs with the raw gate logits "z" (same stream and distribution as
+    the logits behind g, gate dtype) in place of g, plus per-head "A_log"."""
+    assert w.kind == "fwd"
+    out = {n: fwd_tensor(w, n, seed) for n in ("q", "k", "v", "beta", "S0")}
+    B, T, H, dk = w.B, w.T, w.H, w.dk
+    out["z"] = _to_dtype(_gate_logits(_rng(seed, _STREAM["g"]), (B, T, H, dk), w, (B, H, dk)), w.gate)
+    out["A_log"] = head_log_scales(H, seed=seed)
+    return out
+
+
+def decode_gate_logit_inputs(w: Workload, step: int, seed: int = 0) -> Dict[str, HostTensor]:
+    """decode_step_inputs with raw gate logits "z" in place of g, plus "A_log"."""
+    assert w.kind == "decode"
+    out = decode_step_inputs(w, step, seed)
+    del out["g"]
+    B, H, dk = w.B, w.H, w.dk
+    out["z"] = _to_dtype(_gate_logits(_rng(seed, _DECODE_STEP_BASE + 8 * step + 4), (B, H, dk), w, (B, H, dk)),
+                         w.gate)
+    out["A_log"] = head_log_scales(H, seed=seed)
+    return out
 
 
 def decode_initial_state(w: Workload, seed: int = 0) -> HostTensor:

@@ -123,6 +123,27 @@ def kda_decode_step(q, k, v, g, beta, S, **kw):
     return default().decode_step(q, k, v, g, beta, S, **kw)
 
 
+def gate_log_decay(z, A_log, head_axis: int = -2) -> np.ndarray:
+    """Log-decay from gate logits, float64: g = g_min * sigmoid(exp(A_h) * z)
+    with g_min = -5 ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the
+    scaled-sigmoid mapping: sigmoid bounded in (0, 1) scaled by g_min bounds
+    the log-decay in (-5, 0); A_h a per-head learnable log-scale initialised
+    to 0).  The page omits the formula; the log-scale is read as scaling the
+    logit inside the sigmoid, the one placement that keeps g in (-5, 0) for
+    every A_h and reduces to -5 sigmoid(z) at A_h = 0.
+
+    z: [..., H, dk] (H on `head_axis`), A_log: [H].  Written with exp of a
+    non-positive argument on both branches, so no overflow for any finite z.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    shape = [1] * z.ndim
+    shape[head_axis] = -1
+    x = np.exp(np.asarray(A_log, dtype=np.float64)).reshape(shape) * z
+    e = np.exp(-np.abs(x))
+    sig = np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return -5.0 * sig
+
+
 def build_variant(source_text: str) -> Oracle:
     """Compile a modified copy of the oracle source into a temporary library.
 
