@@ -7,8 +7,10 @@ One step = one kda_chunk_fwd over the training-shape workload
 already resident in HBM.  `value` is tokens/s (B*T tokens per step, each
 token carrying all H heads).  The decode path is timed on its own workload
 (B=256 sequences x H=96, d=128, 64 consecutive steps) and reported under
-"decode" in GB/s.  Each carries a roofline object for its kernel, with the
-kernel's average duration measured by HIP events on the launch stream.
+"decode" in GB/s.  Speculative decoding on the same states (verify 16 draft
+tokens, commit 8 of them) is reported under "speculative".  Each carries a
+roofline object for its kernel, with the kernel's average duration measured
+by HIP events on the launch stream.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -178,6 +180,44 @@ def bench_decode(kda, reps):
     }
 
 
+def spec_bytes(B, H, K, n, dk, dv, s_qkv, s_g, s_o):
+    """Algorithmic bytes of one speculative verify of K draft tokens per state
+    (reads the state once, the drafts' q, k, v, g, beta, writes K outputs)
+    and one commit of n accepted tokens per state (reads and writes the state
+    once, reads the accepted tokens' k, v, g, beta and the counts)."""
+    state = B * H * dk * dv * 4
+    verify = state + B * K * H * ((2 * dk + dv) * s_qkv + (dk + 1) * s_g + dv * s_o)
+    commit = 2 * state + B * n * H * ((dk + dv) * s_qkv + (dk + 1) * s_g) + 4 * B
+    return verify, commit
+
+
+def bench_speculative(kda, reps, K=16):
+    """Verify + commit of K draft tokens on the decode workload's states."""
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.DECODE_BF16
+    fw = configs.Workload(name="spec_drafts", kind="fwd", B=w.B, H=w.H, dk=w.dk, dv=w.dv, T=K,
+                          qkv=w.qkv, gate=w.gate, s0_sd=None)
+    log(f"[bench] speculative: {w.B}x{w.H} states, {K} draft tokens")
+    S = gen_torch.decode_initial_state(w)
+    x = gen_torch.fwd_inputs(fw)
+    o = torch.empty((w.B, K, w.H, w.dv), dtype=torch.float32, device="cuda")
+    n = K // 2
+    acc = torch.full((w.B,), n, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    verify_b, commit_b = spec_bytes(w.B, w.H, K, n, w.dk, w.dv, 2, 4, 4)
+    out = {"workload": f"kda_spec_B{w.B}_H{w.H}_d{w.dk}_bf16_K{K}", "draft_tokens": K, "accepted": n}
+    calls = (("verify", lambda: kda.kda_verify_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S, o=o), verify_b),
+             ("commit", lambda: kda.kda_commit_step(x["k"], x["v"], x["g"], x["beta"], acc, S), commit_b))
+    for name, fn, nbytes in calls:
+        wall, ker = time_launches(fn, reps, 2, stream)
+        gbs = nbytes * reps / wall / 1e9
+        log(f"[bench] {name} {wall / reps * 1e3:.3f} ms (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
+        out[name] = {"ms": round(wall / reps * 1e3, 4), "GB/s": round(gbs, 1),
+                     "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}
+    return out
+
+
 def cpu_baseline(w, d, batch=32):
     """The float64 oracle on the same workload, every head over the full
     sequence, on all host threads, `batch` heads per call (only the recurrence
@@ -327,6 +367,7 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(kda, args.decode_reps)
+        out["speculative"] = bench_speculative(kda, 10)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d)
     print(json.dumps(out), flush=True)

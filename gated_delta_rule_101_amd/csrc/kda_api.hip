@@ -92,6 +92,19 @@ kda::ChunkFwdArgs chunk_args(const void *q, const void *k, const void *v, const 
     return a;
 }
 
+kda::SpecArgs spec_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                        float *S, int B, int K, int H, int dk, int dv,
+                        kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype)
+{
+    kda::SpecArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S;
+    a.B = B; a.K = K; a.H = H; a.dk = dk; a.dv = dv;
+    a.qkv_bf16 = qkv_dtype == KDA_BF16;
+    a.gate_bf16 = gate_dtype == KDA_BF16;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    return a;
+}
+
 kda_status_t decode(const void *q, const void *k, const void *v, const void *g, const void *beta,
                     const float *A_log, float *S, void *o, int B, int H, int dk, int dv,
                     kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype, void *stream)
@@ -170,7 +183,13 @@ kda_status_t kda_verify_step(const void *q, const void *k, const void *v, const 
     const kda_status_t st = check_chunk(q, k, v, g, beta, S, o, nullptr, nullptr, nullptr, B, K, H, dk, dv,
                                         qkv_dtype, gate_dtype, out_dtype, true, true);
     if (st != KDA_OK) return st;
-    if (K == 0) return KDA_OK;
+    if (K == 0 || B == 0 || H == 0) return KDA_OK;
+    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // the token-loop kernel
+        kda::SpecArgs a = spec_args(q, k, v, g, beta, const_cast<float *>(S), B, K, H, dk, dv,
+                                    qkv_dtype, gate_dtype, out_dtype);
+        a.o = o;
+        return kda::launch_spec_step(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
     kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S, o, nullptr, B, K, H, dk, dv,
                                      qkv_dtype, gate_dtype, out_dtype);
     return run_chunk(a, stream);
@@ -184,8 +203,13 @@ kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const 
     const kda_status_t st = check_chunk(nullptr, k, v, g, beta, S, nullptr, S, nullptr, accepted, B, K, H,
                                         dk, dv, qkv_dtype, gate_dtype, KDA_F32, false, false);
     if (st != KDA_OK) return st;
-    if (K == 0) return KDA_OK;
-    // the kernels read a query row for every token; the keys stand in (no output is written)
+    if (K == 0 || B == 0 || H == 0) return KDA_OK;
+    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // the token-loop kernel
+        kda::SpecArgs a = spec_args(nullptr, k, v, g, beta, S, B, K, H, dk, dv, qkv_dtype, gate_dtype, KDA_F32);
+        a.accepted = accepted;
+        return kda::launch_spec_step(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+    // the chunk kernels read a query row for every token; the keys stand in (no output is written)
     kda::ChunkFwdArgs a = chunk_args(k, k, v, g, beta, S, nullptr, S, B, K, H, dk, dv,
                                      qkv_dtype, gate_dtype, KDA_F32);
     a.lengths = accepted;

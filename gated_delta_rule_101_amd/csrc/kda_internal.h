@@ -27,8 +27,20 @@ struct DecodeArgs {
     bool qkv_bf16, gate_bf16, out_bf16;
 };
 
+// Speculative verify (accepted == nullptr: outputs of all K drafts, S read
+// only) or commit (accepted != nullptr: S advanced by accepted[b] drafts).
+struct SpecArgs {
+    const void *q, *k, *v, *g, *beta;
+    float *S;
+    void *o = nullptr;
+    const int *accepted = nullptr;
+    int B, K, H, dk, dv;
+    bool qkv_bf16, gate_bf16, out_bf16;
+};
+
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        // any dtypes
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_spec_step(const SpecArgs &a, hipStream_t stream);           // dk, dv in {64, 128}
 
 }  // namespace kda

@@ -1,0 +1,35 @@
+"""The benchmark's algorithmic byte and FLOP counts, checked by hand counts.
+
+The roofline fractions the benchmark reports divide these counts by measured
+kernel times, so a wrong count would misstate every fraction.
+"""
+
+import bench
+
+
+def test_forward_counts_at_training_shape():
+    # B4 H32 T16384 d128, bf16 q/k/v/g/beta, fp32 outputs, final state written:
+    # per token-head 2*(128+128+128) + 2*129 + 4*128 bytes, plus one fp32 state per head
+    per_tok = 2 * 384 + 2 * 129 + 4 * 128
+    tok_heads = 4 * 16384 * 32
+    state = 4 * 32 * 128 * 128 * 4
+    assert bench.fwd_bytes(4, 16384, 32, 128, 128, 2, 2, 4, False, True) == tok_heads * per_tok + state
+    assert bench.fwd_bytes(4, 16384, 32, 128, 128, 2, 2, 4, True, True) == tok_heads * per_tok + 2 * state
+    # 6 d^2 + 2 C (2 d) + C^2/3 at C = 64, d = 128
+    assert bench.fwd_flops(1, 1, 1, 128, 128) == 6 * 16384 + 128 * 256 + 4096 // 3 == 132437
+
+
+def test_decode_counts():
+    # B256 H96 d128: fp32 state read and written, bf16 q, k, v, fp32 g, beta, fp32 o
+    per_state = 2 * 128 * 128 * 4 + 2 * 384 + 4 * 129 + 4 * 128
+    assert bench.decode_bytes(256, 96, 128, 128, 2, 4, 4) == 256 * 96 * per_state
+
+
+def test_speculative_counts():
+    B, H, K, n, d = 2, 3, 16, 5, 64
+    state = B * H * d * d * 4
+    # verify: the state once, K drafts of q, k, v (bf16), g, beta (fp32), K fp32 outputs
+    verify = state + B * H * K * (2 * 3 * d + 4 * (d + 1) + 4 * d)
+    # commit: the state read and written, n accepted drafts of k, v, g, beta, B int32 counts
+    commit = 2 * state + B * H * n * (2 * 2 * d + 4 * (d + 1)) + 4 * B
+    assert bench.spec_bytes(B, H, K, n, d, d, 2, 4, 4) == (verify, commit)

@@ -55,6 +55,8 @@ SPEC_CASES = [
     configs.TRAIN_BF16.scaled(B=2, H=2, T=64, s0_sd=0.02, name="spec_bf16_K64_bf16gates"),
     configs.TINY_F32.scaled(B=3, H=2, T=16, dk=128, dv=128, s0_sd=0.3, name="spec_f32_K16"),
     configs.TINY_F32.scaled(B=2, H=2, T=1, s0_sd=0.3, name="spec_f32_K1"),
+    configs.HEADGROUP_BF16.scaled(B=2, H=3, T=37, dk=64, dv=128, name="spec_bf16_K37_dk64"),
+    configs.TINY_F32.scaled(B=2, H=2, T=7, dv=256, s0_sd=0.3, name="spec_f32_K7_dv256"),  # chunk-kernel route
 ]
 
 
