@@ -8,7 +8,9 @@ already resident in HBM.  `value` is tokens/s (B*T tokens per step, each
 token carrying all H heads).  The decode path is timed on its own workload
 (B=256 sequences x H=96, d=128, 64 consecutive steps) and reported under
 "decode" in GB/s.  Speculative decoding on the same states (verify 16 draft
-tokens, commit 8 of them) is reported under "speculative".  Each carries a
+tokens, commit 8 of them) is reported under "speculative", the output
+epilogue (alone over the training-shape reads, and fused into decode) under
+"epilogue".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
 by HIP events on the launch stream.
 
@@ -59,6 +61,18 @@ def fwd_flops(B, T, H, dk, dv, C=CHUNK) -> int:
 def decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) -> int:
     """One decode step: fp32 state read + written, q, k, v, g, beta read, o written."""
     return B * H * (8 * dk * dv + s_qkv * (2 * dk + dv) + s_g * (dk + 1) + s_o * dv)
+
+
+def epilogue_bytes(rows, dv, s_o, s_z, s_y) -> int:
+    """Output epilogue: each read and gate logit read once, each result written
+    once, plus the fp32 weight vector."""
+    return rows * dv * (s_o + s_z + s_y) + 4 * dv
+
+
+def gated_decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) -> int:
+    """A decode step with the epilogue fused: the decode's bytes plus the
+    output-gate logits (q's dtype) and the weight vector."""
+    return decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) + B * H * dv * s_qkv + 4 * dv
 
 
 def kernel_source_hash(files) -> str:
@@ -218,6 +232,54 @@ def bench_speculative(kda, reps, K=16):
     return out
 
 
+def bench_epilogue(kda, reps=10):
+    """The output epilogue over the training-shape reads (float32 o, bf16
+    logits, float32 y), and the decode step with the epilogue fused."""
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.TRAIN_BF16
+    shape = (w.B, w.T, w.H, w.dv)
+    rows = w.B * w.T * w.H
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    o = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32)
+    z = gen_torch.output_gate_logits(shape, "bf16")
+    wt = gen_torch.output_norm_weight(w.dv)
+    y = torch.empty_like(o)
+    stream = torch.cuda.current_stream()
+    wall, ker = time_launches(lambda: kda.kda_output_gate(o, z, wt, 1e-6, y=y), reps, 2, stream)
+    nbytes = epilogue_bytes(rows, w.dv, 4, 2, 4)
+    gbs = nbytes * reps / wall / 1e9
+    log(f"[bench] output_gate {wall / reps * 1e3:.3f} ms (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
+    out = {"output_gate": {"workload": f"kda_output_gate_B{w.B}_T{w.T}_H{w.H}_dv{w.dv}_f32o_bf16z",
+                           "ms": round(wall / reps * 1e3, 4), "GB/s": round(gbs, 1),
+                           "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}}
+    del o, z, y
+
+    dw = configs.DECODE_BF16
+    S = gen_torch.decode_initial_state(dw)
+    xs = [gen_torch.decode_step_inputs(dw, s) for s in range(dw.steps)]
+    zs = [gen_torch.output_gate_logits((dw.B, dw.H, dw.dv), dw.qkv, seed=s) for s in range(dw.steps)]
+    wd = gen_torch.output_norm_weight(dw.dv)
+    yd = torch.empty((dw.B, dw.H, dw.dv), dtype=torch.float32, device="cuda")
+    it = {"i": 0}
+
+    def one():
+        i = it["i"] % dw.steps
+        it["i"] += 1
+        x = xs[i]
+        kda.kda_decode_step_gated(x["q"], x["k"], x["v"], x["g"], x["beta"], S, zs[i], wd, 1e-6, y=yd)
+
+    wall, ker = time_launches(one, dw.steps, dw.steps // 4, stream)
+    per_step = gated_decode_bytes(dw.B, dw.H, dw.dk, dw.dv, 2, 4, 4)
+    gbs = per_step * dw.steps / wall / 1e9
+    log(f"[bench] decode+epilogue {wall / dw.steps * 1e3:.3f} ms/step (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
+    out["decode_gated"] = {"workload": dw.name + "_gated", "ms_per_step": round(wall / dw.steps * 1e3, 4),
+                           "GB/s": round(gbs, 1), "algorithmic_bytes_per_step": per_step,
+                           "roofline": roofline(per_step, ker, None)}
+    return out
+
+
 def cpu_baseline(w, d, batch=32):
     """The float64 oracle on the same workload, every head over the full
     sequence, on all host threads, `batch` heads per call (only the recurrence
@@ -368,6 +430,7 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(kda, args.decode_reps)
         out["speculative"] = bench_speculative(kda, 10)
+        out["epilogue"] = bench_epilogue(kda)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d)
     print(json.dumps(out), flush=True)

@@ -105,9 +105,20 @@ kda::SpecArgs spec_args(const void *q, const void *k, const void *v, const void 
     return a;
 }
 
+// Checks of the output epilogue's own arguments: z_out [n, dv] (storage
+// `z_bytes` per value), weight [dv] float32, eps >= 0 and finite.
+bool epilogue_args_ok(const void *z_out, const float *weight, float eps)
+{
+    if (!z_out || !weight) return false;
+    if (!aligned16(weight)) return false;
+    return eps >= 0.f && eps <= 3.0e38f;   // rejects NaN and inf too
+}
+
 kda_status_t decode(const void *q, const void *k, const void *v, const void *g, const void *beta,
                     const float *A_log, float *S, void *o, int B, int H, int dk, int dv,
-                    kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype, void *stream)
+                    kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype, void *stream,
+                    const void *z_out = nullptr, const float *weight = nullptr, float eps = 0.f,
+                    bool gated = false)
 {
     if (B < 0 || H < 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(out_dtype))
@@ -118,6 +129,8 @@ kda_status_t decode(const void *q, const void *k, const void *v, const void *g, 
     if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
     if (!aligned16(S)) return KDA_ERR_INVALID_ARG;
     if (A_log && ((uintptr_t)A_log & 3u)) return KDA_ERR_INVALID_ARG;
+    if (gated && (!epilogue_args_ok(z_out, weight, eps) || !aligned16(z_out)))
+        return KDA_ERR_INVALID_ARG;
 
     const size_t n = (size_t)B * H;
     const size_t sq = dsize(qkv_dtype), sg = dsize(gate_dtype), so = dsize(out_dtype);
@@ -125,13 +138,18 @@ kda_status_t decode(const void *q, const void *k, const void *v, const void *g, 
     const Span sp_g = span(g, n * dk * sg), sp_b = span(beta, n * sg);
     const Span sp_a = span(A_log, A_log ? (size_t)H * sizeof(float) : 0);
     const Span sp_s = span(S, n * dk * dv * sizeof(float)), sp_o = span(o, n * dv * so);
-    const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b, sp_a};
+    const Span sp_z = span(gated ? z_out : nullptr, gated ? n * dv * sq : 0);
+    const Span sp_w = span(gated ? weight : nullptr, gated ? (size_t)dv * sizeof(float) : 0);
+    const Span ins[] = {sp_q, sp_k, sp_v, sp_g, sp_b, sp_a, sp_z, sp_w};
     for (const Span &s : ins)
         if (overlap(sp_o, s) || overlap(sp_s, s)) return KDA_ERR_INVALID_ARG;
     if (overlap(sp_o, sp_s)) return KDA_ERR_INVALID_ARG;
 
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S = S; a.o = o; a.A_log = A_log;
+    if (gated) {
+        a.z_out = z_out; a.weight = weight; a.eps = eps;
+    }
     a.B = B; a.H = H; a.dk = dk; a.dv = dv;
     a.qkv_bf16 = qkv_dtype == KDA_BF16;
     a.gate_bf16 = gate_dtype == KDA_BF16;
@@ -232,6 +250,43 @@ kda_status_t kda_decode_step_gate(const void *q, const void *k, const void *v, c
 {
     if (!A_log && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
     return decode(q, k, v, z, beta, A_log, S, o, B, H, dk, dv, qkv_dtype, gate_dtype, out_dtype, stream);
+}
+
+kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v, const void *g,
+                                   const float *A_log, const void *beta, float *S, const void *z_out,
+                                   const float *weight, float eps, void *y, int B, int H, int dk, int dv,
+                                   kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                   void *stream)
+{
+    return decode(q, k, v, g, beta, A_log, S, y, B, H, dk, dv, qkv_dtype, gate_dtype, out_dtype, stream,
+                  z_out, weight, eps, true);
+}
+
+kda_status_t kda_output_gate(const void *o, const void *z, const float *weight, float eps, void *y,
+                             int64_t rows, int dv, kda_dtype_t o_dtype, kda_dtype_t z_dtype,
+                             kda_dtype_t y_dtype, void *stream)
+{
+    if (rows < 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (!valid_dtype(o_dtype) || !valid_dtype(z_dtype) || !valid_dtype(y_dtype)) return KDA_ERR_INVALID_ARG;
+    if (dv % 64 != 0 || dv > 512) return KDA_ERR_UNSUPPORTED;
+    if (rows > ((int64_t)1 << 40)) return KDA_ERR_UNSUPPORTED;
+    if (rows == 0) return KDA_OK;
+    if (!o || !y || !epilogue_args_ok(z, weight, eps)) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(o) || !aligned16(z) || !aligned16(y)) return KDA_ERR_INVALID_ARG;
+    const size_t n = (size_t)rows * dv;
+    const Span sp_o = span(o, n * dsize(o_dtype)), sp_z = span(z, n * dsize(z_dtype));
+    const Span sp_w = span(weight, (size_t)dv * sizeof(float)), sp_y = span(y, n * dsize(y_dtype));
+    // y may be o itself (same dtype): each element is read before it is written
+    const bool in_place = y == o && y_dtype == o_dtype;
+    if ((!in_place && overlap(sp_y, sp_o)) || overlap(sp_y, sp_z) || overlap(sp_y, sp_w)) return KDA_ERR_INVALID_ARG;
+
+    kda::OutputGateArgs a;
+    a.o = o; a.z = z; a.weight = weight; a.y = y;
+    a.rows = rows; a.dv = dv; a.eps = eps;
+    a.o_bf16 = o_dtype == KDA_BF16;
+    a.z_bf16 = z_dtype == KDA_BF16;
+    a.y_bf16 = y_dtype == KDA_BF16;
+    return kda::launch_output_gate(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 const char *kda_status_string(kda_status_t status)

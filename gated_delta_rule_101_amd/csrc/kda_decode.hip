@@ -14,6 +14,12 @@
 //   o = S^T (alpha . q) + (q.k) w   the read of the updated state
 //   S <- D S + k w^T
 // which is one token of the recurrence with a single read and write of S.
+//
+// With the output epilogue fused (OG), each thread's four outputs are
+// normalised by the RMS of the head's dv outputs (reduced across the row
+// group's lanes), scaled by the per-channel weight and gated by
+// sigmoid(z_out) before the store ("Kimi K3 - Lesson 3 of 14", the output-gate
+// paragraph; the form is read as RMS normalisation then a sigmoid gate).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -22,7 +28,7 @@ namespace {
 
 constexpr int NTHREADS = 256;
 
-template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL>
+template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL, bool OG>
 __global__ void __launch_bounds__(NTHREADS)
 kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
                   const typename Store<QBF>::type *__restrict__ k,
@@ -30,7 +36,8 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
                   const typename Store<GBF>::type *__restrict__ g,
                   const typename Store<GBF>::type *__restrict__ beta,
                   float *__restrict__ S, typename Store<OBF>::type *__restrict__ o,
-                  const float *__restrict__ A_log, int H)
+                  const float *__restrict__ A_log, int H,
+                  const typename Store<QBF>::type *__restrict__ z_out, const float *__restrict__ weight, float eps)
 {
     typedef typename Store<QBF>::type QT;
     typedef typename Store<OBF>::type OT;
@@ -73,6 +80,14 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
 #pragma unroll
         for (int c = 0; c < 4; ++c) vv[c] = to_f32(vp[c]);
     }
+    float zo[4], wo[4];
+    if constexpr (OG) {
+        Raw4<QT> rz;
+        rz.load(z_out + (size_t)bh * DV + 4 * cg);
+        rz.to_f32(zo);
+        const float4 t = *reinterpret_cast<const float4 *>(weight + 4 * cg);
+        wo[0] = t.x; wo[1] = t.y; wo[2] = t.z; wo[3] = t.w;
+    }
     lds_barrier();
 
     f32x4 p = {0.f, 0.f, 0.f, 0.f}, rd = {0.f, 0.f, 0.f, 0.f};
@@ -101,7 +116,24 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
     f32x4 w;
 #pragma unroll
     for (int c = 0; c < 4; ++c) w[c] = bt * (vv[c] - pt[c]);
-    if (rg == 0) {
+    if constexpr (OG) {
+        // every row group holds the full outputs; reduce over one group's lanes
+        float oc[4], ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            oc[c] = rt[c] + qkt * w[c];
+            ss += oc[c] * oc[c];
+        }
+#pragma unroll
+        for (int m = 1; m < NCG; m <<= 1) ss += __shfl_xor(ss, m, NCG);
+        const float inv = rsqrtf(ss * (1.f / DV) + eps);
+        if (rg == 0) {
+            float yv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) yv[c] = oc[c] * inv * wo[c] * sigmoid_f32(zo[c]);
+            store4(o + (size_t)bh * DV + 4 * cg, yv);
+        }
+    } else if (rg == 0) {
         OT *op = o + (size_t)bh * DV + 4 * cg;
 #pragma unroll
         for (int c = 0; c < 4; ++c) op[c] = from_f32<OT>(rt[c] + qkt * w[c]);
@@ -115,22 +147,29 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
     }
 }
 
-template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL>
+template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL, bool OG>
 hipError_t launch(const DecodeArgs &a, hipStream_t stream)
 {
     typedef typename Store<QBF>::type QT;
     typedef typename Store<GBF>::type GT;
     typedef typename Store<OBF>::type OT;
-    kda_decode_kernel<DK, DV, QBF, GBF, OBF, GL><<<(unsigned)(a.B * a.H), NTHREADS, 0, stream>>>(
+    kda_decode_kernel<DK, DV, QBF, GBF, OBF, GL, OG><<<(unsigned)(a.B * a.H), NTHREADS, 0, stream>>>(
         (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta,
-        a.S, (OT *)a.o, a.A_log, a.H);
+        a.S, (OT *)a.o, a.A_log, a.H, (const QT *)a.z_out, a.weight, a.eps);
     return hipGetLastError();
+}
+
+template <int DK, int DV, bool QBF, bool GBF, bool OBF, bool GL>
+hipError_t dispatch_epilogue(const DecodeArgs &a, hipStream_t s)
+{
+    return a.z_out ? launch<DK, DV, QBF, GBF, OBF, GL, true>(a, s) : launch<DK, DV, QBF, GBF, OBF, GL, false>(a, s);
 }
 
 template <int DK, int DV, bool QBF, bool GBF, bool GL>
 hipError_t dispatch_gate(const DecodeArgs &a, hipStream_t s)
 {
-    return a.out_bf16 ? launch<DK, DV, QBF, GBF, true, GL>(a, s) : launch<DK, DV, QBF, GBF, false, GL>(a, s);
+    return a.out_bf16 ? dispatch_epilogue<DK, DV, QBF, GBF, true, GL>(a, s)
+                      : dispatch_epilogue<DK, DV, QBF, GBF, false, GL>(a, s);
 }
 
 template <int DK, int DV, bool QBF, bool GBF>

@@ -93,6 +93,16 @@ template <> struct Raw4<float> {
     __device__ __forceinline__ void to_f32(float (&x)[4]) const { x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; }
 };
 
+// Store 4 consecutive values in the storage type (one 8- or 16-byte store).
+__device__ __forceinline__ void store4(uint16_t *p, const float (&x)[4]) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    *reinterpret_cast<uint2 *>(p) = make_uint2(lo, hi);
+}
+__device__ __forceinline__ void store4(float *p, const float (&x)[4]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
 // ------------------------------------------------------ MFMA precisions
 
 
@@ -362,6 +372,12 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float gate_from_logit(float z, float s) {
     constexpr float LOG2E_ = 1.4426950408889634f;
     return -5.0f * fast_rcp(1.0f + fast_exp2(-s * z * LOG2E_));
+}
+
+// Logistic sigmoid; for very negative x the exp overflows and rcp(inf) = 0.
+__device__ __forceinline__ float sigmoid_f32(float x) {
+    constexpr float LOG2E_ = 1.4426950408889634f;
+    return fast_rcp(1.0f + fast_exp2(-x * LOG2E_));
 }
 
 }  // namespace kda

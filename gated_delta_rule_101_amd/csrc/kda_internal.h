@@ -21,8 +21,11 @@ struct ChunkFwdArgs {
 struct DecodeArgs {
     const void *q, *k, *v, *g, *beta;
     float *S;
-    void *o;
+    void *o;                          // o, or y when the output epilogue is fused
     const float *A_log = nullptr;     // as in ChunkFwdArgs
+    const void *z_out = nullptr;      // non-null: o -> o / rms(o) * weight * sigmoid(z_out), z_out in q's dtype
+    const float *weight = nullptr;
+    float eps = 0.f;
     int B, H, dk, dv;
     bool qkv_bf16, gate_bf16, out_bf16;
 };
@@ -38,9 +41,21 @@ struct SpecArgs {
     bool qkv_bf16, gate_bf16, out_bf16;
 };
 
+// y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(z) per row of dv channels.
+struct OutputGateArgs {
+    const void *o, *z;
+    const float *weight;
+    void *y;
+    int64_t rows;
+    int dv;                           // multiple of 64, at most 512
+    float eps;
+    bool o_bf16, z_bf16, y_bf16;
+};
+
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        // any dtypes
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_spec_step(const SpecArgs &a, hipStream_t stream);           // dk, dv in {64, 128}
+hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
 
 }  // namespace kda

@@ -7,6 +7,7 @@ the library is missing or a call fails, an exception is raised.
 
     o, S_final = kda_chunk_fwd(q, k, v, g, beta, S0=None)
     o = kda_decode_step(q, k, v, g, beta, S)        # S updated in place
+    y = kda_output_gate(o, z_out, weight, eps)      # RMS-normalised, sigmoid-gated
 
 The output is float32 unless out_dtype=torch.bfloat16 is asked for: a
 bfloat16 output carries only 8 significant bits, which for heavy-tailed
@@ -29,7 +30,8 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_verify_step", "kda_commit_step",
-           "kda_decode_step", "kda_decode_step_gate", "kda_status_string", "kda_abi_version")
+           "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
+           "kda_status_string", "kda_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -62,6 +64,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_verify_step.restype = i
     lib.kda_commit_step.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_commit_step.restype = i
+    f = ctypes.c_float
+    lib.kda_output_gate.argtypes = [vp, vp, vp, f, vp, ctypes.c_int64, i, i, i, i, vp]
+    lib.kda_output_gate.restype = i
+    lib.kda_decode_step_gated.argtypes = [vp] * 9 + [f, vp] + [i] * 7 + [vp]
+    lib.kda_decode_step_gated.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -283,3 +290,64 @@ def kda_commit_step(k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: tor
                              B, K, H, dk, dv, _dtype_code(k), _dtype_code(g), _stream_handle(stream, dev))
     _raise(st, "kda_commit_step")
     return S
+
+
+def kda_output_gate(o: torch.Tensor, z: torch.Tensor, weight: torch.Tensor, eps: float = 1e-6, *,
+                    y: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                    stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The output epilogue y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(z)
+    over the last axis (dv) of o [..., dv]; z has o's shape, weight is float32
+    [dv].  y may be passed (o itself for in place, same dtype); otherwise it is
+    allocated with out_dtype (default o's dtype)."""
+    lib = load_library()
+    dv = o.shape[-1]
+    if z.shape != o.shape:
+        raise ValueError("z must have o's shape")
+    if weight.shape != (dv,) or weight.dtype != torch.float32:
+        raise ValueError("weight must be float32 [dv]")
+    if y is None:
+        y = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=o.device)
+    elif y.shape != o.shape:
+        raise ValueError("y must have o's shape")
+    dev = _check_dev(o, z, weight, y)
+    rows = o.numel() // dv if dv else 0
+    st = lib.kda_output_gate(_ptr(o), _ptr(z), _ptr(weight), float(eps), _ptr(y), rows, dv,
+                             _dtype_code(o), _dtype_code(z), _dtype_code(y), _stream_handle(stream, dev))
+    _raise(st, "kda_output_gate")
+    return y
+
+
+def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, S: torch.Tensor, z_out: torch.Tensor, weight: torch.Tensor,
+                          eps: float = 1e-6, *, A_log: Optional[torch.Tensor] = None,
+                          y: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """kda_decode_step followed, in the same kernel, by the output epilogue:
+    returns y [B,H,dv] = o / sqrt(mean(o^2) + eps) * weight * sigmoid(z_out)
+    (z_out [B,H,dv] in q's dtype, weight float32 [dv]); S is updated in place.
+    With A_log [H] given, g holds gate logits as in kda_decode_step_gate."""
+    lib = load_library()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, H, dv) or beta.shape != (B, H):
+        raise ValueError("shape mismatch between q, k, v, g, beta")
+    if S.shape != (B, H, dk, dv) or S.dtype != torch.float32:
+        raise ValueError("S must be float32 [B,H,dk,dv]")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != g.dtype:
+        raise TypeError("q, k, v share one dtype; g and beta share one dtype")
+    if z_out.shape != (B, H, dv) or z_out.dtype != q.dtype:
+        raise ValueError("z_out must be [B,H,dv] in q's dtype")
+    if weight.shape != (dv,) or weight.dtype != torch.float32:
+        raise ValueError("weight must be float32 [dv]")
+    if A_log is not None:
+        _check_head_scale(A_log, H)
+    if y is None:
+        y = torch.empty((B, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif y.shape != (B, H, dv):
+        raise ValueError("y must be [B,H,dv]")
+    dev = _check_dev(q, k, v, g, beta, S, z_out, weight, A_log, y)
+    st = lib.kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(A_log), _ptr(beta), _ptr(S),
+                                   _ptr(z_out), _ptr(weight), float(eps), _ptr(y), B, H, dk, dv,
+                                   _dtype_code(q), _dtype_code(g), _dtype_code(y), _stream_handle(stream, dev))
+    _raise(st, "kda_decode_step_gated")
+    return y

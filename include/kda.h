@@ -36,6 +36,17 @@
  * scale is read as acting on the logit inside the sigmoid, which keeps every
  * g in [-5, 0] for any A_h and is the plain -5 sigmoid(z) at A_h = 0.
  *
+ * kda_output_gate and kda_decode_step_gated apply the module's output
+ * epilogue to the read: per (token, head) row of dv channels
+ *     y = o / sqrt(mean_j o_j^2 + eps) * weight * sigmoid(z_out)
+ * ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the output-gate paragraph: a
+ * full-rank, input-dependent gate after the recurrent read decides which
+ * channels pass; "K3 Architecture Illustrated", the KDA section under FIG 21:
+ * the module includes normalisation and output gating).  The pages give no
+ * formula; the reading is RMS normalisation over the head's dv channels with
+ * a learnable per-channel weight [dv] shared by all heads, then a sigmoid
+ * gate from per-token logits with o's shape.
+ *
  * Conventions for every entry point
  * ---------------------------------
  *  - Tensor pointers are DEVICE pointers to contiguous row-major memory, each
@@ -57,6 +68,8 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -74,7 +87,7 @@ typedef enum {
 } kda_status_t;
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /*
  * kda_chunk_fwd -- chunkwise forward over T tokens for B sequences x H heads.
@@ -198,6 +211,44 @@ kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const 
                              const int *accepted, float *S,
                              int B, int K, int H, int dk, int dv,
                              kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, void *stream);
+
+/*
+ * kda_output_gate -- the output epilogue over `rows` rows of dv channels
+ * (rows = B * T * H for a forward's o [B, T, H, dv]).
+ *
+ *   o      [rows, dv] o_dtype       the reads
+ *   z      [rows, dv] z_dtype       gate logits
+ *   weight [dv] float32             per-channel normalisation weight
+ *   eps    >= 0, finite             added to the mean square (eps = 0 makes an
+ *                                   all-zero row NaN, as the formula does)
+ *   y      [rows, dv] y_dtype       the result; may be o itself when
+ *                                   y_dtype == o_dtype, must not overlap z or
+ *                                   weight otherwise
+ *
+ * dv a multiple of 64 up to 512 (else KDA_ERR_UNSUPPORTED).  float32 arithmetic.
+ */
+kda_status_t kda_output_gate(const void *o, const void *z, const float *weight, float eps, void *y,
+                             int64_t rows, int dv, kda_dtype_t o_dtype, kda_dtype_t z_dtype,
+                             kda_dtype_t y_dtype, void *stream);
+
+/*
+ * kda_decode_step_gated -- a decode step whose output goes through the output
+ * epilogue inside the same kernel: y = kda_output_gate(o) with o the read
+ * kda_decode_step would write.
+ *
+ *   g       [B, H, dk] gate_dtype: the log-decay when A_log is NULL, gate
+ *           logits (as kda_decode_step_gate) when A_log [H] float32 is given
+ *   z_out   [B, H, dv] qkv_dtype    output-gate logits
+ *   weight  [dv] float32, eps >= 0  as kda_output_gate
+ *   y       [B, H, dv] out_dtype    the gated output (o itself is not stored)
+ *
+ * Otherwise as kda_decode_step; y must not overlap any input or S.
+ */
+kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v, const void *g,
+                                   const float *A_log, const void *beta, float *S, const void *z_out,
+                                   const float *weight, float eps, void *y, int B, int H, int dk, int dv,
+                                   kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                   void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status_t status);

@@ -185,6 +185,32 @@ def decode_gate_logit_inputs(w: Workload, step: int, seed: int = 0) -> Dict[str,
     return out
 
 
+_OUT_GATE_STREAM = 8
+_OUT_WEIGHT_STREAM = 9
+_OUT_ROWS_STREAM = 10
+
+
+def output_gate_logits(shape, dtype: str, seed: int = 0, stream: int = 0) -> HostTensor:
+    """Output-gate logits z_out ~ N(0, 1) of any shape, rounded to `dtype`."""
+    return _to_dtype(_normal_f32(_rng(seed, _OUT_GATE_STREAM, stream), tuple(shape)), dtype)
+
+
+def output_norm_weight(dv: int, seed: int = 0) -> HostTensor:
+    """Per-channel normalisation weight 1 + 0.1 N(0, 1), float32 [dv]."""
+    return HostTensor(np.float32(1.0) + np.float32(0.1) * _normal_f32(_rng(seed, _OUT_WEIGHT_STREAM), (dv,)),
+                      "f32")
+
+
+def read_rows(rows: int, dv: int, dtype: str, seed: int = 0) -> HostTensor:
+    """Stand-in reads o [rows, dv] for the output epilogue: N(0, 1) rows each
+    scaled by exp(N(0, 1.5)), so row norms span several orders of magnitude;
+    rows 3, 10, 17, ... are all zero (the eps-only case)."""
+    rng = _rng(seed, _OUT_ROWS_STREAM)
+    x = _normal_f32(rng, (rows, dv)) * np.exp(np.float32(1.5) * _normal_f32(rng, (rows, 1)))
+    x[3::7] = 0.0
+    return _to_dtype(x, dtype)
+
+
 def decode_initial_state(w: Workload, seed: int = 0) -> HostTensor:
     """S before the first decode step: [B, H, dk, dv] fp32, N(0, s0_sd) (zero if s0_sd is None)."""
     assert w.kind == "decode"

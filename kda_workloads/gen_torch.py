@@ -91,3 +91,17 @@ def decode_step_inputs(w: Workload, step: int, seed: int = 0, device="cuda") -> 
     out["g"] = _log_decay((B, H, dk), w, _gen(seed, base + 4, device), device, (B, H, dk)).to(_DTYPE[w.gate])
     out["beta"] = torch.sigmoid(_normal((B, H), _gen(seed, base + 5, device), device)).to(_DTYPE[w.gate])
     return out
+
+
+_OUT_GATE_STREAM = 8
+_OUT_WEIGHT_STREAM = 9
+
+
+def output_gate_logits(shape, dtype: str, seed: int = 0, device="cuda") -> torch.Tensor:
+    """Output-gate logits z_out ~ N(0, 1) (same recipe as gen.output_gate_logits)."""
+    return _normal(tuple(shape), _gen(seed, _OUT_GATE_STREAM, device), device).to(_DTYPE[dtype])
+
+
+def output_norm_weight(dv: int, seed: int = 0, device="cuda") -> torch.Tensor:
+    """Per-channel normalisation weight 1 + 0.1 N(0, 1), float32 [dv]."""
+    return _normal((dv,), _gen(seed, _OUT_WEIGHT_STREAM, device), device).mul_(0.1).add_(1.0)

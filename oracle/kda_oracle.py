@@ -144,6 +144,31 @@ def gate_log_decay(z, A_log, head_axis: int = -2) -> np.ndarray:
     return -5.0 * sig
 
 
+def output_gate(o, z, weight, eps: float) -> np.ndarray:
+    """The output epilogue after the read, float64:
+    y = o / sqrt(mean_j o_j^2 + eps) * weight * sigmoid(z), per (token, head)
+    row over the dv value channels.
+
+    "Kimi K3 - Lesson 3 of 14 - Sequence axis", the output-gate paragraph: after
+    the recurrent read a gate decides which channels of the result pass through,
+    full-rank and input-dependent per token; "K3 Architecture Illustrated", the
+    KDA section under FIG 21: the module also holds a normalisation and output
+    gating.  Neither page gives the form.  Reading: RMS normalisation of each
+    head's read over its dv channels with a learnable per-channel weight
+    [dv], then a sigmoid gate (a value in (0, 1) per channel, "which channels
+    pass") from per-token logits z with o's shape.
+
+    o, z: [..., dv]; weight: [dv]; eps >= 0.
+    """
+    o = np.asarray(o, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    inv_rms = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    e = np.exp(-np.abs(z))
+    sig = np.where(z >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return o * inv_rms * w * sig
+
+
 def build_variant(source_text: str) -> Oracle:
     """Compile a modified copy of the oracle source into a temporary library.
 

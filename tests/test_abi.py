@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     from gated_delta_rule_101_amd import kda
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for st in (kda.KDA_OK, kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_LAUNCH):
         assert lib.kda_status_string(st).decode().startswith("KDA_")
     assert lib.kda_status_string(77).decode() == "KDA_ERR_UNKNOWN"
@@ -159,3 +159,41 @@ def test_follow_on_entry_points_validation(lib):
         1, 2, 64, 64, 1, 0, 0, None)
     assert decg(A=None) == INV
     assert decg(S=A) == INV                    # S over A_log
+
+
+def test_output_epilogue_validation(lib):
+    from gated_delta_rule_101_amd import kda
+    INV, UNS, OK = kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_OK
+    big = 1 << 24
+    o, z, w, y = big, 2 * big, 3 * big, 4 * big
+    gate = lambda o=o, z=z, w=w, y=y, eps=1e-6, rows=10, dv=128, od=0, zd=1, yd=0: \
+        lib.kda_output_gate(o, z, w, eps, y, rows, dv, od, zd, yd, None)  # noqa: E731
+    assert gate(o=None) == INV
+    assert gate(z=None) == INV
+    assert gate(w=None) == INV
+    assert gate(y=None) == INV
+    assert gate(w=w + 4) == INV                  # misaligned weight
+    assert gate(y=y + 8) == INV                  # misaligned output
+    assert gate(eps=-1.0) == INV
+    assert gate(eps=float("nan")) == INV
+    assert gate(eps=float("inf")) == INV
+    assert gate(rows=-1) == INV
+    assert gate(od=3) == INV
+    assert gate(y=z + 256) == INV                # y overlaps z
+    assert gate(y=o + 256) == INV                # partial overlap with o
+    assert gate(y=w) == INV                      # y over the weight
+    assert gate(dv=96) == UNS
+    assert gate(dv=1024) == UNS
+    assert gate(rows=0) == OK
+    # fused decode: the epilogue's arguments are checked with the decode's
+    q, k, v, g, b, S, zo, wt, yy = (i * big for i in range(1, 10))
+    dec = lambda **kw: lib.kda_decode_step_gated(*(kw.get(n, d) for n, d in (  # noqa: E731
+        ("q", q), ("k", k), ("v", v), ("g", g), ("A", None), ("beta", b), ("S", S), ("z", zo), ("w", wt))),
+        kw.get("eps", 1e-6), kw.get("y", yy), kw.get("B", 2), 3, 128, 128, 1, 0, 0, None)
+    assert dec(z=None) == INV
+    assert dec(w=None) == INV
+    assert dec(eps=-0.5) == INV
+    assert dec(z=zo + 4) == INV                  # misaligned logits
+    assert dec(y=zo + 128) == INV                # y over the logits
+    assert dec(y=wt) == INV                      # y over the weight
+    assert dec(B=0) == OK

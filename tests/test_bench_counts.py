@@ -33,3 +33,11 @@ def test_speculative_counts():
     # commit: the state read and written, n accepted drafts of k, v, g, beta, B int32 counts
     commit = 2 * state + B * H * n * (2 * 2 * d + 4 * (d + 1)) + 4 * B
     assert bench.spec_bytes(B, H, K, n, d, d, 2, 4, 4) == (verify, commit)
+
+
+def test_epilogue_counts():
+    # rows of dv = 128: fp32 read, bf16 logit, fp32 result per channel, plus the weight
+    assert bench.epilogue_bytes(10, 128, 4, 2, 4) == 10 * 128 * 10 + 4 * 128
+    # fused decode: the decode step plus bf16 output-gate logits and the weight
+    assert bench.gated_decode_bytes(256, 96, 128, 128, 2, 4, 4) == \
+        bench.decode_bytes(256, 96, 128, 128, 2, 4, 4) + 256 * 96 * 128 * 2 + 4 * 128
