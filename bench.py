@@ -10,7 +10,7 @@ token carrying all H heads).  The decode path is timed on its own workload
 "decode" in GB/s.  Speculative decoding on the same states (verify 16 draft
 tokens, commit 8 of them) is reported under "speculative", the output
 epilogue (alone over the training-shape reads, and fused into decode) under
-"epilogue".  Each carries a
+"epilogue", the chunkwise backward under "backward".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
 by HIP events on the launch stream.
 
@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 METRIC = "KDA chunk-fwd tokens/s + TFLOP/s (H=32,d=128,T=16K); decode GB/s vs roofline"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 CHUNK = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -73,6 +74,23 @@ def gated_decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) -> int:
     """A decode step with the epilogue fused: the decode's bytes plus the
     output-gate logits (q's dtype) and the weight vector."""
     return decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) + B * H * dv * s_qkv + 4 * dv
+
+
+def bwd_flops(B, T, H, dk, dv, C=CHUNK) -> int:
+    """Algorithmic FLOP of the chunkwise backward per token-head: eight
+    C x d x d products with the state or its gradient (recomputed W S and
+    K-bar^T U; K-bar dS', (Gamma.Q)^T dO, W^T dU; dO S^T, dU S^T, U dS'^T)
+    = 16 dk dv; the C x C x d products at their non-zero half (A_qk, A_kk,
+    W, dT's key part, dK~ and four pairwise-gradient products on the key
+    side = 9 C dk; U_v, A_qk^T dO, dA_qk, dT's value part, dV = 5 C dv);
+    the inverse and N^T dN N^T ~ C^2."""
+    return B * T * H * (16 * dk * dv + 9 * C * dk + 5 * C * dv + C * C)
+
+
+def bwd_bytes(B, T, H, dk, dv, s_qkv, s_g, s_do) -> int:
+    """Compulsory HBM bytes of one backward: read q, k, v, g, beta, dO once,
+    write float32 dq, dk, dv, dg, dbeta once (no initial or final state)."""
+    return B * T * H * (s_qkv * (2 * dk + dv) + s_g * (dk + 1) + s_do * dv + 4 * (3 * dk + dv + 1))
 
 
 def kernel_source_hash(files) -> str:
@@ -280,6 +298,34 @@ def bench_epilogue(kda, reps=10):
     return out
 
 
+def bench_backward(kda, reps=3):
+    """kda_chunk_bwd on the training shape (bf16 q, k, v, g, beta; float32
+    upstream gradient dO; zero initial state, no final-state gradient)."""
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.TRAIN_BF16
+    d = gen_torch.fwd_inputs(w)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    dO = torch.randn((w.B, w.T, w.H, w.dv), generator=gen, device="cuda", dtype=torch.float32)
+    ws = torch.empty(kda.kda_chunk_bwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+    log(f"[bench] backward workspace {ws.numel() / 1e9:.2f} GB")
+    stream = torch.cuda.current_stream()
+    fn = lambda: kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None, dO, None,  # noqa: E731
+                                   want_dS0=False, workspace=ws)
+    wall, ker = time_launches(fn, reps, 1, stream)
+    flops = bwd_flops(w.B, w.T, w.H, w.dk, w.dv)
+    nbytes = bwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 4)
+    tfs = flops / ker / 1e12
+    log(f"[bench] backward {wall / reps * 1e3:.3f} ms (kernels {ker * 1e3:.3f} ms), {tfs:.1f} TFLOP/s, "
+        f"{w.B * w.T / (wall / reps):.3e} tokens/s")
+    return {"workload": w.name + "_bwd", "ms": round(wall / reps * 1e3, 4),
+            "tokens_per_s": round(w.B * w.T / (wall / reps), 1),
+            "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
+
+
 def cpu_baseline(w, d, batch=32):
     """The float64 oracle on the same workload, every head over the full
     sequence, on all host threads, `batch` heads per call (only the recurrence
@@ -431,6 +477,7 @@ def main():
         out["decode"] = bench_decode(kda, args.decode_reps)
         out["speculative"] = bench_speculative(kda, 10)
         out["epilogue"] = bench_epilogue(kda)
+        out["backward"] = bench_backward(kda)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d)
     print(json.dumps(out), flush=True)

@@ -5,11 +5,12 @@ for gfx950 (libkda.so, declared in include/kda.h) and its Python binding.
     from gated_delta_rule_101_amd import kda_verify_step, kda_commit_step        # speculative decoding
     from gated_delta_rule_101_amd import kda_chunk_fwd_gate, kda_decode_step_gate  # g from gate logits
     from gated_delta_rule_101_amd import kda_output_gate, kda_decode_step_gated    # output epilogue
+    from gated_delta_rule_101_amd import kda_chunk_bwd                             # gradients
 """
 
 from .kda import (  # noqa: F401
     EXPORTS, KDA_BF16, KDA_ERR_INVALID_ARG, KDA_ERR_LAUNCH, KDA_ERR_UNSUPPORTED, KDA_F32, KDA_OK,
-    KdaError, kda_chunk_fwd, kda_chunk_fwd_gate, kda_commit_step, kda_decode_step,
+    KdaError, kda_chunk_bwd, kda_chunk_bwd_workspace_bytes, kda_chunk_fwd, kda_chunk_fwd_gate, kda_commit_step, kda_decode_step,
     kda_decode_step_gate, kda_decode_step_gated, kda_output_gate, kda_verify_step, load_library,
     status_string,
 )

@@ -289,6 +289,65 @@ kda_status_t kda_output_gate(const void *o, const void *z, const float *weight, 
     return kda::launch_output_gate(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+    return kda::chunk_bwd_workspace_floats(B, T, H, dk, dv) * sizeof(float);
+}
+
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           const float *S0, const void *dO, const float *dS_final,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                           void *workspace, size_t workspace_bytes,
+                           int B, int T, int H, int dk_dim, int dv_dim,
+                           kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t do_dtype, void *stream)
+{
+    if (B < 0 || T < 0 || H < 0 || dk_dim <= 0 || dv_dim <= 0) return KDA_ERR_INVALID_ARG;
+    if (!valid_dtype(qkv_dtype) || !valid_dtype(gate_dtype) || !valid_dtype(do_dtype)) return KDA_ERR_INVALID_ARG;
+    if ((dk_dim != 64 && dk_dim != 128) || (dv_dim != 64 && dv_dim != 128)) return KDA_ERR_UNSUPPORTED;
+    const int64_t nc = ((int64_t)T + 31) / 32;
+    if ((int64_t)B * T >= ((int64_t)1 << 31) || (int64_t)B * H * nc >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return KDA_OK;
+
+    const size_t tok = (size_t)B * T * H, st = (size_t)B * H * dk_dim * dv_dim * sizeof(float);
+    const size_t sq = dsize(qkv_dtype), sg = dsize(gate_dtype), so = dsize(do_dtype);
+    const size_t need = kda_chunk_bwd_workspace_bytes(B, T, H, dk_dim, dv_dim);
+    if (T > 0) {
+        const void *req[] = {q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta};
+        for (const void *p : req)
+            if (!p || !aligned16(p)) return KDA_ERR_INVALID_ARG;
+        if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    }
+    if ((S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        return KDA_ERR_INVALID_ARG;
+    const bool run = T > 0;
+    const Span ins[] = {span(run ? q : nullptr, run ? tok * dk_dim * sq : 0), span(run ? k : nullptr, run ? tok * dk_dim * sq : 0),
+                        span(run ? v : nullptr, run ? tok * dv_dim * sq : 0), span(run ? g : nullptr, run ? tok * dk_dim * sg : 0),
+                        span(run ? beta : nullptr, run ? tok * sg : 0), span(run ? dO : nullptr, run ? tok * dv_dim * so : 0),
+                        span(S0, S0 ? st : 0), span(dS_final, dS_final ? st : 0)};
+    const Span outs[] = {span(run ? dq : nullptr, run ? tok * dk_dim * 4 : 0), span(run ? dk : nullptr, run ? tok * dk_dim * 4 : 0),
+                         span(run ? dv : nullptr, run ? tok * dv_dim * 4 : 0), span(run ? dg : nullptr, run ? tok * dk_dim * 4 : 0),
+                         span(run ? dbeta : nullptr, run ? tok * 4 : 0), span(dS0, dS0 ? st : 0),
+                         span(run ? workspace : nullptr, run ? need : 0)};
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        for (const Span &s : ins)
+            if (overlap(outs[i], s)) return KDA_ERR_INVALID_ARG;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+            if (overlap(outs[i], outs[j])) return KDA_ERR_INVALID_ARG;
+    }
+    if (T == 0 && !dS0) return KDA_OK;
+
+    kda::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.S0 = S0; a.dO = dO; a.dS_final = dS_final;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dS0 = dS0;
+    a.ws = kda::chunk_bwd_workspace(run ? (float *)workspace : nullptr, B, T, H, dk_dim, dv_dim);
+    a.B = B; a.T = T; a.H = H; a.dk_dim = dk_dim; a.dv_dim = dv_dim;
+    a.qkv_bf16 = qkv_dtype == KDA_BF16;
+    a.gate_bf16 = gate_dtype == KDA_BF16;
+    a.do_bf16 = do_dtype == KDA_BF16;
+    return kda::launch_chunk_bwd(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
 const char *kda_status_string(kda_status_t status)
 {
     switch (status) {

@@ -1,0 +1,576 @@
+// Chunkwise KDA backward for gfx950: gradients of a forward pass with respect
+// to q, k, v, g, beta and the initial state, given the upstream gradients of
+// the outputs (and of the final state).
+//
+// The pages teach the chunkwise forward ("Kimi K3 - Lesson 3 of 14 - Sequence
+// axis": sequential between chunks, parallel within, keys rescaled by 1/Gamma
+// inside 16-token tiles bounded by e^80 under g_min = -5) and describe the
+// layer being trained, but give no gradients; these kernels differentiate the
+// same chunk algebra.  With b the chunk-local inclusive cumsum of g and
+// Gamma = e^b, per chunk of BC tokens:
+//   A_qk = tril(sum_c q_rc k_sc e^{b_rc - b_sc}),  A_kk0 = strict_tril(k, k same)
+//   N = (I + Diag(beta) A_kk0)^-1,  W = N Diag(beta) (Gamma . K),  U_v = N Diag(beta) V
+//   forward carry   U = U_v - W S,   S' = Diag(Gamma_C) S + K-bar^T U
+//   reverse carry   dU = K-bar dS' + A_qk^T dO,
+//                   dS = Diag(Gamma_C) dS' + (Gamma . Q)^T dO - W^T dU
+// then, per chunk, dQ~ = dO S^T, dW = -dU S^T, dK-bar = U dS'^T,
+// dA_qk = tril(dO U^T), dT = tril(dW K~^T + dU V^T), dN = dT Diag(beta),
+// dA_kk = -strict_tril(N^T dN N^T), the pairwise e^{b_r - b_s} products
+// differentiated in both roles with tile-local references, and
+// dg = reverse cumsum of db.
+//
+// Five kernels, all float32 (matrix-core v_mfma_f32_16x16x4_f32), with
+// 32-token chunks so that every per-chunk matrix sits in LDS:
+//   prep     (per chunk)         b, A_qk, A_kk0, N, W, U_v        -> workspace
+//   states   (per head, slab)    chunk-start states S, U          -> workspace
+//   dstates  (per head, slab)    reverse carry: chunk-end dS', dU -> workspace; dS0
+//   sgrads   (per chunk)         dQ~, dW, dK-bar, dA_qk, dGamma_C -> workspace
+//   intra    (per chunk)         dq, dk, dv, dg, dbeta
+// Value columns of S (and of dS) evolve independently, so the two carries
+// split dv into 64-column slabs like the forward.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int BC = 32;        // tokens per chunk in the backward
+constexpr int TL = 16;        // tokens per tile (reference granularity)
+constexpr int NTH = 256;
+constexpr int NW = NTH / 64;
+constexpr int SW = 64;        // value columns per slab in the carries
+
+// Cooperative GEMM over the workgroup: out(i, j) = sum_kk A(i, kk) B(kk, j),
+// i < M, j < N (multiples of 16), kk < K (multiple of 4).  Each 16 x 16 tile
+// goes to one wave; lane (r16, kq) feeds A(i0 + r16, kk + kq) and
+// B(kk + kq, j0 + r16) and receives rows i0 + 4 kq + 0..3 of column j0 + r16.
+// epi(i, j, value) is called once per result.
+template <typename FA, typename FB, typename FE>
+__device__ __forceinline__ void wg_gemm(int M, int N, int K, FA A, FB B, FE epi)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int tn = N >> 4, nt = (M >> 4) * tn;
+    for (int t = wave; t < nt; t += NW) {
+        const int i0 = (t / tn) << 4, j0 = (t % tn) << 4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < K; kk += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + kq), B(kk + kq, j0 + r16), acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) epi(i0 + 4 * kq + r, j0 + r16, acc[r]);
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    return x;
+}
+
+// element (b, t, h, c) of a [B, T, H, d] tensor
+__device__ __forceinline__ size_t tix(int b, int t, int h, int c, int T, int H, int d)
+{
+    return (((size_t)b * T + t) * H + h) * d + c;
+}
+
+// ---------------------------------------------------------------- prep
+
+template <int DK, int DV, typename QT, typename GT>
+__global__ void __launch_bounds__(NTH)
+kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
+                    const GT *__restrict__ g, const GT *__restrict__ beta, BwdWorkspace ws, int T, int H, int NC)
+{
+    constexpr int LK = DK + 4, LV = DV + 4, LC = BC + 4;
+    __shared__ float sq[BC][LK], sk[BC][LK], sb[BC][LK], sv[BC][LV];
+    __shared__ float sA[BC][LC], sL[BC][LC], sN[BC][LC];
+    __shared__ float sbeta[BC];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
+    const size_t ch = (size_t)bh * NC + c;
+
+    for (int e = tid; e < BC * DK; e += NTH) {
+        const int r = e / DK, x = e % DK, t = c * BC + r;
+        const bool live = t < T;
+        const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
+        sq[r][x] = live ? to_f32(q[i]) : 0.f;
+        sk[r][x] = live ? to_f32(k[i]) : 0.f;
+        sb[r][x] = live ? to_f32(g[i]) : 0.f;
+    }
+    for (int e = tid; e < BC * DV; e += NTH) {
+        const int r = e / DV, x = e % DV, t = c * BC + r;
+        sv[r][x] = t < T ? to_f32(v[tix(bb, t, h, x, T, H, DV)]) : 0.f;
+    }
+    if (tid < BC) {
+        const int t = c * BC + tid;
+        sbeta[tid] = t < T ? to_f32(beta[((size_t)bb * T + t) * H + h]) : 0.f;
+    }
+    for (int e = tid; e < BC * LC; e += NTH) {
+        (&sA[0][0])[e] = 0.f;
+        (&sL[0][0])[e] = 0.f;
+    }
+    __syncthreads();
+    if (tid < DK) {   // chunk-local inclusive cumsum of g per key channel
+        float acc = 0.f;
+        for (int r = 0; r < BC; ++r) {
+            acc += sb[r][tid];
+            sb[r][tid] = acc;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < BC * DK; e += NTH) ws.b[ch * BC * DK + e] = sb[e / DK][e % DK];
+
+    // Gram matrices, one row tile at a time: rows scaled by e^{b - rho},
+    // keys by e^{rho - b}, rho = b at the end of the previous tile.
+    for (int m = 0; m < BC / TL; ++m) {
+        auto rho = [&](int x) { return m ? sb[TL * m - 1][x] : 0.f; };
+        wg_gemm(2 * TL, TL * (m + 1), DK,
+                [&](int i, int x) {
+                    const int r = TL * m + (i & (TL - 1));
+                    const float f = expf(sb[r][x] - rho(x));
+                    return (i < TL ? sq[r][x] : sk[r][x]) * f;
+                },
+                [&](int x, int s) { return sk[s][x] * expf(rho(x) - sb[s][x]); },
+                [&](int i, int s, float val) {
+                    const int r = TL * m + (i & (TL - 1));
+                    if (i < TL) sA[r][s] = s <= r ? val : 0.f;
+                    else sL[r][s] = s < r ? val : 0.f;
+                });
+    }
+    __syncthreads();
+    if (tid < BC) {   // column tid of N = (I + Diag(beta) A_kk0)^-1 by forward substitution
+        const int j = tid;
+        float x[BC];
+#pragma unroll
+        for (int i = 0; i < BC; ++i) {
+            float s = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int l = 0; l < i; ++l) s -= sbeta[i] * sL[i][l] * x[l];
+            x[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < BC; ++i) sN[i][j] = x[i];
+    }
+    __syncthreads();
+    for (int e = tid; e < BC * BC; e += NTH) {
+        const int r = e / BC, s = e % BC;
+        ws.Aqk[ch * BC * BC + e] = sA[r][s];
+        ws.Akk0[ch * BC * BC + e] = sL[r][s];
+        ws.N[ch * BC * BC + e] = sN[r][s];
+    }
+    // W = N Diag(beta) (Gamma . K),  U_v = N Diag(beta) V
+    wg_gemm(BC, DK, BC, [&](int i, int s) { return sN[i][s]; },
+            [&](int s, int x) { return sbeta[s] * expf(sb[s][x]) * sk[s][x]; },
+            [&](int i, int x, float val) { ws.W[(ch * BC + i) * DK + x] = val; });
+    wg_gemm(BC, DV, BC, [&](int i, int s) { return sN[i][s]; },
+            [&](int s, int x) { return sbeta[s] * sv[s][x]; },
+            [&](int i, int x, float val) { ws.U[(ch * BC + i) * DV + x] = val; });
+}
+
+// --------------------------------------------------------- forward carry
+
+template <int DK, int DV, typename QT>
+__global__ void __launch_bounds__(NTH)
+kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, BwdWorkspace ws,
+                      int T, int H, int NC, int nslab)
+{
+    constexpr int LK = DK + 4, LS = SW + 4;
+    __shared__ float sS[DK][LS], sW[BC][LK], sKb[BC][LK], sU[BC][LS], sG[DK];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / nslab, col0 = (blockIdx.x % nslab) * SW, bb = bh / H, h = bh % H;
+
+    for (int e = tid; e < DK * SW; e += NTH) {
+        const int r = e / SW, j = e % SW;
+        sS[r][j] = S0 ? S0[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int c = 0; c < NC; ++c) {
+        const size_t ch = (size_t)bh * NC + c;
+        for (int e = tid; e < DK * SW; e += NTH) {
+            const int r = e / SW, j = e % SW;
+            ws.h[(ch * DK + r) * DV + col0 + j] = sS[r][j];
+        }
+        for (int e = tid; e < BC * DK; e += NTH) {
+            const int r = e / DK, x = e % DK, t = c * BC + r;
+            const float bl = ws.b[(ch * BC + BC - 1) * DK + x], br = ws.b[ch * BC * DK + e];
+            const float kv = t < T ? to_f32(k[tix(bb, t, h, x, T, H, DK)]) : 0.f;
+            sW[r][x] = ws.W[ch * BC * DK + e];
+            sKb[r][x] = kv * expf(bl - br);
+        }
+        if (tid < DK) sG[tid] = expf(ws.b[(ch * BC + BC - 1) * DK + tid]);
+        __syncthreads();
+        // U = U_v - W S  (U_v is replaced by U in the workspace)
+        wg_gemm(BC, SW, DK, [&](int i, int x) { return sW[i][x]; }, [&](int x, int j) { return sS[x][j]; },
+                [&](int i, int j, float val) {
+                    float *p = ws.U + (ch * BC + i) * DV + col0 + j;
+                    const float u = *p - val;
+                    sU[i][j] = u;
+                    *p = u;
+                });
+        __syncthreads();
+        // S <- Diag(Gamma_C) S + K-bar^T U
+        wg_gemm(DK, SW, BC, [&](int x, int r) { return sKb[r][x]; }, [&](int r, int j) { return sU[r][j]; },
+                [&](int x, int j, float val) { sS[x][j] = sG[x] * sS[x][j] + val; });
+        __syncthreads();
+    }
+}
+
+// --------------------------------------------------------- reverse carry
+
+template <int DK, int DV, typename QT, typename OT>
+__global__ void __launch_bounds__(NTH)
+kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const OT *__restrict__ dO,
+                       const float *__restrict__ dS_T, float *__restrict__ dS0, BwdWorkspace ws,
+                       int T, int H, int NC, int nslab)
+{
+    constexpr int LK = DK + 4, LS = SW + 4, LC = BC + 4;
+    __shared__ float sD[DK][LS], sX1[BC][LK], sX2[BC][LK], sA[BC][LC], sO[BC][LS], sdU[BC][LS], sG[DK];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / nslab, col0 = (blockIdx.x % nslab) * SW, bb = bh / H, h = bh % H;
+
+    for (int e = tid; e < DK * SW; e += NTH) {
+        const int r = e / SW, j = e % SW;
+        sD[r][j] = dS_T ? dS_T[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
+    }
+    __syncthreads();
+    for (int c = NC - 1; c >= 0; --c) {
+        const size_t ch = (size_t)bh * NC + c;
+        for (int e = tid; e < DK * SW; e += NTH) {
+            const int r = e / SW, j = e % SW;
+            ws.dh[(ch * DK + r) * DV + col0 + j] = sD[r][j];
+        }
+        for (int e = tid; e < BC * DK; e += NTH) {
+            const int r = e / DK, x = e % DK, t = c * BC + r;
+            const float bl = ws.b[(ch * BC + BC - 1) * DK + x], br = ws.b[ch * BC * DK + e];
+            const float kv = t < T ? to_f32(k[tix(bb, t, h, x, T, H, DK)]) : 0.f;
+            sX1[r][x] = kv * expf(bl - br);
+        }
+        for (int e = tid; e < BC * BC; e += NTH) sA[e / BC][e % BC] = ws.Aqk[ch * BC * BC + e];
+        for (int e = tid; e < BC * SW; e += NTH) {
+            const int r = e / SW, j = e % SW, t = c * BC + r;
+            sO[r][j] = t < T ? to_f32(dO[tix(bb, t, h, col0 + j, T, H, DV)]) : 0.f;
+        }
+        if (tid < DK) sG[tid] = expf(ws.b[(ch * BC + BC - 1) * DK + tid]);
+        __syncthreads();
+        // dU = K-bar dS' + A_qk^T dO
+        wg_gemm(BC, SW, DK + BC,
+                [&](int i, int x) { return x < DK ? sX1[i][x] : sA[x - DK][i]; },
+                [&](int x, int j) { return x < DK ? sD[x][j] : sO[x - DK][j]; },
+                [&](int i, int j, float val) {
+                    sdU[i][j] = val;
+                    ws.dU[(ch * BC + i) * DV + col0 + j] = val;
+                });
+        __syncthreads();
+        for (int e = tid; e < BC * DK; e += NTH) {
+            const int r = e / DK, x = e % DK, t = c * BC + r;
+            const float qv = t < T ? to_f32(q[tix(bb, t, h, x, T, H, DK)]) : 0.f;
+            sX1[r][x] = qv * expf(ws.b[ch * BC * DK + e]);
+            sX2[r][x] = ws.W[ch * BC * DK + e];
+        }
+        __syncthreads();
+        // dS = Diag(Gamma_C) dS' + (Gamma . Q)^T dO - W^T dU
+        wg_gemm(DK, SW, 2 * BC,
+                [&](int x, int r) { return r < BC ? sX1[r][x] : -sX2[r - BC][x]; },
+                [&](int r, int j) { return r < BC ? sO[r][j] : sdU[r - BC][j]; },
+                [&](int x, int j, float val) { sD[x][j] = sG[x] * sD[x][j] + val; });
+        __syncthreads();
+    }
+    if (dS0)
+        for (int e = tid; e < DK * SW; e += NTH) {
+            const int r = e / SW, j = e % SW;
+            dS0[((size_t)bh * DK + r) * DV + col0 + j] = sD[r][j];
+        }
+}
+
+// ------------------------------------------- products with S and dS'
+
+template <int DK, int DV, typename OT>
+__global__ void __launch_bounds__(NTH)
+kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, int NC)
+{
+    constexpr int LV = DV + 4;
+    __shared__ float sS[DK][LV], sY1[BC][LV], sY2[BC][LV], sGam[DK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
+    const size_t ch = (size_t)bh * NC + c;
+
+    for (int e = tid; e < DK * DV; e += NTH) sS[e / DV][e % DV] = ws.h[ch * DK * DV + e];
+    for (int e = tid; e < BC * DV; e += NTH) {
+        const int r = e / DV, j = e % DV, t = c * BC + r;
+        sY1[r][j] = t < T ? to_f32(dO[tix(bb, t, h, j, T, H, DV)]) : 0.f;
+        sY2[r][j] = ws.dU[ch * BC * DV + e];
+    }
+    if (tid < DK) sGam[tid] = 0.f;
+    __syncthreads();
+    // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1)
+    wg_gemm(2 * BC, DK, DV, [&](int i, int j) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
+            [&](int j, int x) { return sS[x][j]; },
+            [&](int i, int x, float val) {
+                if (i < BC) ws.dQt[(ch * BC + i) * DK + x] = val;
+                else ws.dW[(ch * BC + i - BC) * DK + x] = -val;
+            });
+    __syncthreads();
+    for (int e = tid; e < BC * DV; e += NTH) sY2[e / DV][e % DV] = ws.U[ch * BC * DV + e];
+    // dGamma_C = rowsum(S . dS'), then S is replaced by dS' (each thread its own elements)
+    for (int e = tid; e < DK * DV; e += NTH) {
+        const int r = e / DV, j = e % DV;   // a wave's 64 elements share one row (DV % 64 == 0)
+        const float d = ws.dh[ch * DK * DV + e];
+        const float p = wave_sum(sS[r][j] * d);
+        sS[r][j] = d;
+        if (lane == 0) atomicAdd(&sGam[r], p);
+    }
+    __syncthreads();
+    if (tid < DK) ws.dGam[ch * DK + tid] = sGam[tid];
+    // dA_qk = tril(dO U^T)
+    wg_gemm(BC, BC, DV, [&](int i, int j) { return sY1[i][j]; }, [&](int j, int s) { return sY2[s][j]; },
+            [&](int i, int s, float val) { ws.dAqk[(ch * BC + i) * BC + s] = s <= i ? val : 0.f; });
+    // dK-bar = U dS'^T
+    wg_gemm(BC, DK, DV, [&](int i, int j) { return sY2[i][j]; }, [&](int j, int x) { return sS[x][j]; },
+            [&](int i, int x, float val) { ws.dKb[(ch * BC + i) * DK + x] = val; });
+}
+
+// ------------------------------------------------ intra-chunk gradients
+
+template <int DK, int DV, typename QT, typename GT>
+__global__ void __launch_bounds__(NTH)
+kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
+                     const GT *__restrict__ beta, float *__restrict__ dq, float *__restrict__ dk,
+                     float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta,
+                     BwdWorkspace ws, int T, int H, int NC)
+{
+    constexpr int LK = DK + 4, LM = (DK > DV ? DK : DV) + 4, LC = BC + 4;
+    __shared__ float sq[BC][LK], sk[BC][LK], sb[BC][LK];
+    __shared__ float sP[BC][LM];    // dW, then the dq accumulator
+    __shared__ float sV[BC][LM];    // v, then the dk accumulator
+    __shared__ float sU[BC][LM];    // dU, then the db accumulator
+    __shared__ float sN[BC][LC], sAk[BC][LC], sdA[BC][LC], sT[BC][LC], sX[BC][LC];
+    __shared__ float sbeta[BC], sdb1[BC];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
+    const size_t ch = (size_t)bh * NC + c;
+
+    for (int e = tid; e < BC * DK; e += NTH) {
+        const int r = e / DK, x = e % DK, t = c * BC + r;
+        const bool live = t < T;
+        const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
+        sq[r][x] = live ? to_f32(q[i]) : 0.f;
+        sk[r][x] = live ? to_f32(k[i]) : 0.f;
+        sb[r][x] = ws.b[ch * BC * DK + e];
+        sP[r][x] = ws.dW[ch * BC * DK + e];
+    }
+    for (int e = tid; e < BC * DV; e += NTH) {
+        const int r = e / DV, x = e % DV, t = c * BC + r;
+        sV[r][x] = t < T ? to_f32(v[tix(bb, t, h, x, T, H, DV)]) : 0.f;
+        sU[r][x] = ws.dU[ch * BC * DV + e];
+    }
+    for (int e = tid; e < BC * BC; e += NTH) {
+        const int r = e / BC, s = e % BC;
+        sN[r][s] = ws.N[ch * BC * BC + e];
+        sAk[r][s] = ws.Akk0[ch * BC * BC + e];
+        sdA[r][s] = ws.dAqk[ch * BC * BC + e];
+    }
+    if (tid < BC) {
+        const int t = c * BC + tid;
+        sbeta[tid] = t < T ? to_f32(beta[((size_t)bb * T + t) * H + h]) : 0.f;
+    }
+    __syncthreads();
+    // dT = tril(dW (Gamma . K)^T + dU V^T)
+    wg_gemm(BC, BC, DK + DV,
+            [&](int i, int x) { return x < DK ? sP[i][x] : sU[i][x - DK]; },
+            [&](int x, int s) { return x < DK ? sk[s][x] * expf(sb[s][x]) : sV[s][x - DK]; },
+            [&](int i, int s, float val) { sT[i][s] = s <= i ? val : 0.f; });
+    // dv = Diag(beta) N^T dU
+    wg_gemm(BC, DV, BC, [&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int j) { return sU[s][j]; },
+            [&](int i, int j, float val) {
+                const int t = c * BC + i;
+                if (t < T) dv[tix(bb, t, h, j, T, H, DV)] = val;
+            });
+    __syncthreads();
+    // dK~ = Diag(beta) N^T dW: dk accumulator <- Gamma . dK~, db accumulator <- K~ . dK~
+    wg_gemm(BC, DK, BC, [&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int x) { return sP[s][x]; },
+            [&](int i, int x, float val) {
+                const float e = expf(sb[i][x]);
+                sV[i][x] = e * val;
+                sU[i][x] = e * sk[i][x] * val;
+            });
+    if (tid < BC) {   // dbeta from T = N Diag(beta): sum_i dT[i][r] N[i][r]
+        float s = 0.f;
+        for (int i = 0; i < BC; ++i) s += sT[i][tid] * sN[i][tid];
+        sdb1[tid] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < BC * BC; e += NTH) sT[e / BC][e % BC] *= sbeta[e % BC];   // dN = dT Diag(beta)
+    for (int e = tid; e < BC * DK; e += NTH) {
+        const int r = e / DK, x = e % DK;
+        const float eb = expf(sb[r][x]), ekb = expf(sb[BC - 1][x] - sb[r][x]);
+        const float dqt = ws.dQt[ch * BC * DK + e], dkb = ws.dKb[ch * BC * DK + e];
+        sP[r][x] = eb * dqt;
+        sV[r][x] += ekb * dkb;
+        sU[r][x] += eb * sq[r][x] * dqt - ekb * sk[r][x] * dkb;
+    }
+    __syncthreads();
+    // dA_kk = -strict_tril(N^T dN N^T)
+    wg_gemm(BC, BC, BC, [&](int i, int l) { return sN[l][i]; }, [&](int l, int s) { return sT[l][s]; },
+            [&](int i, int s, float val) { sX[i][s] = val; });
+    __syncthreads();
+    wg_gemm(BC, BC, BC, [&](int i, int l) { return sX[i][l]; }, [&](int l, int s) { return sN[s][l]; },
+            [&](int i, int s, float val) { sT[i][s] = s < i ? -val : 0.f; });
+    __syncthreads();
+    if (tid < BC) {   // dbeta from A_kk = Diag(beta) A_kk0; then dA_kk0 = Diag(beta) dA_kk (row tid)
+        const int r = tid, t = c * BC + r;
+        float s = 0.f;
+        for (int x = 0; x < BC; ++x) s += sT[r][x] * sAk[r][x];
+        if (t < T) dbeta[((size_t)bb * T + t) * H + h] = sdb1[r] + s;
+        for (int x = 0; x < BC; ++x) sT[r][x] *= sbeta[r];
+    }
+    __syncthreads();
+    // Pairwise products differentiated, per row tile m with reference rho_m:
+    //   row role    out[r] += e^{b_r - rho} sum_s D[r,s] (X[s] e^{rho - b_s})
+    //   column role out[s] += e^{rho - b_s} sum_{r in m} D[r,s] (X[r] e^{b_r - rho})
+    // for (D, X) = (dA_qk, k) row / (dA_qk, q) column / (dA_kk0, k) both.
+    for (int m = 0; m < BC / TL; ++m) {
+        auto rho = [&](int x) { return m ? sb[TL * m - 1][x] : 0.f; };
+        // dq += row(dA_qk, k);  db += q . row(dA_qk, k)
+        wg_gemm(TL, DK, TL * (m + 1), [&](int i, int s) { return sdA[TL * m + i][s]; },
+                [&](int s, int x) { return sk[s][x] * expf(rho(x) - sb[s][x]); },
+                [&](int i, int x, float val) {
+                    const int r = TL * m + i;
+                    const float y = expf(sb[r][x] - rho(x)) * val;
+                    sP[r][x] += y;
+                    sU[r][x] += sq[r][x] * y;
+                });
+        __syncthreads();
+        // dk += row(dA_kk0, k);  db += k . row(dA_kk0, k)
+        wg_gemm(TL, DK, TL * (m + 1), [&](int i, int s) { return sT[TL * m + i][s]; },
+                [&](int s, int x) { return sk[s][x] * expf(rho(x) - sb[s][x]); },
+                [&](int i, int x, float val) {
+                    const int r = TL * m + i;
+                    const float y = expf(sb[r][x] - rho(x)) * val;
+                    sV[r][x] += y;
+                    sU[r][x] += sk[r][x] * y;
+                });
+        __syncthreads();
+        // dk += col(dA_qk, q);  db -= k . col(dA_qk, q)
+        wg_gemm(TL * (m + 1), DK, TL, [&](int s, int i) { return sdA[TL * m + i][s]; },
+                [&](int i, int x) { return sq[TL * m + i][x] * expf(sb[TL * m + i][x] - rho(x)); },
+                [&](int s, int x, float val) {
+                    const float y = expf(rho(x) - sb[s][x]) * val;
+                    sV[s][x] += y;
+                    sU[s][x] -= sk[s][x] * y;
+                });
+        __syncthreads();
+        // dk += col(dA_kk0, k);  db -= k . col(dA_kk0, k)
+        wg_gemm(TL * (m + 1), DK, TL, [&](int s, int i) { return sT[TL * m + i][s]; },
+                [&](int i, int x) { return sk[TL * m + i][x] * expf(sb[TL * m + i][x] - rho(x)); },
+                [&](int s, int x, float val) {
+                    const float y = expf(rho(x) - sb[s][x]) * val;
+                    sV[s][x] += y;
+                    sU[s][x] -= sk[s][x] * y;
+                });
+        __syncthreads();
+    }
+    // chunk-end terms of db (K-bar and Gamma_C depend on b at the last token),
+    // then dg = reverse cumsum of db over the chunk
+    if (tid < DK) {
+        const int x = tid;
+        const float bl = sb[BC - 1][x];
+        float tail = expf(bl) * ws.dGam[ch * DK + x];
+        for (int r = 0; r < BC; ++r) tail += expf(bl - sb[r][x]) * sk[r][x] * ws.dKb[(ch * BC + r) * DK + x];
+        float acc = tail;
+        for (int r = BC - 1; r >= 0; --r) {
+            acc += sU[r][x];
+            sU[r][x] = acc;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < BC * DK; e += NTH) {
+        const int r = e / DK, x = e % DK, t = c * BC + r;
+        if (t < T) {
+            const size_t i = tix(bb, t, h, x, T, H, DK);
+            dq[i] = sP[r][x];
+            dk[i] = sV[r][x];
+            dg[i] = sU[r][x];
+        }
+    }
+}
+
+// ------------------------------------------------------------- launch
+
+template <int DK, int DV, typename QT, typename GT, typename OT>
+hipError_t launch_all(const ChunkBwdArgs &a, hipStream_t s)
+{
+    const int BH = a.B * a.H, NC = (a.T + BC - 1) / BC, nslab = DV / SW;
+    const BwdWorkspace &ws = a.ws;
+    if (NC > 0) {
+        kda_bwd_prep_kernel<DK, DV, QT, GT><<<BH * NC, NTH, 0, s>>>(
+            (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta, ws, a.T, a.H, NC);
+        kda_bwd_states_kernel<DK, DV, QT><<<BH * nslab, NTH, 0, s>>>(a.S0, (const QT *)a.k, ws, a.T, a.H, NC, nslab);
+    }
+    kda_bwd_dstates_kernel<DK, DV, QT, OT><<<BH * nslab, NTH, 0, s>>>(
+        (const QT *)a.q, (const QT *)a.k, (const OT *)a.dO, a.dS_final, a.dS0, ws, a.T, a.H, NC, nslab);
+    if (NC > 0) {
+        kda_bwd_sgrads_kernel<DK, DV, OT><<<BH * NC, NTH, 0, s>>>((const OT *)a.dO, ws, a.T, a.H, NC);
+        kda_bwd_intra_kernel<DK, DV, QT, GT><<<BH * NC, NTH, 0, s>>>(
+            (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.beta, a.dq, a.dk, a.dv, a.dg, a.dbeta,
+            ws, a.T, a.H, NC);
+    }
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t dispatch_types(const ChunkBwdArgs &a, hipStream_t s)
+{
+    typedef uint16_t b16;
+    if (a.qkv_bf16) {
+        if (a.gate_bf16) return a.do_bf16 ? launch_all<DK, DV, b16, b16, b16>(a, s) : launch_all<DK, DV, b16, b16, float>(a, s);
+        return a.do_bf16 ? launch_all<DK, DV, b16, float, b16>(a, s) : launch_all<DK, DV, b16, float, float>(a, s);
+    }
+    if (a.gate_bf16) return a.do_bf16 ? launch_all<DK, DV, float, b16, b16>(a, s) : launch_all<DK, DV, float, b16, float>(a, s);
+    return a.do_bf16 ? launch_all<DK, DV, float, float, b16>(a, s) : launch_all<DK, DV, float, float, float>(a, s);
+}
+
+}  // namespace
+
+size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv)
+{
+    const size_t BH = (size_t)B * H, NC = (size_t)(T + BC - 1) / BC;
+    const size_t per = (size_t)BC * dk * 5      // b, W, dQ~, dW, dK-bar
+                       + (size_t)BC * BC * 4    // A_qk, A_kk0, N, dA_qk
+                       + (size_t)BC * dv * 2    // U, dU
+                       + (size_t)dk * dv * 2    // h, dh
+                       + (size_t)dk;            // dGamma_C
+    return BH * NC * per;
+}
+
+BwdWorkspace chunk_bwd_workspace(float *base, int B, int T, int H, int dk, int dv)
+{
+    const size_t n = (size_t)B * H * ((T + BC - 1) / BC);
+    BwdWorkspace w;
+    float *p = base;
+    auto take = [&](size_t count) { float *r = p; p += count; return r; };
+    w.b = take(n * BC * dk);
+    w.W = take(n * BC * dk);
+    w.dQt = take(n * BC * dk);
+    w.dW = take(n * BC * dk);
+    w.dKb = take(n * BC * dk);
+    w.Aqk = take(n * BC * BC);
+    w.Akk0 = take(n * BC * BC);
+    w.N = take(n * BC * BC);
+    w.dAqk = take(n * BC * BC);
+    w.U = take(n * BC * dv);
+    w.dU = take(n * BC * dv);
+    w.h = take(n * dk * dv);
+    w.dh = take(n * dk * dv);
+    w.dGam = take(n * dk);
+    return w;
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    if (a.dk_dim == 64)
+        return a.dv_dim == 64 ? dispatch_types<64, 64>(a, stream) : dispatch_types<64, 128>(a, stream);
+    return a.dv_dim == 64 ? dispatch_types<128, 64>(a, stream) : dispatch_types<128, 128>(a, stream);
+}
+
+}  // namespace kda

@@ -52,10 +52,35 @@ struct OutputGateArgs {
     bool o_bf16, z_bf16, y_bf16;
 };
 
+// Per-chunk intermediates of the backward, float32, one block per
+// (sequence, head, 32-token chunk), head-major.
+struct BwdWorkspace {
+    float *b, *W, *dQt, *dW, *dKb;   // [chunk][32][dk]
+    float *Aqk, *Akk0, *N, *dAqk;    // [chunk][32][32]
+    float *U, *dU;                   // [chunk][32][dv]
+    float *h, *dh;                   // [chunk][dk][dv]: state before / state gradient after the chunk
+    float *dGam;                     // [chunk][dk]
+};
+
+struct ChunkBwdArgs {
+    const void *q, *k, *v, *g, *beta;
+    const float *S0 = nullptr;        // nullable: zero initial state
+    const void *dO;
+    const float *dS_final = nullptr;  // nullable: no gradient on the final state
+    float *dq, *dk, *dv, *dg, *dbeta;
+    float *dS0 = nullptr;             // nullable: not written
+    BwdWorkspace ws;
+    int B, T, H, dk_dim, dv_dim;      // (dk, dv name the gradient outputs here)
+    bool qkv_bf16, gate_bf16, do_bf16;
+};
+
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        // any dtypes
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_spec_step(const SpecArgs &a, hipStream_t stream);           // dk, dv in {64, 128}
 hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
+hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream);       // dk, dv in {64, 128}
+size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv);
+BwdWorkspace chunk_bwd_workspace(float *base, int B, int T, int H, int dk, int dv);
 
 }  // namespace kda

@@ -31,7 +31,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_verify_step", "kda_commit_step",
            "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
-           "kda_status_string", "kda_abi_version")
+           "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_status_string", "kda_abi_version")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -69,6 +69,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_output_gate.restype = i
     lib.kda_decode_step_gated.argtypes = [vp] * 9 + [f, vp] + [i] * 7 + [vp]
     lib.kda_decode_step_gated.restype = i
+    sz = ctypes.c_size_t
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 5
+    lib.kda_chunk_bwd_workspace_bytes.restype = sz
+    lib.kda_chunk_bwd.argtypes = [vp] * 15 + [sz] + [i] * 8 + [vp]
+    lib.kda_chunk_bwd.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -351,3 +356,44 @@ def kda_decode_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
                                    _dtype_code(q), _dtype_code(g), _dtype_code(y), _stream_handle(stream, dev))
     _raise(st, "kda_decode_step_gated")
     return y
+
+
+def kda_chunk_bwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int) -> int:
+    """Bytes of device workspace kda_chunk_bwd needs for these sizes."""
+    return int(load_library().kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv))
+
+
+def kda_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                  S0: Optional[torch.Tensor], dO: torch.Tensor, dS_final: Optional[torch.Tensor] = None, *,
+                  want_dS0: bool = True, workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """Gradients of kda_chunk_fwd(q, k, v, g, beta, S0) for upstream dO
+    [B,T,H,dv] (and dS_final [B,H,dk,dv] float32 or None).  Returns float32
+    (dq, dk, dv, dg, dbeta, dS0) with the inputs' shapes (dS0 None unless
+    want_dS0).  `workspace` (bytes, on the device) is allocated if not given."""
+    lib = load_library()
+    B, T, H, dk, dv = _check_chunk_shapes(q, k, v, g, beta)
+    if dO.shape != (B, T, H, dv):
+        raise ValueError("dO must be [B,T,H,dv]")
+    for name, t in (("S0", S0), ("dS_final", dS_final)):
+        if t is not None and (t.shape != (B, H, dk, dv) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [B,H,dk,dv]")
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk_, dg = (torch.empty((B, T, H, dk), **f32) for _ in range(3))
+    dv_ = torch.empty((B, T, H, dv), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    dS0 = torch.empty((B, H, dk, dv), **f32) if want_dS0 else None
+    need = int(lib.kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    dev = _check_dev(q, k, v, g, beta, S0, dO, dS_final, workspace)
+    st = lib.kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(dO), _ptr(dS_final),
+                           _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dbeta), _ptr(dS0),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           B, T, H, dk, dv, _dtype_code(q), _dtype_code(g), _dtype_code(dO),
+                           _stream_handle(stream, dev))
+    _raise(st, "kda_chunk_bwd")
+    return dq, dk_, dv_, dg, dbeta, dS0

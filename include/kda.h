@@ -68,6 +68,7 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -87,7 +88,7 @@ typedef enum {
 } kda_status_t;
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /*
  * kda_chunk_fwd -- chunkwise forward over T tokens for B sequences x H heads.
@@ -249,6 +250,37 @@ kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v, 
                                    const float *weight, float eps, void *y, int B, int H, int dk, int dv,
                                    kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
                                    void *stream);
+
+/*
+ * kda_chunk_bwd -- gradients of kda_chunk_fwd.  Given the upstream gradients
+ * dO of the outputs (and dS_final of the final state), computes the
+ * gradients of L = sum(o * dO) + sum(S_final * dS_final) with respect to
+ * q, k, v, g, beta and S0.  The pages describe training the layer but give
+ * no gradients; these are the derivatives of the recurrence above, taken
+ * through the chunkwise form (32-token chunks, tile-local 1/Gamma references
+ * as in the forward, float32 arithmetic throughout).
+ *
+ *   q, k, v, g, beta, S0   as kda_chunk_fwd (S0 NULL = zero state)
+ *   dO        [B, T, H, dv]  do_dtype
+ *   dS_final  [B, H, dk, dv] float32, or NULL (= zero)
+ *   dq, dk, dg [B, T, H, dk], dv [B, T, H, dv], dbeta [B, T, H]: float32 outputs
+ *   dS0       [B, H, dk, dv] float32 output, or NULL (not written)
+ *   workspace device memory of at least kda_chunk_bwd_workspace_bytes(B, T,
+ *             H, dk, dv) bytes, owned by the caller, contents undefined
+ *             before and after; it must not overlap any argument
+ *
+ * dk, dv in {64, 128} (else KDA_ERR_UNSUPPORTED).  No output may overlap an
+ * input, another output or the workspace.  Preconditions as the forward.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
+
+kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                           const float *S0, const void *dO, const float *dS_final,
+                           float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dS0,
+                           void *workspace, size_t workspace_bytes,
+                           int B, int T, int H, int dk_dim, int dv_dim,
+                           kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t do_dtype,
+                           void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_string(kda_status_t status);

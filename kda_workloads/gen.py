@@ -211,6 +211,20 @@ def read_rows(rows: int, dv: int, dtype: str, seed: int = 0) -> HostTensor:
     return _to_dtype(x, dtype)
 
 
+_GRAD_OUT_STREAM = 11
+_GRAD_STATE_STREAM = 12
+
+
+def grad_outputs(w: Workload, seed: int = 0, dtype: Optional[str] = None):
+    """Upstream gradients for a forward workload: dO [B, T, H, dv] ~ N(0, 1)
+    (rounded to `dtype`, default the q/k/v dtype) and dS_T [B, H, dk, dv] ~
+    N(0, 1) float32."""
+    assert w.kind == "fwd"
+    dO = _to_dtype(_normal_f32(_rng(seed, _GRAD_OUT_STREAM), (w.B, w.T, w.H, w.dv)), dtype or w.qkv)
+    dS = _to_dtype(_normal_f32(_rng(seed, _GRAD_STATE_STREAM), (w.B, w.H, w.dk, w.dv)), "f32")
+    return dO, dS
+
+
 def decode_initial_state(w: Workload, seed: int = 0) -> HostTensor:
     """S before the first decode step: [B, H, dk, dv] fp32, N(0, s0_sd) (zero if s0_sd is None)."""
     assert w.kind == "decode"

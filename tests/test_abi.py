@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     from gated_delta_rule_101_amd import kda
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for st in (kda.KDA_OK, kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_LAUNCH):
         assert lib.kda_status_string(st).decode().startswith("KDA_")
     assert lib.kda_status_string(77).decode() == "KDA_ERR_UNKNOWN"
@@ -197,3 +197,36 @@ def test_output_epilogue_validation(lib):
     assert dec(y=zo + 128) == INV                # y over the logits
     assert dec(y=wt) == INV                      # y over the weight
     assert dec(B=0) == OK
+
+
+def test_backward_validation(lib):
+    from gated_delta_rule_101_amd import kda
+    INV, UNS, OK = kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_OK
+    big = 1 << 28
+    B, T, H, d = 1, 64, 2, 64
+    need = lib.kda_chunk_bwd_workspace_bytes(B, T, H, d, d)
+    assert need > 0 and need % 4 == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(B, 0, H, d, d) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(B, T, H, 96, d) == 0
+    names = ("q", "k", "v", "g", "beta", "S0", "dO", "dS", "dq", "dk", "dv", "dg", "dbeta", "dS0", "ws")
+    base = {n: (i + 1) * big for i, n in enumerate(names)}
+    base["S0"] = base["dS"] = None
+
+    def call(size=need, B=B, T=T, kdim=d, vdim=d, qd=1, **kw):
+        p = {**base, **kw}
+        return lib.kda_chunk_bwd(*(p[n] for n in names[:-1]), p["ws"], size, B, T, H, kdim, vdim, qd, 0, 0, None)
+
+    assert call(q=None) == INV
+    assert call(dq=None) == INV
+    assert call(ws=None) == INV
+    assert call(size=need - 4) == INV                    # workspace too small
+    assert call(dk=base["q"] + 64) == INV                # a gradient over an input
+    assert call(dg=base["dq"] + 256) == INV              # two gradients overlap
+    assert call(ws=base["dv"] + 1024) == INV             # workspace over a gradient
+    assert call(dS0=base["dO"]) == INV
+    assert call(T=-1) == INV
+    assert call(qd=4) == INV
+    assert call(kdim=96) == UNS
+    assert call(vdim=256) == UNS
+    assert call(B=0) == OK
+    assert call(T=0, dS0=None) == OK                     # nothing to write

@@ -41,3 +41,11 @@ def test_epilogue_counts():
     # fused decode: the decode step plus bf16 output-gate logits and the weight
     assert bench.gated_decode_bytes(256, 96, 128, 128, 2, 4, 4) == \
         bench.decode_bytes(256, 96, 128, 128, 2, 4, 4) + 256 * 96 * 128 * 2 + 4 * 128
+
+
+def test_backward_counts():
+    # per token-head at C = 64, d = 128: 16 d^2 + 9 C d + 5 C d + C^2
+    assert bench.bwd_flops(1, 1, 1, 128, 128) == 16 * 16384 + 14 * 64 * 128 + 4096 == 380928
+    # bf16 q, k, v, g, beta and fp32 dO read; fp32 dq, dk, dg (d each), dv (d), dbeta written
+    per = 2 * 384 + 2 * 129 + 4 * 128 + 4 * (3 * 128 + 128 + 1)
+    assert bench.bwd_bytes(4, 16384, 32, 128, 128, 2, 2, 4) == 4 * 16384 * 32 * per

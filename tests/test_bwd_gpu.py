@@ -1,0 +1,114 @@
+"""GPU parity of the chunkwise backward (kda_chunk_bwd) against the float64
+autograd oracle of the token recurrence (oracle/kda_oracle_bwd.py).
+
+The gradients are of L = sum(o * dO) + sum(S_T * dS_T).  The kernels compute
+in float32 from the exact stored inputs (which the oracle also receives), so
+the bound is the float32 one for every input dtype: max |gpu - oracle| <=
+tau * RMS(oracle) per gradient, tau = 1e-4 (dbeta and dg, sums with
+cancellation over the whole chunk, 1e-3).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import f64, say, to_dev
+from kda_workloads import configs, gen
+
+pytestmark = pytest.mark.gpu
+
+TAU = {"dq": 1e-4, "dk": 1e-4, "dv": 1e-4, "dg": 1e-3, "dbeta": 1e-3, "dS0": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_101_amd as m
+    m.load_library()
+    return m
+
+
+def _err(got, ref):
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(got - ref))) / rms if rms > 0 else float(np.max(np.abs(got)))
+
+
+CASES = [
+    configs.TINY_F32.scaled(name="bwd_f32_T256_d64"),
+    configs.HEADGROUP_BF16.scaled(B=1, H=2, T=150, name="bwd_bf16_T150_d128"),
+    configs.TRAIN_BF16.scaled(B=2, H=1, T=97, dk=64, dv=128, name="bwd_bf16gates_T97_dk64_dv128"),
+    configs.TINY_F32.scaled(B=1, H=3, T=33, dk=128, dv=64, s0_sd=0.3, name="bwd_f32_T33_dk128_dv64"),
+    configs.TINY_F32.scaled(B=2, H=2, T=1, s0_sd=0.3, name="bwd_f32_T1"),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+@pytest.mark.parametrize("with_dS", [True, False], ids=["dS_T", "no_dS_T"])
+def test_backward_matches_autograd(kda, w, with_dS):
+    from oracle.kda_oracle_bwd import kda_bwd
+    x = gen.fwd_inputs(w, 2)
+    dO, dS = gen.grad_outputs(w, 2)
+    d = {n: to_dev(x[n]) for n in ("q", "k", "v", "g", "beta", "S0")}
+    say(f"[bwd] {w.name} B={w.B} T={w.T} H={w.H} dk={w.dk} dv={w.dv} qkv={w.qkv} gate={w.gate} dS_T={with_dS}")
+    out = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], to_dev(dO),
+                            to_dev(dS) if with_dS else None)
+    torch.cuda.synchronize()
+    ref = kda_bwd(*[x[n].f64() for n in ("q", "k", "v", "g", "beta")],
+                  None if x["S0"] is None else x["S0"].f64(), dO.f64(), dS.f64() if with_dS else None)
+    errs = {}
+    for n, t in zip(("dq", "dk", "dv", "dg", "dbeta", "dS0"), out):
+        errs[n] = _err(f64(t), ref[n])
+    say("      " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TAU[n], (n, e)
+
+
+def test_empty_sequence_passes_the_state_gradient_through(kda):
+    B, H, d = 2, 3, 64
+    z = lambda *s: torch.zeros(s, dtype=torch.float32, device="cuda")  # noqa: E731
+    dS = torch.randn((B, H, d, d), device="cuda")
+    out = kda.kda_chunk_bwd(z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H), None,
+                            z(B, 0, H, d), dS)
+    torch.cuda.synchronize()
+    assert torch.equal(out[5], dS)
+    out = kda.kda_chunk_bwd(z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H, d), z(B, 0, H), None,
+                            z(B, 0, H, d), None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[5]).item() == 0
+
+
+def test_backward_is_deterministic(kda):
+    w = configs.HEADGROUP_BF16.scaled(B=1, H=2, T=200, name="bwd_det")
+    x = gen.fwd_inputs(w, 4)
+    dO, dS = gen.grad_outputs(w, 4)
+    d = {n: to_dev(x[n]) for n in ("q", "k", "v", "g", "beta", "S0")}
+    a = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], to_dev(dO), to_dev(dS))
+    b = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], to_dev(dO), to_dev(dS))
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_backward_head_group_shape_sampled_head(kda):
+    """B1 H8 T4096 d128 (bf16 q/k/v, fp32 gates): all heads on the GPU, one
+    head against the oracle over the whole sequence."""
+    from oracle.kda_oracle_bwd import kda_bwd
+    w = configs.HEADGROUP_BF16
+    x = gen.fwd_inputs(w, 0)
+    dO, dS = gen.grad_outputs(w, 0)
+    d = {n: to_dev(x[n]) for n in ("q", "k", "v", "g", "beta", "S0")}
+    say(f"[bwd head group] {w.name}: kernels")
+    out = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], to_dev(dO), to_dev(dS))
+    torch.cuda.synchronize()
+    h = 5
+    say(f"[bwd head group] oracle on head {h}")
+    sl = lambda a: a[:, :, h:h + 1]  # noqa: E731
+    ref = kda_bwd(*[sl(x[n].f64()) for n in ("q", "k", "v", "g")], x["beta"].f64()[:, :, h:h + 1],
+                  x["S0"].f64()[:, h:h + 1], sl(dO.f64()), dS.f64()[:, h:h + 1])
+    got = {"dq": sl(f64(out[0])), "dk": sl(f64(out[1])), "dv": sl(f64(out[2])), "dg": sl(f64(out[3])),
+           "dbeta": f64(out[4])[:, :, h:h + 1], "dS0": f64(out[5])[:, h:h + 1]}
+    errs = {n: _err(got[n], ref[n]) for n in got}
+    say("      " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TAU[n], (n, e)
