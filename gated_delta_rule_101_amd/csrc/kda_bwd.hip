@@ -27,7 +27,10 @@
 //   sgrads   (per chunk)         dQ~, dW, dK-bar, dA_qk, dGamma_C -> workspace
 //   intra    (per chunk)         dq, dk, dv, dg, dbeta
 // Value columns of S (and of dS) evolve independently, so the two carries
-// split dv into 64-column slabs like the forward.
+// split dv into 32-column slabs (more workgroups in flight for the two
+// sequential passes, which are latency-bound).
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -38,34 +41,38 @@ constexpr int BC = 32;        // tokens per chunk in the backward
 constexpr int TL = 16;        // tokens per tile (reference granularity)
 constexpr int NTH = 256;
 constexpr int NW = NTH / 64;
-constexpr int SW = 64;        // value columns per slab in the carries
+constexpr int SW = 32;        // value columns per slab in the carries
 
 // Cooperative GEMM over the workgroup: out(i, j) = sum_kk A(i, kk) B(kk, j),
-// i < M, j < N (multiples of 16), kk < K (multiple of 4).  Each 16 x 16 tile
-// goes to one wave; lane (r16, kq) feeds A(i0 + r16, kk + kq) and
-// B(kk + kq, j0 + r16) and receives rows i0 + 4 kq + 0..3 of column j0 + r16.
-// epi(i, j, value) is called once per result.
-template <typename FA, typename FB, typename FE>
-__device__ __forceinline__ void wg_gemm(int M, int N, int K, FA A, FB B, FE epi)
+// i < M, j < N (multiples of 16), kk < K (multiple of 4), all compile-time so
+// the k loop unrolls and the operand reads run ahead of the matrix-core ops.
+// 16 x 16 tiles are dealt to the waves round-robin, two at a time (two
+// independent accumulation chains); lane (r16, kq) feeds A(i0 + r16, kk + kq)
+// and B(kk + kq, j0 + r16) and receives rows i0 + 4 kq + 0..3 of column
+// j0 + r16.  epi(i, j, value) is called once per result.
+template <int M, int N, int K, typename FA, typename FB, typename FE>
+__device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
 {
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
+    constexpr int TN = N / 16, NT = (M / 16) * TN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
-    const int tn = N >> 4, nt = (M >> 4) * tn;
-    for (int t = wave; t < nt; t += NW) {
-        const int i0 = (t / tn) << 4, j0 = (t % tn) << 4;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kk = 0; kk < K; kk += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + kq), B(kk + kq, j0 + r16), acc, 0, 0, 0);
+    for (int t = wave; t < NT; t += 2 * NW) {
+        const int u = t + NW < NT ? t + NW : t;   // second tile (or t again when none is left)
+        const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
+        const int i1 = (u / TN) * 16, j1 = (u % TN) * 16;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) epi(i0 + 4 * kq + r, j0 + r16, acc[r]);
+        for (int kk = 0; kk < K; kk += 4) {
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + kq), B(kk + kq, j0 + r16), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i1 + r16, kk + kq), B(kk + kq, j1 + r16), acc1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) epi(i0 + 4 * kq + r, j0 + r16, acc0[r]);
+        if (u != t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) epi(i1 + 4 * kq + r, j1 + r16, acc1[r]);
     }
-}
-
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-    return x;
 }
 
 // element (b, t, h, c) of a [B, T, H, d] tensor
@@ -122,10 +129,11 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
 
     // Gram matrices, one row tile at a time: rows scaled by e^{b - rho},
     // keys by e^{rho - b}, rho = b at the end of the previous tile.
-    for (int m = 0; m < BC / TL; ++m) {
-        auto rho = [&](int x) { return m ? sb[TL * m - 1][x] : 0.f; };
-        wg_gemm(2 * TL, TL * (m + 1), DK,
-                [&](int i, int x) {
+    static_assert(BC == 2 * TL, "two row tiles per chunk");
+    auto gram_rows = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        auto rho = [&](int x) { if constexpr (m == 0) return 0.f; else return sb[TL * m - 1][x]; };
+        wg_gemm<2 * TL, TL * (m + 1), DK>([&](int i, int x) {
                     const int r = TL * m + (i & (TL - 1));
                     const float f = expf(sb[r][x] - rho(x));
                     return (i < TL ? sq[r][x] : sk[r][x]) * f;
@@ -136,7 +144,9 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
                     if (i < TL) sA[r][s] = s <= r ? val : 0.f;
                     else sL[r][s] = s < r ? val : 0.f;
                 });
-    }
+    };
+    gram_rows(std::integral_constant<int, 0>{});
+    gram_rows(std::integral_constant<int, 1>{});
     __syncthreads();
     if (tid < BC) {   // column tid of N = (I + Diag(beta) A_kk0)^-1 by forward substitution
         const int j = tid;
@@ -159,10 +169,10 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
         ws.N[ch * BC * BC + e] = sN[r][s];
     }
     // W = N Diag(beta) (Gamma . K),  U_v = N Diag(beta) V
-    wg_gemm(BC, DK, BC, [&](int i, int s) { return sN[i][s]; },
+    wg_gemm<BC, DK, BC>([&](int i, int s) { return sN[i][s]; },
             [&](int s, int x) { return sbeta[s] * expf(sb[s][x]) * sk[s][x]; },
             [&](int i, int x, float val) { ws.W[(ch * BC + i) * DK + x] = val; });
-    wg_gemm(BC, DV, BC, [&](int i, int s) { return sN[i][s]; },
+    wg_gemm<BC, DV, BC>([&](int i, int s) { return sN[i][s]; },
             [&](int s, int x) { return sbeta[s] * sv[s][x]; },
             [&](int i, int x, float val) { ws.U[(ch * BC + i) * DV + x] = val; });
 }
@@ -175,42 +185,66 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
                       int T, int H, int NC, int nslab)
 {
     constexpr int LK = DK + 4, LS = SW + 4;
+    constexpr int PE = BC * DK / NTH, PU = BC * SW / NTH;   // per-thread elements of a chunk block
     __shared__ float sS[DK][LS], sW[BC][LK], sKb[BC][LK], sU[BC][LS], sG[DK];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / nslab, col0 = (blockIdx.x % nslab) * SW, bb = bh / H, h = bh % H;
+
+    // the next chunk's inputs, loaded one chunk ahead into registers
+    float pw[PE], pk[PE], pb[PE], pbl[PE], pu[PU];
+    auto fetch = [&](int c) {
+        const size_t ch = (size_t)bh * NC + c;
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            const int e = tid + NTH * i, r = e / DK, x = e % DK, t = c * BC + r;
+            pw[i] = ws.W[ch * BC * DK + e];
+            pb[i] = ws.b[ch * BC * DK + e];
+            pbl[i] = ws.b[(ch * BC + BC - 1) * DK + x];
+            pk[i] = t < T ? to_f32(k[tix(bb, t, h, x, T, H, DK)]) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PU; ++i) {
+            const int e = tid + NTH * i, r = e / SW, j = e % SW;
+            pu[i] = ws.U[(ch * BC + r) * DV + col0 + j];
+        }
+    };
 
     for (int e = tid; e < DK * SW; e += NTH) {
         const int r = e / SW, j = e % SW;
         sS[r][j] = S0 ? S0[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
     }
-    __syncthreads();
+    if (NC > 0) fetch(0);
     for (int c = 0; c < NC; ++c) {
         const size_t ch = (size_t)bh * NC + c;
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            const int e = tid + NTH * i, r = e / DK, x = e % DK;
+            sW[r][x] = pw[i];
+            sKb[r][x] = pk[i] * expf(pbl[i] - pb[i]);
+            if (i == 0 && tid < DK) sG[x] = expf(pbl[i]);   // element 0 of threads < DK is channel tid
+        }
+#pragma unroll
+        for (int i = 0; i < PU; ++i) {
+            const int e = tid + NTH * i;
+            sU[e / SW][e % SW] = pu[i];
+        }
+        __syncthreads();
+        if (c + 1 < NC) fetch(c + 1);
         for (int e = tid; e < DK * SW; e += NTH) {
             const int r = e / SW, j = e % SW;
             ws.h[(ch * DK + r) * DV + col0 + j] = sS[r][j];
         }
-        for (int e = tid; e < BC * DK; e += NTH) {
-            const int r = e / DK, x = e % DK, t = c * BC + r;
-            const float bl = ws.b[(ch * BC + BC - 1) * DK + x], br = ws.b[ch * BC * DK + e];
-            const float kv = t < T ? to_f32(k[tix(bb, t, h, x, T, H, DK)]) : 0.f;
-            sW[r][x] = ws.W[ch * BC * DK + e];
-            sKb[r][x] = kv * expf(bl - br);
-        }
-        if (tid < DK) sG[tid] = expf(ws.b[(ch * BC + BC - 1) * DK + tid]);
-        __syncthreads();
         // U = U_v - W S  (U_v is replaced by U in the workspace)
-        wg_gemm(BC, SW, DK, [&](int i, int x) { return sW[i][x]; }, [&](int x, int j) { return sS[x][j]; },
-                [&](int i, int j, float val) {
-                    float *p = ws.U + (ch * BC + i) * DV + col0 + j;
-                    const float u = *p - val;
-                    sU[i][j] = u;
-                    *p = u;
-                });
+        wg_gemm<BC, SW, DK>([&](int i, int x) { return sW[i][x]; }, [&](int x, int j) { return sS[x][j]; },
+                            [&](int i, int j, float val) {
+                                const float u = sU[i][j] - val;
+                                sU[i][j] = u;
+                                ws.U[(ch * BC + i) * DV + col0 + j] = u;
+                            });
         __syncthreads();
         // S <- Diag(Gamma_C) S + K-bar^T U
-        wg_gemm(DK, SW, BC, [&](int x, int r) { return sKb[r][x]; }, [&](int r, int j) { return sU[r][j]; },
-                [&](int x, int j, float val) { sS[x][j] = sG[x] * sS[x][j] + val; });
+        wg_gemm<DK, SW, BC>([&](int x, int r) { return sKb[r][x]; }, [&](int r, int j) { return sU[r][j]; },
+                            [&](int x, int j, float val) { sS[x][j] = sG[x] * sS[x][j] + val; });
         __syncthreads();
     }
 }
@@ -224,55 +258,83 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
                        int T, int H, int NC, int nslab)
 {
     constexpr int LK = DK + 4, LS = SW + 4, LC = BC + 4;
+    constexpr int PE = BC * DK / NTH, PO = BC * SW / NTH, PA = BC * BC / NTH;
     __shared__ float sD[DK][LS], sX1[BC][LK], sX2[BC][LK], sA[BC][LC], sO[BC][LS], sdU[BC][LS], sG[DK];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / nslab, col0 = (blockIdx.x % nslab) * SW, bb = bh / H, h = bh % H;
+
+    // the previous chunk's inputs (the pass runs backwards), one chunk ahead
+    float pk[PE], pq[PE], pb[PE], pbl[PE], pw[PE], po[PO], pa[PA];
+    auto fetch = [&](int c) {
+        const size_t ch = (size_t)bh * NC + c;
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            const int e = tid + NTH * i, r = e / DK, x = e % DK, t = c * BC + r;
+            const bool live = t < T;
+            const size_t ti = tix(bb, live ? t : 0, h, x, T, H, DK);
+            pk[i] = live ? to_f32(k[ti]) : 0.f;
+            pq[i] = live ? to_f32(q[ti]) : 0.f;
+            pb[i] = ws.b[ch * BC * DK + e];
+            pbl[i] = ws.b[(ch * BC + BC - 1) * DK + x];
+            pw[i] = ws.W[ch * BC * DK + e];
+        }
+#pragma unroll
+        for (int i = 0; i < PO; ++i) {
+            const int e = tid + NTH * i, r = e / SW, j = e % SW, t = c * BC + r;
+            po[i] = t < T ? to_f32(dO[tix(bb, t, h, col0 + j, T, H, DV)]) : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < PA; ++i) pa[i] = ws.Aqk[ch * BC * BC + tid + NTH * i];
+    };
 
     for (int e = tid; e < DK * SW; e += NTH) {
         const int r = e / SW, j = e % SW;
         sD[r][j] = dS_T ? dS_T[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
     }
-    __syncthreads();
+    if (NC > 0) fetch(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const size_t ch = (size_t)bh * NC + c;
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            const int e = tid + NTH * i, r = e / DK, x = e % DK;
+            sX1[r][x] = pk[i] * expf(pbl[i] - pb[i]);       // K-bar
+            sX2[r][x] = pw[i];
+            if (i == 0 && tid < DK) sG[x] = expf(pbl[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < PO; ++i) {
+            const int e = tid + NTH * i;
+            sO[e / SW][e % SW] = po[i];
+        }
+#pragma unroll
+        for (int i = 0; i < PA; ++i) {
+            const int e = tid + NTH * i;
+            sA[e / BC][e % BC] = pa[i];
+        }
+        __syncthreads();
         for (int e = tid; e < DK * SW; e += NTH) {
             const int r = e / SW, j = e % SW;
             ws.dh[(ch * DK + r) * DV + col0 + j] = sD[r][j];
         }
-        for (int e = tid; e < BC * DK; e += NTH) {
-            const int r = e / DK, x = e % DK, t = c * BC + r;
-            const float bl = ws.b[(ch * BC + BC - 1) * DK + x], br = ws.b[ch * BC * DK + e];
-            const float kv = t < T ? to_f32(k[tix(bb, t, h, x, T, H, DK)]) : 0.f;
-            sX1[r][x] = kv * expf(bl - br);
-        }
-        for (int e = tid; e < BC * BC; e += NTH) sA[e / BC][e % BC] = ws.Aqk[ch * BC * BC + e];
-        for (int e = tid; e < BC * SW; e += NTH) {
-            const int r = e / SW, j = e % SW, t = c * BC + r;
-            sO[r][j] = t < T ? to_f32(dO[tix(bb, t, h, col0 + j, T, H, DV)]) : 0.f;
-        }
-        if (tid < DK) sG[tid] = expf(ws.b[(ch * BC + BC - 1) * DK + tid]);
-        __syncthreads();
         // dU = K-bar dS' + A_qk^T dO
-        wg_gemm(BC, SW, DK + BC,
-                [&](int i, int x) { return x < DK ? sX1[i][x] : sA[x - DK][i]; },
-                [&](int x, int j) { return x < DK ? sD[x][j] : sO[x - DK][j]; },
-                [&](int i, int j, float val) {
-                    sdU[i][j] = val;
-                    ws.dU[(ch * BC + i) * DV + col0 + j] = val;
-                });
+        wg_gemm<BC, SW, DK + BC>([&](int i, int x) { return x < DK ? sX1[i][x] : sA[x - DK][i]; },
+                                 [&](int x, int j) { return x < DK ? sD[x][j] : sO[x - DK][j]; },
+                                 [&](int i, int j, float val) {
+                                     sdU[i][j] = val;
+                                     ws.dU[(ch * BC + i) * DV + col0 + j] = val;
+                                 });
         __syncthreads();
-        for (int e = tid; e < BC * DK; e += NTH) {
-            const int r = e / DK, x = e % DK, t = c * BC + r;
-            const float qv = t < T ? to_f32(q[tix(bb, t, h, x, T, H, DK)]) : 0.f;
-            sX1[r][x] = qv * expf(ws.b[ch * BC * DK + e]);
-            sX2[r][x] = ws.W[ch * BC * DK + e];
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {   // Gamma . Q replaces K-bar
+            const int e = tid + NTH * i;
+            sX1[e / DK][e % DK] = pq[i] * expf(pb[i]);
         }
         __syncthreads();
+        if (c > 0) fetch(c - 1);
         // dS = Diag(Gamma_C) dS' + (Gamma . Q)^T dO - W^T dU
-        wg_gemm(DK, SW, 2 * BC,
-                [&](int x, int r) { return r < BC ? sX1[r][x] : -sX2[r - BC][x]; },
-                [&](int r, int j) { return r < BC ? sO[r][j] : sdU[r - BC][j]; },
-                [&](int x, int j, float val) { sD[x][j] = sG[x] * sD[x][j] + val; });
+        wg_gemm<DK, SW, 2 * BC>([&](int x, int r) { return r < BC ? sX1[r][x] : -sX2[r - BC][x]; },
+                                [&](int r, int j) { return r < BC ? sO[r][j] : sdU[r - BC][j]; },
+                                [&](int x, int j, float val) { sD[x][j] = sG[x] * sD[x][j] + val; });
         __syncthreads();
     }
     if (dS0)
@@ -290,7 +352,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
 {
     constexpr int LV = DV + 4;
     __shared__ float sS[DK][LV], sY1[BC][LV], sY2[BC][LV], sGam[DK];
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
@@ -300,10 +362,9 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         sY1[r][j] = t < T ? to_f32(dO[tix(bb, t, h, j, T, H, DV)]) : 0.f;
         sY2[r][j] = ws.dU[ch * BC * DV + e];
     }
-    if (tid < DK) sGam[tid] = 0.f;
     __syncthreads();
     // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1)
-    wg_gemm(2 * BC, DK, DV, [&](int i, int j) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
+    wg_gemm<2 * BC, DK, DV>([&](int i, int j) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
             [&](int j, int x) { return sS[x][j]; },
             [&](int i, int x, float val) {
                 if (i < BC) ws.dQt[(ch * BC + i) * DK + x] = val;
@@ -311,21 +372,31 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
             });
     __syncthreads();
     for (int e = tid; e < BC * DV; e += NTH) sY2[e / DV][e % DV] = ws.U[ch * BC * DV + e];
-    // dGamma_C = rowsum(S . dS'), then S is replaced by dS' (each thread its own elements)
-    for (int e = tid; e < DK * DV; e += NTH) {
-        const int r = e / DV, j = e % DV;   // a wave's 64 elements share one row (DV % 64 == 0)
-        const float d = ws.dh[ch * DK * DV + e];
-        const float p = wave_sum(sS[r][j] * d);
-        sS[r][j] = d;
-        if (lane == 0) atomicAdd(&sGam[r], p);
+    // dGamma_C = rowsum(S . dS'): TPR threads per row, each over a contiguous
+    // run of columns; S is replaced by dS' element by element as it goes.
+    {
+        constexpr int TPR = NTH / DK, CPT = DV / TPR;
+        const int r = tid / TPR, j0 = (tid % TPR) * CPT;
+        const float4 *src = reinterpret_cast<const float4 *>(ws.dh + ch * DK * DV + (size_t)r * DV + j0);
+        float p = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPT / 4; ++j) {
+            const float4 d = src[j];
+            float *sp = &sS[r][j0 + 4 * j];
+            p += sp[0] * d.x + sp[1] * d.y + sp[2] * d.z + sp[3] * d.w;
+            sp[0] = d.x; sp[1] = d.y; sp[2] = d.z; sp[3] = d.w;
+        }
+#pragma unroll
+        for (int m = 1; m < TPR; m <<= 1) p += __shfl_xor(p, m, TPR);
+        if (tid % TPR == 0) sGam[r] = p;
     }
     __syncthreads();
     if (tid < DK) ws.dGam[ch * DK + tid] = sGam[tid];
     // dA_qk = tril(dO U^T)
-    wg_gemm(BC, BC, DV, [&](int i, int j) { return sY1[i][j]; }, [&](int j, int s) { return sY2[s][j]; },
+    wg_gemm<BC, BC, DV>([&](int i, int j) { return sY1[i][j]; }, [&](int j, int s) { return sY2[s][j]; },
             [&](int i, int s, float val) { ws.dAqk[(ch * BC + i) * BC + s] = s <= i ? val : 0.f; });
     // dK-bar = U dS'^T
-    wg_gemm(BC, DK, DV, [&](int i, int j) { return sY2[i][j]; }, [&](int j, int x) { return sS[x][j]; },
+    wg_gemm<BC, DK, DV>([&](int i, int j) { return sY2[i][j]; }, [&](int j, int x) { return sS[x][j]; },
             [&](int i, int x, float val) { ws.dKb[(ch * BC + i) * DK + x] = val; });
 }
 
@@ -375,19 +446,18 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     }
     __syncthreads();
     // dT = tril(dW (Gamma . K)^T + dU V^T)
-    wg_gemm(BC, BC, DK + DV,
-            [&](int i, int x) { return x < DK ? sP[i][x] : sU[i][x - DK]; },
+    wg_gemm<BC, BC, DK + DV>([&](int i, int x) { return x < DK ? sP[i][x] : sU[i][x - DK]; },
             [&](int x, int s) { return x < DK ? sk[s][x] * expf(sb[s][x]) : sV[s][x - DK]; },
             [&](int i, int s, float val) { sT[i][s] = s <= i ? val : 0.f; });
     // dv = Diag(beta) N^T dU
-    wg_gemm(BC, DV, BC, [&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int j) { return sU[s][j]; },
+    wg_gemm<BC, DV, BC>([&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int j) { return sU[s][j]; },
             [&](int i, int j, float val) {
                 const int t = c * BC + i;
                 if (t < T) dv[tix(bb, t, h, j, T, H, DV)] = val;
             });
     __syncthreads();
     // dK~ = Diag(beta) N^T dW: dk accumulator <- Gamma . dK~, db accumulator <- K~ . dK~
-    wg_gemm(BC, DK, BC, [&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int x) { return sP[s][x]; },
+    wg_gemm<BC, DK, BC>([&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int x) { return sP[s][x]; },
             [&](int i, int x, float val) {
                 const float e = expf(sb[i][x]);
                 sV[i][x] = e * val;
@@ -410,10 +480,10 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     }
     __syncthreads();
     // dA_kk = -strict_tril(N^T dN N^T)
-    wg_gemm(BC, BC, BC, [&](int i, int l) { return sN[l][i]; }, [&](int l, int s) { return sT[l][s]; },
+    wg_gemm<BC, BC, BC>([&](int i, int l) { return sN[l][i]; }, [&](int l, int s) { return sT[l][s]; },
             [&](int i, int s, float val) { sX[i][s] = val; });
     __syncthreads();
-    wg_gemm(BC, BC, BC, [&](int i, int l) { return sX[i][l]; }, [&](int l, int s) { return sN[s][l]; },
+    wg_gemm<BC, BC, BC>([&](int i, int l) { return sX[i][l]; }, [&](int l, int s) { return sN[s][l]; },
             [&](int i, int s, float val) { sT[i][s] = s < i ? -val : 0.f; });
     __syncthreads();
     if (tid < BC) {   // dbeta from A_kk = Diag(beta) A_kk0; then dA_kk0 = Diag(beta) dA_kk (row tid)
@@ -428,10 +498,11 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     //   row role    out[r] += e^{b_r - rho} sum_s D[r,s] (X[s] e^{rho - b_s})
     //   column role out[s] += e^{rho - b_s} sum_{r in m} D[r,s] (X[r] e^{b_r - rho})
     // for (D, X) = (dA_qk, k) row / (dA_qk, q) column / (dA_kk0, k) both.
-    for (int m = 0; m < BC / TL; ++m) {
-        auto rho = [&](int x) { return m ? sb[TL * m - 1][x] : 0.f; };
+    auto pair_grads = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        auto rho = [&](int x) { if constexpr (m == 0) return 0.f; else return sb[TL * m - 1][x]; };
         // dq += row(dA_qk, k);  db += q . row(dA_qk, k)
-        wg_gemm(TL, DK, TL * (m + 1), [&](int i, int s) { return sdA[TL * m + i][s]; },
+        wg_gemm<TL, DK, TL * (m + 1)>([&](int i, int s) { return sdA[TL * m + i][s]; },
                 [&](int s, int x) { return sk[s][x] * expf(rho(x) - sb[s][x]); },
                 [&](int i, int x, float val) {
                     const int r = TL * m + i;
@@ -441,7 +512,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
                 });
         __syncthreads();
         // dk += row(dA_kk0, k);  db += k . row(dA_kk0, k)
-        wg_gemm(TL, DK, TL * (m + 1), [&](int i, int s) { return sT[TL * m + i][s]; },
+        wg_gemm<TL, DK, TL * (m + 1)>([&](int i, int s) { return sT[TL * m + i][s]; },
                 [&](int s, int x) { return sk[s][x] * expf(rho(x) - sb[s][x]); },
                 [&](int i, int x, float val) {
                     const int r = TL * m + i;
@@ -451,7 +522,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
                 });
         __syncthreads();
         // dk += col(dA_qk, q);  db -= k . col(dA_qk, q)
-        wg_gemm(TL * (m + 1), DK, TL, [&](int s, int i) { return sdA[TL * m + i][s]; },
+        wg_gemm<TL * (m + 1), DK, TL>([&](int s, int i) { return sdA[TL * m + i][s]; },
                 [&](int i, int x) { return sq[TL * m + i][x] * expf(sb[TL * m + i][x] - rho(x)); },
                 [&](int s, int x, float val) {
                     const float y = expf(rho(x) - sb[s][x]) * val;
@@ -460,7 +531,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
                 });
         __syncthreads();
         // dk += col(dA_kk0, k);  db -= k . col(dA_kk0, k)
-        wg_gemm(TL * (m + 1), DK, TL, [&](int s, int i) { return sT[TL * m + i][s]; },
+        wg_gemm<TL * (m + 1), DK, TL>([&](int s, int i) { return sT[TL * m + i][s]; },
                 [&](int i, int x) { return sk[TL * m + i][x] * expf(sb[TL * m + i][x] - rho(x)); },
                 [&](int s, int x, float val) {
                     const float y = expf(rho(x) - sb[s][x]) * val;
@@ -468,7 +539,9 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
                     sU[s][x] -= sk[s][x] * y;
                 });
         __syncthreads();
-    }
+    };
+    pair_grads(std::integral_constant<int, 0>{});
+    pair_grads(std::integral_constant<int, 1>{});
     // chunk-end terms of db (K-bar and Gamma_C depend on b at the last token),
     // then dg = reverse cumsum of db over the chunk
     if (tid < DK) {
