@@ -206,7 +206,10 @@ kda_status_t kda_verify_step(const void *q, const void *k, const void *v, const 
         kda::SpecArgs a = spec_args(q, k, v, g, beta, const_cast<float *>(S), B, K, H, dk, dv,
                                     qkv_dtype, gate_dtype, out_dtype);
         a.o = o;
-        return kda::launch_spec_step(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+        // up to 16 drafts: one tile on the matrix cores; more: the token loop
+        const hipError_t e = K <= 16 ? kda::launch_verify_tile(a, (hipStream_t)stream)
+                                     : kda::launch_spec_step(a, (hipStream_t)stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
     }
     kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S, o, nullptr, B, K, H, dk, dv,
                                      qkv_dtype, gate_dtype, out_dtype);

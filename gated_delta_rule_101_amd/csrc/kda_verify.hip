@@ -1,0 +1,244 @@
+// Speculative verify of up to 16 draft tokens per state on the matrix cores.
+//
+// "K3 Architecture Illustrated", speculative decoding: the target verifies a
+// batch of draft tokens; KDA's state must be rolled back after rejections, so
+// verify only reads the state.  Up to 16 drafts are one tile of the chunkwise
+// form ("Kimi K3 - Lesson 3 of 14 - Sequence axis"), referenced to the state:
+// with b the inclusive cumsum of the drafts' g (at most 80 in magnitude over
+// 16 tokens under g >= -5),
+//   Q~ = e^b q,  K~ = e^b k,  K^ = e^-b k  (<= e^80),
+//   A_qk = tril(Q~ K^T),  A_kk = strict_tril(K~ K^T),
+//   U = (I + Diag(beta) A_kk)^-1 Diag(beta) (V - K~ S),
+//   O = Q~ S + A_qk U.
+// Only the two products with the state are large: [Q~; K~] S is 32 x dk x dv
+// per state, against the token loop's per-token state update.
+//
+// One 4-wave workgroup per state; wave w owns value columns
+// [w dv/4, (w+1) dv/4) and streams its dk x dv/4 slice of S from HBM straight
+// into matrix-core B operands (lane (kq, r16) reads dv/64 consecutive floats
+// of row 16 kb + 4 kq + i: 16 lanes cover one contiguous row segment), so S
+// never passes through LDS and the state is read exactly once.  float32
+// operands throughout (v_mfma_f32_16x16x4_f32).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int KT = 16;          // drafts per tile
+constexpr int NTH = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int DK, int DV, typename QT, typename GT, typename OT>
+__global__ void __launch_bounds__(NTH)
+kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
+                       const GT *__restrict__ g, const GT *__restrict__ beta, const float *__restrict__ S,
+                       OT *__restrict__ o, int K, int H)
+{
+    constexpr int CW = DV / 4;      // value columns per wave
+    constexpr int NC = CW / 16;     // columns per lane (1 or 2)
+    constexpr int LK = DK + 4, LV = DV + 4;
+    __shared__ alignas(16) float sQt[KT][LK], sKt[KT][LK], sKh[KT][LK];
+    __shared__ alignas(16) float sX[KT][LV];    // V - K~ S, then U
+    __shared__ float sA[KT][KT + 4], sL[KT][KT + 4], sN[KT][KT + 4];
+    __shared__ float sbeta[KT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int col0 = wave * CW + NC * r16;   // this lane's first value column
+
+    // The wave's dk x dv/4 slice of the state, in B-operand order (block kb,
+    // step i: key channel 16 kb + 4 kq + i), requested before anything else
+    // so its HBM latency overlaps the draft preparation.
+    float sv[DK / 16][4][NC];
+    auto load_state = [&](int bh) {
+        const float *Sp = S + (size_t)bh * DK * DV;
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float *p = Sp + (size_t)(16 * kb + 4 * kq + i) * DV + col0;
+                if constexpr (NC == 2) {
+                    const f32x2 t = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(p));
+                    sv[kb][i][0] = t[0];
+                    sv[kb][i][1] = t[1];
+                } else {
+                    sv[kb][i][0] = __builtin_nontemporal_load(p);
+                }
+            }
+    };
+
+    const int bh = blockIdx.x;
+    load_state(bh);
+    {
+        const int b = bh / H, h = bh % H;
+        auto row = [&](int t) { return ((size_t)b * K + t) * H + h; };   // draft token t of (b, h)
+
+        // this lane's draft values for X = V - K~ S (C layout: drafts 4 kq + i)
+        float vv[4][NC];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * kq + i;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) vv[i][c] = t < K ? to_f32(v[row(t) * DV + col0 + c]) : 0.f;
+        }
+        // drafts: raw q, k, g into LDS by the whole workgroup (g parked in sKh),
+        // then the cumsum of g down each key channel and the scaled rows
+        for (int e = tid; e < KT * DK; e += NTH) {
+            const int t = e / DK, x = e % DK;
+            const bool live = t < K;
+            const size_t i = row(live ? t : 0) * DK + x;
+            sQt[t][x] = live ? to_f32(q[i]) : 0.f;
+            sKt[t][x] = live ? to_f32(k[i]) : 0.f;
+            sKh[t][x] = live ? to_f32(g[i]) : 0.f;
+        }
+        if (tid < KT) sbeta[tid] = tid < K ? to_f32(beta[row(tid)]) : 0.f;
+        __syncthreads();
+        if (tid < DK) {
+            const int x = tid;
+            float acc = 0.f;
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                acc += sKh[t][x];
+                const float e = __builtin_amdgcn_exp2f(acc * LOG2E), ei = __builtin_amdgcn_exp2f(-acc * LOG2E);
+                const float kv = sKt[t][x];
+                sQt[t][x] *= e;
+                sKt[t][x] = kv * e;
+                sKh[t][x] = kv * ei;
+            }
+        }
+        __syncthreads();
+
+        // [Q~; K~] S for this wave's columns
+        f32x4 aq[NC], ak[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) aq[c] = ak[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb) {
+            const int x = 16 * kb + 4 * kq;
+            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&sQt[r16][x]);
+            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&sKt[r16][x]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    aq[c] = mma(qa[i], sv[kb][i][c], aq[c]);
+                    ak[c] = mma(ka[i], sv[kb][i][c], ak[c]);
+                }
+        }
+        // aq[c], ak[c]: lane (kq, r16) holds draft rows 4 kq + i of column col0 + c.
+        // X = V - K~ S to LDS (the B operand of the solve below).
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) sX[4 * kq + i][col0 + c] = vv[i][c] - ak[c][i];
+        // Gram tiles: wave 0 A_qk = tril(Q~ K^T), wave 1 A_kk0 = strict_tril(K~ K^T)
+        if (wave < 2) {
+            const float(*L)[LK] = wave == 0 ? sQt : sKt;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; ++kb) {
+                const int x = 16 * kb + 4 * kq;
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&L[r16][x]);
+                const f32x4 bb = *reinterpret_cast<const f32x4 *>(&sKh[r16][x]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc = mma(a[i], bb[i], acc);
+            }
+            // acc[i]: row 4 kq + i, column r16
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * kq + i, s = r16;
+                if (wave == 0) sA[r][s] = s <= r ? acc[i] : 0.f;
+                else sL[r][s] = s < r ? acc[i] : 0.f;
+            }
+        }
+        __syncthreads();
+        if (tid < KT) {   // column tid of N = (I + Diag(beta) A_kk0)^-1
+            const int j = tid;
+            float xs[KT];
+#pragma unroll
+            for (int i = 0; i < KT; ++i) {
+                float s = i == j ? 1.f : 0.f;
+#pragma unroll
+                for (int l = 0; l < i; ++l) s -= sbeta[i] * sL[i][l] * xs[l];
+                xs[i] = s;
+            }
+#pragma unroll
+            for (int i = 0; i < KT; ++i) sN[i][j] = xs[i];
+        }
+        __syncthreads();
+        // U = N Diag(beta) X for this wave's columns (lane (kq, r16) feeds
+        // draft index 4 kq + i; the result lands in the same C layout as aq)
+        f32x4 au[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) au[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 4 * kq + i;
+            const float a = sN[r16][s] * sbeta[s];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) au[c] = mma(a, sX[s][col0 + c], au[c]);
+        }
+        __syncthreads();   // every wave has read its X before U overwrites it
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) sX[4 * kq + i][col0 + c] = au[c][i];
+        __syncthreads();
+        // O = Q~ S + A_qk U, accumulated onto aq
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 4 * kq + i;
+            const float a = sA[r16][s];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) aq[c] = mma(a, sX[s][col0 + c], aq[c]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 4 * kq + i;
+            if (t < K) {
+                OT *op = o + row(t) * DV + col0;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) op[c] = from_f32<OT>(aq[c][i]);
+            }
+        }
+    }
+}
+
+template <int DK, int DV, typename QT, typename GT, typename OT>
+hipError_t launch(const SpecArgs &a, hipStream_t s)
+{
+    kda_verify_tile_kernel<DK, DV, QT, GT, OT><<<(unsigned)(a.B * a.H), NTH, 0, s>>>(
+        (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta, a.S, (OT *)a.o,
+        a.K, a.H);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t dispatch(const SpecArgs &a, hipStream_t s)
+{
+    typedef uint16_t b16;
+    if (a.qkv_bf16) {
+        if (a.gate_bf16) return a.out_bf16 ? launch<DK, DV, b16, b16, b16>(a, s) : launch<DK, DV, b16, b16, float>(a, s);
+        return a.out_bf16 ? launch<DK, DV, b16, float, b16>(a, s) : launch<DK, DV, b16, float, float>(a, s);
+    }
+    if (a.gate_bf16) return a.out_bf16 ? launch<DK, DV, float, b16, b16>(a, s) : launch<DK, DV, float, b16, float>(a, s);
+    return a.out_bf16 ? launch<DK, DV, float, float, b16>(a, s) : launch<DK, DV, float, float, float>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_verify_tile(const SpecArgs &a, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    if (a.dk == 64) return a.dv == 64 ? dispatch<64, 64>(a, stream) : dispatch<64, 128>(a, stream);
+    return a.dv == 64 ? dispatch<128, 64>(a, stream) : dispatch<128, 128>(a, stream);
+}
+
+}  // namespace kda
