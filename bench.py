@@ -440,6 +440,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: calibration copy, then each kernel a few times")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="run only the backward leg (two calls) and print its JSON object")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc runs of --profile-pass")
     args = ap.parse_args()
@@ -447,8 +449,8 @@ def main():
         counters_to_traffic(*args.counters_from)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the KDA path "
-              "runs one workload per GPU; multi-GPU runs are not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): every workload here "
+              "runs on a single GPU (heads would shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -459,6 +461,9 @@ def main():
     kda.load_library()
     if args.profile_pass:
         profile_pass(kda)
+        return
+    if args.only_backward:
+        print(json.dumps(bench_backward(kda, reps=2)), flush=True)
         return
 
     w, d, ms, tok_s, rf, extra = bench_fwd(kda, args.steps, args.warmup)
