@@ -112,3 +112,31 @@ def test_backward_head_group_shape_sampled_head(kda):
     say("      " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
         assert e <= TAU[n], (n, e)
+
+
+def test_backward_full_training_shape_sampled_head(kda):
+    """The benchmark's backward: B4 H32 T16384 d128 (bf16 q/k/v/g/beta,
+    float32 dO, zero initial state); one head against the oracle over the
+    whole 16384-token sequence."""
+    from oracle.kda_oracle_bwd import kda_bwd
+    from kda_workloads import gen_torch
+    w = configs.TRAIN_BF16
+    say(f"[bwd full] {w.name}: generating")
+    d = gen_torch.fwd_inputs(w)
+    gen_ = torch.Generator(device="cuda")
+    gen_.manual_seed(7)
+    dO = torch.randn((w.B, w.T, w.H, w.dv), generator=gen_, device="cuda", dtype=torch.float32)
+    say(f"[bwd full] kernels")
+    out = kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None, dO, None)
+    torch.cuda.synchronize()
+    b, h = 3, 17
+    sl = lambda t: f64(t[b:b + 1, :, h:h + 1])  # noqa: E731
+    say(f"[bwd full] oracle on head ({b}, {h})")
+    ref = kda_bwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["g"]), f64(d["beta"][b:b + 1, :, h:h + 1]),
+                  None, sl(dO), None)
+    got = {"dq": sl(out[0]), "dk": sl(out[1]), "dv": sl(out[2]), "dg": sl(out[3]),
+           "dbeta": f64(out[4][b:b + 1, :, h:h + 1]), "dS0": f64(out[5][b:b + 1, h:h + 1])}
+    errs = {n: _err(got[n], ref[n]) for n in got}
+    say("      " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TAU[n], (n, e)

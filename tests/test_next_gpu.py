@@ -192,3 +192,34 @@ def test_decode_with_gate_logits(kda, orc, qkv):
         torch.cuda.synchronize()
         assert err_ratio(f64(o), o_ref) <= tau_for(qkv), step
     assert err_ratio(f64(S_dev), S_ref) <= tau_for(qkv)
+
+
+# ------------------------------------------------------------- full sizes
+
+def test_full_size_verify_and_commit(kda, orc):
+    """The benchmark's speculative workload: 256 x 96 states (dk = dv = 128,
+    bf16 drafts, fp32 gates), 16 drafts, 8 accepted; sampled states against
+    the oracle (verify outputs of all 16 drafts, committed state)."""
+    from gpu_support import head_slices, spread_heads
+    from kda_workloads import gen_torch
+    w = configs.DECODE_BF16
+    fw = configs.Workload(name="spec_drafts", kind="fwd", B=w.B, H=w.H, dk=w.dk, dv=w.dv, T=16,
+                          qkv=w.qkv, gate=w.gate, s0_sd=None)
+    say("[spec full] generating 256 x 96 states and 16 drafts each")
+    S = gen_torch.decode_initial_state(w)
+    x = gen_torch.fwd_inputs(fw)
+    heads = spread_heads(w.B, w.H, 6, seed=3)
+    S_sel = f64(torch.stack([S[b, h] for b, h in heads]).unsqueeze(0))
+    o = kda.kda_verify_step(x["q"], x["k"], x["v"], x["g"], x["beta"], S)
+    acc = torch.full((w.B,), 8, dtype=torch.int32, device="cuda")
+    kda.kda_commit_step(x["k"], x["v"], x["g"], x["beta"], acc, S)
+    torch.cuda.synchronize()
+    s = head_slices(x, heads)
+    say(f"[spec full] oracle on {heads}")
+    o_ref, _ = orc.fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], S_sel, want_state=False)
+    _, S_ref = orc.fwd(*(s[n][:, :8] for n in NAMES), S_sel)
+    og = f64(torch.stack([o[b, :, h] for b, h in heads], dim=1).unsqueeze(0))
+    Sg = f64(torch.stack([S[b, h] for b, h in heads]).unsqueeze(0))
+    eo, es = err_ratio(og, o_ref), err_ratio(Sg, S_ref)
+    say(f"      err/rms o={eo:.3e} S={es:.3e}")
+    assert eo <= tau_for(w.qkv) and es <= tau_for(w.qkv)
