@@ -80,6 +80,18 @@ __device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
     }
 }
 
+// Runs f(e) over this thread's elements tid, tid + NTH, ... of a COUNT-element
+// block.  COUNT is a whole number of workgroup rounds, so the trip count is
+// fixed and the loop unrolls: every global load of the block is issued before
+// any of them is waited for.
+template <int COUNT, typename F>
+__device__ __forceinline__ void for_elems(F &&f)
+{
+    static_assert(COUNT % NTH == 0, "whole rounds of the workgroup");
+#pragma unroll
+    for (int i = 0; i < COUNT / NTH; ++i) f((int)threadIdx.x + NTH * i);
+}
+
 // e^x through the hardware base-2 exponential.  The arguments are
 // differences of chunk-local log-decay sums: tile-local factors stay within
 // [-80, 80] (g >= -5 over 16 tokens), where rounding x log2(e) costs at most
@@ -137,7 +149,7 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
         }
     }
     __syncthreads();
-    for (int e = tid; e < BC * DK; e += NTH) ws.b[ch * BC * DK + e] = sb[e / DK][e % DK];
+    for (int e = tid; e < BC * DK; e += NTH) { ws.b[ch * BC * DK + e] = sb[e / DK][e % DK]; }
 
     // Gram matrices, one row tile at a time: rows scaled by e^{b - rho},
     // keys by e^{rho - b}, rho = b at the end of the previous tile.
@@ -221,10 +233,10 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
         }
     };
 
-    for (int e = tid; e < DK * SW; e += NTH) {
+    for_elems<DK * SW>([&](int e) {
         const int r = e / SW, j = e % SW;
         sS[r][j] = S0 ? S0[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
-    }
+    });
     if (NC > 0) fetch(0);
     for (int c = 0; c < NC; ++c) {
         const size_t ch = (size_t)bh * NC + c;
@@ -242,10 +254,10 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
         }
         __syncthreads();
         if (c + 1 < NC) fetch(c + 1);
-        for (int e = tid; e < DK * SW; e += NTH) {
+        for_elems<DK * SW>([&](int e) {
             const int r = e / SW, j = e % SW;
             ws.h[(ch * DK + r) * DV + col0 + j] = sS[r][j];
-        }
+        });
         // U = U_v - W S  (U_v is replaced by U in the workspace)
         wg_gemm<BC, SW, DK>([&](int i, int x) { return sW[i][x]; }, [&](int x, int j) { return sS[x][j]; },
                             [&](int i, int j, float val) {
@@ -370,14 +382,14 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
-    for (int e = tid; e < BC * DV; e += NTH) {
+    for_elems<BC * DV>([&](int e) {
         const int r = e / DV, j = e % DV, t = c * BC + r;
         sY1[r][j] = t < T ? to_f32(dO[tix(bb, t, h, j, T, H, DV)]) : 0.f;
         sY2[r][j] = ws.dU[ch * BC * DV + e];
-    }
+    });
     for (int half = 0; half < 2; ++half) {
         const int x0 = half * DH;
-        for (int e = tid; e < DH * DV; e += NTH) sS[e / DV][e % DV] = ws.h[ch * DK * DV + (size_t)x0 * DV + e];
+        for_elems<DH * DV>([&](int e) { sS[e / DV][e % DV] = ws.h[ch * DK * DV + (size_t)x0 * DV + e]; });
         __syncthreads();
         // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1), key columns x0..x0+DH-1
         wg_gemm<2 * BC, DH, DV>([&](int i, int j) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
@@ -389,7 +401,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         __syncthreads();
         if (half == 0) continue;
         // U replaces dU (both halves of dW are done)
-        for (int e = tid; e < BC * DV; e += NTH) sY2[e / DV][e % DV] = ws.U[ch * BC * DV + e];
+        for_elems<BC * DV>([&](int e) { sY2[e / DV][e % DV] = ws.U[ch * BC * DV + e]; });
         __syncthreads();
         // dA_qk = tril(dO U^T)
         wg_gemm<BC, BC, DV>([&](int i, int j) { return sY1[i][j]; }, [&](int j, int s) { return sY2[s][j]; },
@@ -399,7 +411,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         // the upper half of S is still in LDS; the lower half is reloaded
         const int half = 1 - hh, x0 = half * DH;
         if (half == 0) {
-            for (int e = tid; e < DH * DV; e += NTH) sS[e / DV][e % DV] = ws.h[ch * DK * DV + e];
+            for_elems<DH * DV>([&](int e) { sS[e / DV][e % DV] = ws.h[ch * DK * DV + e]; });
             __syncthreads();
         }
         // dGamma_C = rowsum(S . dS') with TPR threads per row; dS' replaces S
@@ -448,7 +460,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
-    for (int e = tid; e < BC * DK; e += NTH) {
+    for_elems<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK, t = c * BC + r;
         const bool live = t < T;
         const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
@@ -456,18 +468,18 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         sk[r][x] = live ? to_f32(k[i]) : 0.f;
         sb[r][x] = ws.b[ch * BC * DK + e];
         sP[r][x] = ws.dW[ch * BC * DK + e];
-    }
-    for (int e = tid; e < BC * DV; e += NTH) {
+    });
+    for_elems<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
         sV[r][x] = t < T ? to_f32(v[tix(bb, t, h, x, T, H, DV)]) : 0.f;
         sU[r][x] = ws.dU[ch * BC * DV + e];
-    }
-    for (int e = tid; e < BC * BC; e += NTH) {
+    });
+    for_elems<BC * BC>([&](int e) {
         const int r = e / BC, s = e % BC;
         sN[r][s] = ws.N[ch * BC * BC + e];
         sAk[r][s] = ws.Akk0[ch * BC * BC + e];
         sdA[r][s] = ws.dAqk[ch * BC * BC + e];
-    }
+    });
     if (tid < BC) {
         const int t = c * BC + tid;
         sbeta[tid] = t < T ? to_f32(beta[((size_t)bb * T + t) * H + h]) : 0.f;
@@ -497,15 +509,15 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         sdb1[tid] = s;
     }
     __syncthreads();
-    for (int e = tid; e < BC * BC; e += NTH) sT[e / BC][e % BC] *= sbeta[e % BC];   // dN = dT Diag(beta)
-    for (int e = tid; e < BC * DK; e += NTH) {
+    for_elems<BC * BC>([&](int e) { sT[e / BC][e % BC] *= sbeta[e % BC]; });   // dN = dT Diag(beta)
+    for_elems<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK;
         const float eb = ex(sb[r][x]), ekb = ex(sb[BC - 1][x] - sb[r][x]);
         const float dqt = ws.dQt[ch * BC * DK + e], dkb = ws.dKb[ch * BC * DK + e];
         sP[r][x] = eb * dqt;
         sV[r][x] += ekb * dkb;
         sU[r][x] += eb * sq[r][x] * dqt - ekb * sk[r][x] * dkb;
-    }
+    });
     __syncthreads();
     // dA_kk = -strict_tril(N^T dN N^T)
     wg_gemm<BC, BC, BC>([&](int i, int l) { return sN[l][i]; }, [&](int l, int s) { return sT[l][s]; },
@@ -576,6 +588,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         const int x = tid;
         const float bl = sb[BC - 1][x];
         float tail = ex(bl) * ws.dGam[ch * DK + x];
+#pragma unroll
         for (int r = 0; r < BC; ++r) tail += ex(bl - sb[r][x]) * sk[r][x] * ws.dKb[(ch * BC + r) * DK + x];
         float acc = tail;
         for (int r = BC - 1; r >= 0; --r) {
@@ -584,7 +597,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         }
     }
     __syncthreads();
-    for (int e = tid; e < BC * DK; e += NTH) {
+    for_elems<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK, t = c * BC + r;
         if (t < T) {
             const size_t i = tix(bb, t, h, x, T, H, DK);
@@ -592,7 +605,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
             dk[i] = sV[r][x];
             dg[i] = sU[r][x];
         }
-    }
+    });
 }
 
 // ------------------------------------------------------------- launch
