@@ -90,9 +90,8 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         }
         // drafts: raw q, k, g into LDS by the whole workgroup (g parked in sKh),
         // then the cumsum of g down each key channel and the scaled rows
-#pragma unroll
-        for (int ii = 0; ii < KT * DK / NTH; ++ii) {   // fixed count: all loads issue first
-            const int e = tid + NTH * ii, t = e / DK, x = e % DK;
+        for (int e = tid; e < KT * DK; e += NTH) {
+            const int t = e / DK, x = e % DK;
             const bool live = t < K;
             const size_t i = row(live ? t : 0) * DK + x;
             sQt[t][x] = live ? to_f32(q[i]) : 0.f;
