@@ -105,6 +105,16 @@ __device__ __forceinline__ size_t tix(int b, int t, int h, int c, int T, int H, 
     return (((size_t)b * T + t) * H + h) * d + c;
 }
 
+// Loads element i unconditionally (i built from a token index clamped into
+// [0, T)) and zeroes it for tokens past the end.  A branch around the load
+// instead would make the code after the branch wait for it, one load at a time.
+template <typename X>
+__device__ __forceinline__ float ld_live(const X *p, size_t i, bool live)
+{
+    const float v = to_f32(p[i]);
+    return live ? v : 0.f;
+}
+
 // ---------------------------------------------------------------- prep
 
 template <int DK, int DV, typename QT, typename GT>
@@ -120,21 +130,21 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
-    for (int e = tid; e < BC * DK; e += NTH) {
+    for_elems<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK, t = c * BC + r;
         const bool live = t < T;
         const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
-        sq[r][x] = live ? to_f32(q[i]) : 0.f;
-        sk[r][x] = live ? to_f32(k[i]) : 0.f;
-        sb[r][x] = live ? to_f32(g[i]) : 0.f;
-    }
-    for (int e = tid; e < BC * DV; e += NTH) {
+        sq[r][x] = ld_live(q, i, live);
+        sk[r][x] = ld_live(k, i, live);
+        sb[r][x] = ld_live(g, i, live);
+    });
+    for_elems<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
-        sv[r][x] = t < T ? to_f32(v[tix(bb, t, h, x, T, H, DV)]) : 0.f;
-    }
+        sv[r][x] = ld_live(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T);
+    });
     if (tid < BC) {
         const int t = c * BC + tid;
-        sbeta[tid] = t < T ? to_f32(beta[((size_t)bb * T + t) * H + h]) : 0.f;
+        sbeta[tid] = ld_live(beta, ((size_t)bb * T + (t < T ? t : T - 1)) * H + h, t < T);
     }
     for (int e = tid; e < BC * LC; e += NTH) {
         (&sA[0][0])[e] = 0.f;
@@ -224,7 +234,7 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
             pw[i] = ws.W[ch * BC * DK + e];
             pb[i] = ws.b[ch * BC * DK + e];
             pbl[i] = ws.b[(ch * BC + BC - 1) * DK + x];
-            pk[i] = t < T ? to_f32(k[tix(bb, t, h, x, T, H, DK)]) : 0.f;
+            pk[i] = ld_live(k, tix(bb, t < T ? t : T - 1, h, x, T, H, DK), t < T);
         }
 #pragma unroll
         for (int i = 0; i < PU; ++i) {
@@ -296,8 +306,8 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
             const int e = tid + NTH * i, r = e / DK, x = e % DK, t = c * BC + r;
             const bool live = t < T;
             const size_t ti = tix(bb, live ? t : 0, h, x, T, H, DK);
-            pk[i] = live ? to_f32(k[ti]) : 0.f;
-            pq[i] = live ? to_f32(q[ti]) : 0.f;
+            pk[i] = ld_live(k, ti, live);
+            pq[i] = ld_live(q, ti, live);
             pb[i] = ws.b[ch * BC * DK + e];
             pbl[i] = ws.b[(ch * BC + BC - 1) * DK + x];
             pw[i] = ws.W[ch * BC * DK + e];
@@ -305,7 +315,7 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
 #pragma unroll
         for (int i = 0; i < PO; ++i) {
             const int e = tid + NTH * i, r = e / SW, j = e % SW, t = c * BC + r;
-            po[i] = t < T ? to_f32(dO[tix(bb, t, h, col0 + j, T, H, DV)]) : 0.f;
+            po[i] = ld_live(dO, tix(bb, t < T ? t : T - 1, h, col0 + j, T, H, DV), t < T);
         }
 #pragma unroll
         for (int i = 0; i < PA; ++i) pa[i] = ws.Aqk[ch * BC * BC + tid + NTH * i];
@@ -384,7 +394,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
 
     for_elems<BC * DV>([&](int e) {
         const int r = e / DV, j = e % DV, t = c * BC + r;
-        sY1[r][j] = t < T ? to_f32(dO[tix(bb, t, h, j, T, H, DV)]) : 0.f;
+        sY1[r][j] = ld_live(dO, tix(bb, t < T ? t : T - 1, h, j, T, H, DV), t < T);
         sY2[r][j] = ws.dU[ch * BC * DV + e];
     });
     for (int half = 0; half < 2; ++half) {
@@ -464,14 +474,14 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         const int r = e / DK, x = e % DK, t = c * BC + r;
         const bool live = t < T;
         const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
-        sq[r][x] = live ? to_f32(q[i]) : 0.f;
-        sk[r][x] = live ? to_f32(k[i]) : 0.f;
+        sq[r][x] = ld_live(q, i, live);
+        sk[r][x] = ld_live(k, i, live);
         sb[r][x] = ws.b[ch * BC * DK + e];
         sP[r][x] = ws.dW[ch * BC * DK + e];
     });
     for_elems<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
-        sV[r][x] = t < T ? to_f32(v[tix(bb, t, h, x, T, H, DV)]) : 0.f;
+        sV[r][x] = ld_live(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T);
         sU[r][x] = ws.dU[ch * BC * DV + e];
     });
     for_elems<BC * BC>([&](int e) {
@@ -482,7 +492,7 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     });
     if (tid < BC) {
         const int t = c * BC + tid;
-        sbeta[tid] = t < T ? to_f32(beta[((size_t)bb * T + t) * H + h]) : 0.f;
+        sbeta[tid] = ld_live(beta, ((size_t)bb * T + (t < T ? t : T - 1)) * H + h, t < T);
     }
     __syncthreads();
     // dT = tril(dW (Gamma . K)^T + dU V^T)
