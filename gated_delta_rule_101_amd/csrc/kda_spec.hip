@@ -70,20 +70,26 @@ kda_spec_kernel(const typename Store<QBF>::type *__restrict__ q,
     for (int t0 = 0; t0 < n; t0 += KBLK) {
         const int nb = min(KBLK, n - t0);
         if (t0 > 0) lds_barrier();   // every thread is done with the previous block
-        // stage the block: token t of (b, h) sits at row (b K + t) H + h
-        for (int e = threadIdx.x; e < nb * DK; e += NTHREADS) {
-            const int j = e / DK, c = e % DK;
-            const size_t row = ((size_t)b * K + t0 + j) * H + h;
+        // stage the block: token t of (b, h) sits at row (b K + t) H + h.  A
+        // fixed count of unconditional loads (slots past the block re-read
+        // its last token and are never used), so every load issues before
+        // the first wait.
+#pragma unroll
+        for (int it = 0; it < KBLK * DK / NTHREADS; ++it) {
+            const int e = threadIdx.x + NTHREADS * it, j = e / DK, c = e % DK;
+            const size_t row = ((size_t)b * K + t0 + min(j, nb - 1)) * H + h;
             const int pc = (c % NRG) * RPT + c / NRG;
             if constexpr (!COMMIT) s_q[j][pc] = to_f32(q[row * DK + c]);
             s_k[j][pc] = to_f32(k[row * DK + c]);
             s_a[j][pc] = __expf(to_f32(g[row * DK + c]));
         }
-        for (int e = threadIdx.x; e < nb * DV; e += NTHREADS) {
-            const int j = e / DV, c = e % DV;
-            s_v[j][c] = to_f32(v[(((size_t)b * K + t0 + j) * H + h) * DV + c]);
+#pragma unroll
+        for (int it = 0; it < KBLK * DV / NTHREADS; ++it) {
+            const int e = threadIdx.x + NTHREADS * it, j = e / DV, c = e % DV;
+            s_v[j][c] = to_f32(v[(((size_t)b * K + t0 + min(j, nb - 1)) * H + h) * DV + c]);
         }
-        if (threadIdx.x < nb) s_b[threadIdx.x] = to_f32(beta[((size_t)b * K + t0 + threadIdx.x) * H + h]);
+        if (threadIdx.x < KBLK)
+            s_b[threadIdx.x] = to_f32(beta[((size_t)b * K + t0 + min((int)threadIdx.x, nb - 1)) * H + h]);
         lds_barrier();
 
         for (int j = 0; j < nb; ++j) {

@@ -30,6 +30,16 @@ constexpr int NTH = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Loads element i unconditionally (i built from a draft index clamped into
+// [0, K)) and zeroes it for drafts past the end; a branch around the load
+// would make the code after it wait for each load in turn.
+template <typename X>
+__device__ __forceinline__ float ld_live(const X *p, size_t i, bool live)
+{
+    const float v = to_f32(p[i]);
+    return live ? v : 0.f;
+}
+
 __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -86,19 +96,20 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * kq + i;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) vv[i][c] = t < K ? to_f32(v[row(t) * DV + col0 + c]) : 0.f;
+            for (int c = 0; c < NC; ++c) vv[i][c] = ld_live(v, row(t < K ? t : K - 1) * DV + col0 + c, t < K);
         }
         // drafts: raw q, k, g into LDS by the whole workgroup (g parked in sKh),
         // then the cumsum of g down each key channel and the scaled rows
-        for (int e = tid; e < KT * DK; e += NTH) {
-            const int t = e / DK, x = e % DK;
+#pragma unroll
+        for (int it = 0; it < KT * DK / NTH; ++it) {   // fixed count: all loads issue first
+            const int e = tid + NTH * it, t = e / DK, x = e % DK;
             const bool live = t < K;
             const size_t i = row(live ? t : 0) * DK + x;
-            sQt[t][x] = live ? to_f32(q[i]) : 0.f;
-            sKt[t][x] = live ? to_f32(k[i]) : 0.f;
-            sKh[t][x] = live ? to_f32(g[i]) : 0.f;
+            sQt[t][x] = ld_live(q, i, live);
+            sKt[t][x] = ld_live(k, i, live);
+            sKh[t][x] = ld_live(g, i, live);
         }
-        if (tid < KT) sbeta[tid] = tid < K ? to_f32(beta[row(tid)]) : 0.f;
+        if (tid < KT) sbeta[tid] = ld_live(beta, row(tid < K ? tid : K - 1), tid < K);
         __syncthreads();
         if (tid < DK) {
             const int x = tid;
