@@ -70,6 +70,14 @@ __device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) epi(i1 + 4 * kq + r, j1 + r16, acc1[r]);
+        } else if constexpr (K % 8 == 0) {   // one tile: even and odd k-steps in two chains
+            f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < K; kk += 8) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + kq), B(kk + kq, j0 + r16), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + 4 + kq), B(kk + 4 + kq, j0 + r16), acc1, 0, 0, 0);
+            }
+            acc0 += acc1;
         } else {
 #pragma unroll
             for (int kk = 0; kk < K; kk += 4)
@@ -479,6 +487,15 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         sb[r][x] = ws.b[ch * BC * DK + e];
         sP[r][x] = ws.dW[ch * BC * DK + e];
     });
+    // dQ~ and dK-bar for the element pass further down, requested now (this
+    // kernel runs one workgroup per CU, so registers are plentiful)
+    constexpr int PE = BC * DK / NTH;
+    float pdq[PE], pdk[PE];
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        pdq[i] = ws.dQt[ch * BC * DK + tid + NTH * i];
+        pdk[i] = ws.dKb[ch * BC * DK + tid + NTH * i];
+    }
     for_elems<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
         sV[r][x] = ld_live(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T);
@@ -520,14 +537,15 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     }
     __syncthreads();
     for_elems<BC * BC>([&](int e) { sT[e / BC][e % BC] *= sbeta[e % BC]; });   // dN = dT Diag(beta)
-    for_elems<BC * DK>([&](int e) {
-        const int r = e / DK, x = e % DK;
+#pragma unroll
+    for (int ii = 0; ii < PE; ++ii) {
+        const int e = tid + NTH * ii, r = e / DK, x = e % DK;
         const float eb = ex(sb[r][x]), ekb = ex(sb[BC - 1][x] - sb[r][x]);
-        const float dqt = ws.dQt[ch * BC * DK + e], dkb = ws.dKb[ch * BC * DK + e];
+        const float dqt = pdq[ii], dkb = pdk[ii];
         sP[r][x] = eb * dqt;
         sV[r][x] += ekb * dkb;
         sU[r][x] += eb * sq[r][x] * dqt - ekb * sk[r][x] * dkb;
-    });
+    }
     __syncthreads();
     // dA_kk = -strict_tril(N^T dN N^T)
     wg_gemm<BC, BC, BC>([&](int i, int l) { return sN[l][i]; }, [&](int l, int s) { return sT[l][s]; },
