@@ -123,6 +123,24 @@ __device__ __forceinline__ float ld_live(const X *p, size_t i, bool live)
     return live ? v : 0.f;
 }
 
+// Workgroup -> (head, value slab) for the two carries.  Workgroups are dealt
+// to the 8 XCDs round-robin; when the head count is a multiple of 8, the
+// nslab workgroups of one head get indices congruent mod 8, so they run on
+// one XCD and the chunk inputs they all read come from its L2 after the
+// first read.
+__device__ __forceinline__ void head_and_slab(int nslab, int &bh, int &slab)
+{
+    const int id = blockIdx.x, nheads = gridDim.x / nslab;
+    if (nheads % 8 == 0) {
+        const int grp = id / (8 * nslab), in = id % (8 * nslab);
+        slab = in / 8;
+        bh = grp * 8 + in % 8;
+    } else {
+        bh = id / nslab;
+        slab = id % nslab;
+    }
+}
+
 // ---------------------------------------------------------------- prep
 
 template <int DK, int DV, typename QT, typename GT>
@@ -230,7 +248,9 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
     constexpr int PE = BC * DK / NTH, PU = BC * SW / NTH;   // per-thread elements of a chunk block
     __shared__ float sS[DK][LS], sW[BC][LK], sKb[BC][LK], sU[BC][LS], sG[DK];
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / nslab, col0 = (blockIdx.x % nslab) * SW, bb = bh / H, h = bh % H;
+    int bh, slab;
+    head_and_slab(nslab, bh, slab);
+    const int col0 = slab * SW, bb = bh / H, h = bh % H;
 
     // the next chunk's inputs, loaded one chunk ahead into registers
     float pw[PE], pk[PE], pb[PE], pbl[PE], pu[PU];
@@ -303,7 +323,9 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
     constexpr int PE = BC * DK / NTH, PO = BC * SW / NTH, PA = BC * BC / NTH;
     __shared__ float sD[DK][LS], sX1[BC][LK], sX2[BC][LK], sA[BC][LC], sO[BC][LS], sdU[BC][LS], sG[DK];
     const int tid = threadIdx.x;
-    const int bh = blockIdx.x / nslab, col0 = (blockIdx.x % nslab) * SW, bb = bh / H, h = bh % H;
+    int bh, slab;
+    head_and_slab(nslab, bh, slab);
+    const int col0 = slab * SW, bb = bh / H, h = bh % H;
 
     // the previous chunk's inputs (the pass runs backwards), one chunk ahead
     float pk[PE], pq[PE], pb[PE], pbl[PE], pw[PE], po[PO], pa[PA];
