@@ -168,28 +168,28 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
         for (int i = 0; i < 4; ++i)
             S[kt][i] = S0 ? S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
 
+    // Loads are unconditional: a token past the end re-reads the last real
+    // token (or token 0), so padding content never enters the arithmetic, and
+    // is turned into an identity token where its values are used (g, beta, q,
+    // k zeroed; its v only meets beta = 0).  A branch
+    // around the loads would make the code after it wait for each of them.
+    const int last = len > 0 ? len - 1 : 0;   // what a token past the end re-reads
     auto load_chunk = [&](ChunkIn<DK, QT, GT> &in, int c) {
         const int t = c * C + TILE * wave + r;
-        if (t < len) {
-            const size_t rr = row_qk(t);
+        const size_t rr = row_qk(t < len ? t : last);
 #pragma unroll
-            for (int j = 0; j < KB; ++j) {
-                in.q[j].load(q + rr * DK + 32 * j + 8 * gq);
-                in.k[j].load(k + rr * DK + 32 * j + 8 * gq);
-                in.g[j].load(g + rr * DK + 32 * j + 8 * gq);
-            }
-            in.beta = beta[rr];
-        } else {   // identity token: no decay, no write, zero read
-#pragma unroll
-            for (int j = 0; j < KB; ++j) { in.q[j].zero(); in.k[j].zero(); in.g[j].zero(); }
-            in.beta = GT(0);
+        for (int j = 0; j < KB; ++j) {
+            in.q[j].load(q + rr * DK + 32 * j + 8 * gq);
+            in.k[j].load(k + rr * DK + 32 * j + 8 * gq);
+            in.g[j].load(g + rr * DK + 32 * j + 8 * gq);
         }
+        in.beta = beta[rr];
 #pragma unroll
         for (int m = 0; m < NT; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t2 = c * C + TILE * m + 4 * gq + i;
-                in.v[m][i] = t2 < T ? v[row_qk(t2) * dv + col0 + r] : QT(0);
+                in.v[m][i] = v[row_qk(t2 < len ? t2 : last) * dv + col0 + r];
             }
     };
 
@@ -203,15 +203,18 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
 
         // ====================================================== prep (wave m = tile m)
         const int m = wave;
+        const bool live = c * C + TILE * m + r < len;   // else an identity token
         float fdec[KB][8];   // f = decay since the tile start, in [e^-80, 1]
 #pragma unroll
         for (int j = 0; j < KB; ++j) {
             float gl[8];
             cur.g[j].to_f32(gl);
             if constexpr (GL) {   // an identity token keeps g = 0, not the gate of logit 0
-                const bool live = c * C + TILE * m + r < len;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) gl[i] = live ? gate_from_logit(gl[i], gate_scale) : 0.f;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) gl[i] = live ? gl[i] : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -286,6 +289,11 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
             float qv[8], kv[8];
             cur.q[j].to_f32(qv);
             cur.k[j].to_f32(kv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                qv[i] = live ? qv[i] : 0.f;
+                kv[i] = live ? kv[i] : 0.f;
+            }
             float qt[8], ktv[8], kh[8], kb[8], qf[8], kf[8], ki[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -330,7 +338,7 @@ kda_chunk_fwd_kernel(const typename Store<QBF>::type *__restrict__ q,
                 if constexpr (SPLIT) sm.KbT[1][(ch + i) * LDC + TILE * m + r] = lo;
             }
         }
-        if (gq == 0) sm.beta[TILE * m + r] = to_f32(cur.beta);
+        if (gq == 0) sm.beta[TILE * m + r] = live ? to_f32(cur.beta) : 0.f;
         lds_barrier();
 
         // ====================================================== Gram (wave m = block row m)
