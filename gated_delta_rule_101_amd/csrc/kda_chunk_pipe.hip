@@ -67,6 +67,7 @@ constexpr unsigned SPIN_LIMIT = 1u << 20;   // bound on every producer wait
 // Tiles (m, n) of the lower block triangle, n <= m, and of the strict one, n < m.
 __host__ __device__ constexpr int lower_index(int m, int n) { return m * (m + 1) / 2 + n; }
 __host__ __device__ constexpr int strict_index(int m, int n) { return m * (m - 1) / 2 + n; }
+template <int M> struct TileIndex { static constexpr int value = M; };
 constexpr int NLOWER = NT * (NT + 1) / 2;
 constexpr int NSTRICT = NT * (NT - 1) / 2;
 
@@ -330,112 +331,121 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 producer_meet(&sm.arrivals, NPROD * meetings, lane);
 
                 // ---------------------------------------------- staged operands and block row m of the Gram
-                f32x4 gq_o[NT - 1], gk_o[NT - 1];
+                // Instantiated once per tile: which Gram tiles exist and the
+                // whole-tile decays between tiles are then fixed at compile time,
+                // with no per-tile branches (and no register copies merging them).
+                auto block_row = [&](auto tile) __attribute__((always_inline)) {
+                    constexpr int M = decltype(tile)::value;
+                    f32x4 gq_o[NT - 1], gk_o[NT - 1];
 #pragma unroll
-                for (int d = 0; d < NT - 1; ++d) {
-                    gq_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    gk_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                    for (int d = 0; d < NT - 1; ++d) {
+                        gq_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        gk_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
 #pragma unroll
-                for (int p = 0; p < KB; ++p) {
-                    float qf[8], kf[8], ki[8], v2[8], v3[8];
+                    for (int p = 0; p < KB; ++p) {
+                        float qf[8], kf[8], ki[8], v2[8], v3[8];
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int blk = 2 * p + hh;
-                        const int ch = 16 * blk + 4 * gq;
-                        f32x4 Dt[NT];
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int blk = 2 * p + hh;
+                            const int ch = 16 * blk + 4 * gq;
+                            f32x4 Dt[NT];
 #pragma unroll
-                        for (int t = 0; t < NT; ++t) Dt[t] = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
-                        // whole-tile decay before and after tile m (m is uniform per
-                        // wave), and across the tiles strictly between tile m and the
-                        // tiles m - 2, m - 3
-                        f32x4 before, after, Dm, w2, w3;
-                        const f32x4 one = {1.f, 1.f, 1.f, 1.f};
-                        switch (m) {
-                        case 0: before = one; Dm = Dt[0]; after = Dt[1] * Dt[2] * Dt[3]; w2 = one; w3 = one; break;
-                        case 1: before = Dt[0]; Dm = Dt[1]; after = Dt[2] * Dt[3]; w2 = one; w3 = one; break;
-                        case 2: before = Dt[0] * Dt[1]; Dm = Dt[2]; after = Dt[3]; w2 = Dt[1]; w3 = one; break;
-                        default: before = Dt[0] * Dt[1] * Dt[2]; Dm = Dt[3]; after = one; w2 = Dt[2]; w3 = Dt[2] * Dt[1]; break;
+                            for (int t = 0; t < NT; ++t) Dt[t] = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
+                            // whole-tile decay before tile M, from its start to the chunk
+                            // end, and across the tiles strictly between M and M - 2, M - 3
+                            f32x4 before = {1.f, 1.f, 1.f, 1.f}, dma = Dt[M], w2 = before, w3 = before;
+#pragma unroll
+                            for (int t = 0; t < M; ++t) before = t ? before * Dt[t] : Dt[t];
+#pragma unroll
+                            for (int t = M + 1; t < NT; ++t) dma = dma * Dt[t];
+                            if constexpr (M >= 2) w2 = Dt[M - 1];
+                            if constexpr (M >= 3) w3 = Dt[M - 1] * Dt[M - 2];
+                            if constexpr (M == 0)
+                                if (r == 0) *reinterpret_cast<f32x4 *>(&st.GamC[ch]) = dma;
+                            float qv[4], kv[4];
+                            in.q[blk].to_f32(qv);
+                            in.k[blk].to_f32(kv);
+                            f32x4 qt, kt, kb;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float fq = qv[i] * f[blk][i], fk = kv[i] * f[blk][i];
+                                const float ik = kv[i] * fast_rcp(f[blk][i]);   // 1/f-scaled key, <= e^80 |k|
+                                qf[4 * hh + i] = fq;
+                                kf[4 * hh + i] = fk;
+                                ki[4 * hh + i] = ik;
+                                v2[4 * hh + i] = w2[i];
+                                v3[4 * hh + i] = w3[i];
+                                qt[i] = M ? fq * before[i] : fq;
+                                kt[i] = M ? fk * before[i] : fk;
+                                kb[i] = ik * dma[i];   // decayed to the chunk end, <= |k|
+                            }
+                            const int row = (TILE * M + r) * LDK + ch;
+                            *reinterpret_cast<f16x4 *>(&st.Qt[row]) = h16::pack4(qt);
+                            *reinterpret_cast<f16x4 *>(&st.Kt[row]) = h16::pack4(kt);
+                            *reinterpret_cast<f16x4 *>(&st.Kb[(TILE * M + r) * LDKB + ch]) = h16::pack4(kb);
                         }
-                        const f32x4 dma = Dm * after;   // from the tile start to the chunk end
-                        if (m == 0 && r == 0) *reinterpret_cast<f32x4 *>(&st.GamC[ch]) = dma;
-                        float qv[4], kv[4];
-                        in.q[blk].to_f32(qv);
-                        in.k[blk].to_f32(kv);
-                        f32x4 qt, kt, kb;
+
+                        if constexpr (M < NT - 1) diagonal(qf, kf, ki);
+                        // tiles n = M - d to the left: fp16, B = K-hat of tile n
+                        const int kh_off = r * LDK + 32 * p + 4 * gq;
+                        if constexpr (M >= 1) {
+                            const f16x8 bk = h16::lds4x2(&sm.Kh[M - 1][kh_off], &sm.Kh[M - 1][kh_off + 16]);
+                            gq_o[0] = h16::mma32(h16::pack8(qf), bk, gq_o[0]);
+                            gk_o[0] = h16::mma32(h16::pack8(kf), bk, gk_o[0]);
+                        }
+                        if constexpr (M >= 2) {
+                            const f16x8 bk = h16::lds4x2(&sm.Kh[M - 2][kh_off], &sm.Kh[M - 2][kh_off + 16]);
+                            float a[8], e[8];
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v2[i]; e[i] = kf[i] * v2[i]; }
+                            gq_o[1] = h16::mma32(h16::pack8(a), bk, gq_o[1]);
+                            gk_o[1] = h16::mma32(h16::pack8(e), bk, gk_o[1]);
+                        }
+                        if constexpr (M >= 3) {
+                            const f16x8 bk = h16::lds4x2(&sm.Kh[M - 3][kh_off], &sm.Kh[M - 3][kh_off + 16]);
+                            float a[8], e[8];
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v3[i]; e[i] = kf[i] * v3[i]; }
+                            gq_o[2] = h16::mma32(h16::pack8(a), bk, gq_o[2]);
+                            gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
+                        }
+                    }
+
+                    // q and k of chunk cn are consumed: fetch the next chunk's
+                    load_qk(cnext, r, gq);
+                    lds_wave_sync();
+
+                    // ------------------------------------------ Gram results of block row M
+                    const f32x4 bet = *reinterpret_cast<const f32x4 *>(&sm.betas[cn % 3][TILE * M + 4 * gq]);
+                    {
+                        f32x4 aq, ak;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float fq = qv[i] * f[blk][i], fk = kv[i] * f[blk][i];
-                            const float ik = kv[i] * fast_rcp(f[blk][i]);   // 1/f-scaled key, <= e^80 |k|
-                            qf[4 * hh + i] = fq;
-                            kf[4 * hh + i] = fk;
-                            ki[4 * hh + i] = ik;
-                            v2[4 * hh + i] = w2[i];
-                            v3[4 * hh + i] = w3[i];
-                            qt[i] = fq * before[i];
-                            kt[i] = fk * before[i];
-                            kb[i] = ik * dma[i];   // decayed to the chunk end, <= |k|
+                            const int row = 4 * gq + i;   // row t inside the tile; the column s is r
+                            aq[i] = (r > row) ? 0.f : gq_d[i];             // keep s <= t
+                            ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
                         }
-                        const int row = (TILE * m + r) * LDK + ch;
-                        *reinterpret_cast<f16x4 *>(&st.Qt[row]) = h16::pack4(qt);
-                        *reinterpret_cast<f16x4 *>(&st.Kt[row]) = h16::pack4(kt);
-                        *reinterpret_cast<f16x4 *>(&st.Kb[(TILE * m + r) * LDKB + ch]) = h16::pack4(kb);
+                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, M)][r * LDT + 4 * gq]) = h16::pack4(aq);
+                        *reinterpret_cast<f32x4 *>(&sm.LdT[M][r][4 * gq]) = ak;
                     }
-
-                    if (m < NT - 1) diagonal(qf, kf, ki);
-                    // tiles n = m - d to the left: fp16, B = K-hat of tile n
-                    const int kh_off = r * LDK + 32 * p + 4 * gq;
-                    if (m >= 1) {
-                        const f16x8 bk = h16::lds4x2(&sm.Kh[m - 1][kh_off], &sm.Kh[m - 1][kh_off + 16]);
-                        gq_o[0] = h16::mma32(h16::pack8(qf), bk, gq_o[0]);
-                        gk_o[0] = h16::mma32(h16::pack8(kf), bk, gk_o[0]);
-                    }
-                    if (m >= 2) {
-                        const f16x8 bk = h16::lds4x2(&sm.Kh[m - 2][kh_off], &sm.Kh[m - 2][kh_off + 16]);
-                        float a[8], e[8];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v2[i]; e[i] = kf[i] * v2[i]; }
-                        gq_o[1] = h16::mma32(h16::pack8(a), bk, gq_o[1]);
-                        gk_o[1] = h16::mma32(h16::pack8(e), bk, gk_o[1]);
-                    }
-                    if (m >= 3) {
-                        const f16x8 bk = h16::lds4x2(&sm.Kh[m - 3][kh_off], &sm.Kh[m - 3][kh_off + 16]);
-                        float a[8], e[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v3[i]; e[i] = kf[i] * v3[i]; }
-                        gq_o[2] = h16::mma32(h16::pack8(a), bk, gq_o[2]);
-                        gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
-                    }
-                }
-
-                // q and k of chunk cn are consumed: fetch the next chunk's
-                load_qk(cnext, r, gq);
-                lds_wave_sync();
-
-                // ---------------------------------------------- Gram results of block row m
-                const f32x4 bet = *reinterpret_cast<const f32x4 *>(&sm.betas[cn % 3][TILE * m + 4 * gq]);
-                {
-                    f32x4 aq, ak;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 4 * gq + i;   // row t inside the tile; the column s is r
-                        aq[i] = (r > row) ? 0.f : gq_d[i];             // keep s <= t
-                        ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
-                    }
-                    *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, m)][r * LDT + 4 * gq]) = h16::pack4(aq);
-                    *reinterpret_cast<f32x4 *>(&sm.LdT[m][r][4 * gq]) = ak;
-                }
-#pragma unroll
-                for (int d = 1; d < NT; ++d) {
-                    if (m >= d) {
-                        const int n = m - d;
-                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(m, n)][r * LDT + 4 * gq]) =
+                    for (int d = 1; d <= M; ++d) {
+                        const int n = M - d;
+                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, n)][r * LDT + 4 * gq]) =
                             h16::pack4(gq_o[d - 1]);
-                        *reinterpret_cast<f16x4 *>(&st.LT[strict_index(m, n)][r * LDT + 4 * gq]) =
+                        *reinterpret_cast<f16x4 *>(&st.LT[strict_index(M, n)][r * LDT + 4 * gq]) =
                             h16::pack4(gk_o[d - 1] * bet);
                     }
+                    lds_wave_sync();
+                };
+                static_assert(NT == 4, "one block_row instance per tile");
+                switch (m) {
+                case 0: block_row(TileIndex<0>{}); break;
+                case 1: block_row(TileIndex<1>{}); break;
+                case 2: block_row(TileIndex<2>{}); break;
+                default: block_row(TileIndex<3>{}); break;
                 }
-                lds_wave_sync();
 
                 // ------------------------------------------ (I + L_mm)^-1, lane column r
                 {
