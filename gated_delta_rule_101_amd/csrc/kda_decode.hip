@@ -50,7 +50,7 @@ kda_decode_kernel(const typename Store<QBF>::type *__restrict__ q,
     __shared__ f32x4 s_p[NRG][NCG], s_r[NRG][NCG];
     __shared__ float s_qk[NRG];
 
-    const int bh = blockIdx.x;
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);   // one state per workgroup
     const int cg = threadIdx.x % NCG;
     const int rg = threadIdx.x / NCG;
     f32x4 *Sp = reinterpret_cast<f32x4 *>(S + (size_t)bh * DK * DV);

@@ -375,6 +375,14 @@ __device__ __forceinline__ float gate_from_logit(float z, float s) {
 }
 
 // Logistic sigmoid; for very negative x the exp overflows and rcp(inf) = 0.
+// Workgroups are dealt to the 8 XCDs round robin (block i runs on XCD i mod 8).
+// For a streaming kernel with one workgroup per item, map block i to item
+// (i mod 8) n/8 + i/8, so that each XCD walks a contiguous range of the n items
+// (a bijection when n is a multiple of 8; otherwise blocks keep their index).
+__device__ __forceinline__ int xcd_contiguous(int block, int n) {
+    return (n & 7) ? block : (block & 7) * (n >> 3) + (block >> 3);
+}
+
 __device__ __forceinline__ float sigmoid_f32(float x) {
     constexpr float LOG2E_ = 1.4426950408889634f;
     return fast_rcp(1.0f + fast_exp2(-x * LOG2E_));

@@ -55,7 +55,7 @@ kda_spec_kernel(const typename Store<QBF>::type *__restrict__ q,
     __shared__ f32x4 s_p[2][NRG][NCG], s_r[2][NRG][NCG];
     __shared__ float s_qk[2][NRG];
 
-    const int bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x), b = bh / H, h = bh % H;   // one state per workgroup
     const int cg = threadIdx.x % NCG;
     const int rg = threadIdx.x / NCG;
     f32x4 *Sp = reinterpret_cast<f32x4 *>(S + (size_t)bh * DK * DV);

@@ -84,7 +84,7 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
             }
     };
 
-    const int bh = blockIdx.x;
+    const int bh = xcd_contiguous(blockIdx.x, gridDim.x);   // one state per workgroup
     load_state(bh);
     {
         const int b = bh / H, h = bh % H;
