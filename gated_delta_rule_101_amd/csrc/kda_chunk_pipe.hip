@@ -92,7 +92,10 @@ struct alignas(16) PipeSmem {
     Stage stage[2];
     // Producer scratch.
     alignas(16) _Float16 Kh[NT - 1][TILE * LDK];   // keys of tiles 0..2 decayed to their tile end
-    alignas(16) float D[NT][DK];                // total decay of each tile
+    // total decay of each tile; rows 64 bytes longer than DK floats so that
+    // the four rows a lane row gathers from (same channel) fall in distinct banks
+    static constexpr int LDD = DK + 16;
+    alignas(16) float D[NT][LDD];
     // beta of chunks c, c + 1, c + 2 (slot = chunk mod 3): written by a consumer
     // two iterations ahead, read by the producers one iteration ahead.
     alignas(16) float betas[3][C];
@@ -349,9 +352,10 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         for (int hh = 0; hh < 2; ++hh) {
                             const int blk = 2 * p + hh;
                             const int ch = 16 * blk + 4 * gq;
+                            // the four tiles' totals of these 4 channels: one LDS
+                            // read per lane, shared across the lane's row
                             f32x4 Dt[NT];
-#pragma unroll
-                            for (int t = 0; t < NT; ++t) Dt[t] = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
+                            row_gather16(sm.D[r >> 2][ch + (r & 3)], Dt);
                             // whole-tile decay before tile M, from its start to the chunk
                             // end, and across the tiles strictly between M and M - 2, M - 3
                             f32x4 before = {1.f, 1.f, 1.f, 1.f}, dma = Dt[M], w2 = before, w3 = before;
@@ -535,7 +539,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 for (int j = 0; j < KB; ++j) Sh[j] = h16::pack8(S[2 * j], S[2 * j + 1]);
 
                 // (Gamma.Q) S and X = V - (Gamma.K) S, scaled by beta
-                f32x4 accQ[NT], Y[NT];
+                f32x4 accQ[NT], Y[NT], bts[NT];
+                row_gather16(sm.betas[c % 3][TILE * (r >> 2) + 4 * gq + (r & 3)], bts);
 #pragma unroll
                 for (int mm = 0; mm < NT; ++mm) {
                     f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
@@ -547,9 +552,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         aK = h16::mma32(h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]), Sh[j], aK);
                     }
                     accQ[mm] = aQ;
-                    const f32x4 bt = *reinterpret_cast<const f32x4 *>(&sm.betas[c % 3][TILE * mm + 4 * gq]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) Y[mm][i] = bt[i] * (to_f32(vin[mm][i]) - aK[i]);
+                    for (int i = 0; i < 4; ++i) Y[mm][i] = bts[mm][i] * (to_f32(vin[mm][i]) - aK[i]);
                 }
                 if (w == 0 && c + 2 < nchunks) sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
 
@@ -596,10 +600,14 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 h16::split8(U[0], U[1], Ubh[0], Ubl[0]);
                 h16::split8(U[2], U[3], Ubh[1], Ubl[1]);
                 const int tk = h16::tr_offset(lane, LDKB);
+                // total decay of the chunk for rows 16kt + 4gq + (0..3), four row
+                // tiles per LDS read (one value per lane, shared across the row)
+                static_assert(KT % 4 == 0, "row tiles of the state come in fours");
+                f32x4 gam[4];
 #pragma unroll
                 for (int kt = 0; kt < KT; ++kt) {
-                    const f32x4 gcv = *reinterpret_cast<const f32x4 *>(&st.GamC[16 * kt + 4 * gq]);
-                    f32x4 acc = S[kt] * gcv;
+                    if (kt % 4 == 0) row_gather16(st.GamC[16 * (kt + (r >> 2)) + 4 * gq + (r & 3)], gam);
+                    f32x4 acc = S[kt] * gam[kt % 4];
 #pragma unroll
                     for (int j2 = 0; j2 < 2; ++j2) {
                         const _Float16 *base = &st.Kb[(32 * j2) * LDKB + 16 * kt + tk];

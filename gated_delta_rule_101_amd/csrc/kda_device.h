@@ -320,6 +320,24 @@ __device__ __forceinline__ float row_shr(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + N, 0xF, 0xF, false));
 }
 
+// Every lane of each 16-lane row receives lane N's value of that row (DPP
+// row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, true));
+}
+
+// Sixteen per-row values, one read per lane: lane i of a row holds element i
+// (x = src[i]); afterwards every lane of the row holds all sixteen as four
+// 4-vectors, out[j][e] = element 4j + e.  Replaces sixteen-lane-redundant
+// 16-byte LDS reads by one 4-byte read and sixteen DPP broadcasts.
+__device__ __forceinline__ void row_gather16(float x, f32x4 (&out)[4]) {
+    out[0] = f32x4{row_bcast<0>(x), row_bcast<1>(x), row_bcast<2>(x), row_bcast<3>(x)};
+    out[1] = f32x4{row_bcast<4>(x), row_bcast<5>(x), row_bcast<6>(x), row_bcast<7>(x)};
+    out[2] = f32x4{row_bcast<8>(x), row_bcast<9>(x), row_bcast<10>(x), row_bcast<11>(x)};
+    out[3] = f32x4{row_bcast<12>(x), row_bcast<13>(x), row_bcast<14>(x), row_bcast<15>(x)};
+}
+
 // Inclusive prefix sum over the 16 lanes of each DPP row.
 __device__ __forceinline__ float row_inclusive_scan(float x) {
     x += row_shr<1>(x);
