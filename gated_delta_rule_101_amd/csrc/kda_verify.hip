@@ -17,8 +17,11 @@
 // [w dv/4, (w+1) dv/4) and streams its dk x dv/4 slice of S from HBM straight
 // into matrix-core B operands (lane (kq, r16) reads dv/64 consecutive floats
 // of row 16 kb + 4 kq + i: 16 lanes cover one contiguous row segment), so S
-// never passes through LDS and the state is read exactly once.  float32
-// operands throughout (v_mfma_f32_16x16x4_f32).
+// never passes through LDS and the state is read exactly once.  For
+// bfloat16 drafts the two state products take fp16 operands
+// (v_mfma_f32_16x16x32_f16; the state must stay below the fp16 limit 65504,
+// as in the bfloat16 chunk kernel); everything else, and the whole float32
+// draft path, uses float32 operands (v_mfma_f32_16x16x4_f32).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -100,14 +103,34 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         }
         // drafts: raw q, k, g into LDS by the whole workgroup (g parked in sKh),
         // then the cumsum of g down each key channel and the scaled rows
+        static_assert(KT * DK % (4 * NTH) == 0, "whole 4-channel groups per thread");
+        // 4 consecutive channels per thread and load (8 or 16 bytes; rows are
+        // 16-byte aligned and DK is a multiple of 4); fixed count, so all
+        // loads issue first
 #pragma unroll
-        for (int it = 0; it < KT * DK / NTH; ++it) {   // fixed count: all loads issue first
-            const int e = tid + NTH * it, t = e / DK, x = e % DK;
+        for (int it = 0; it < KT * DK / (4 * NTH); ++it) {
+            const int e = tid + NTH * it, t = e / (DK / 4), x = 4 * (e % (DK / 4));
             const bool live = t < K;
             const size_t i = row(live ? t : 0) * DK + x;
-            sQt[t][x] = ld_live(q, i, live);
-            sKt[t][x] = ld_live(k, i, live);
-            sKh[t][x] = ld_live(g, i, live);
+            Raw4<QT> rq, rk;
+            Raw4<GT> rg;
+            rq.load(q + i);
+            rk.load(k + i);
+            rg.load(g + i);
+            float fq[4], fk[4], fg[4];
+            rq.to_f32(fq);
+            rk.to_f32(fk);
+            rg.to_f32(fg);
+            f32x4 vq, vk, vg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                vq[j] = live ? fq[j] : 0.f;
+                vk[j] = live ? fk[j] : 0.f;
+                vg[j] = live ? fg[j] : 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(&sQt[t][x]) = vq;
+            *reinterpret_cast<f32x4 *>(&sKt[t][x]) = vk;
+            *reinterpret_cast<f32x4 *>(&sKh[t][x]) = vg;
         }
         if (tid < KT) sbeta[tid] = ld_live(beta, row(tid < K ? tid : K - 1), tid < K);
         __syncthreads();
@@ -130,18 +153,41 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         f32x4 aq[NC], ak[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) aq[c] = ak[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (sizeof(QT) == 2) {
+            // bfloat16 drafts: fp16 operands (Q~, K~ <= |q|, |k|; the state
+            // below the fp16 limit), 16x16x32 products.  k-items of block pair
+            // p: key channels 32p + 4kq + (0..3) and 32p + 16 + 4kq + (0..3),
+            // which are exactly this lane's state rows of blocks 2p and 2p + 1.
 #pragma unroll
-        for (int kb = 0; kb < DK / 16; ++kb) {
-            const int x = 16 * kb + 4 * kq;
-            const f32x4 qa = *reinterpret_cast<const f32x4 *>(&sQt[r16][x]);
-            const f32x4 ka = *reinterpret_cast<const f32x4 *>(&sKt[r16][x]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int p = 0; p < DK / 32; ++p) {
+                const int x = 32 * p + 4 * kq;
+                const f16x8 qa = h16::pack8(*reinterpret_cast<const f32x4 *>(&sQt[r16][x]),
+                                                 *reinterpret_cast<const f32x4 *>(&sQt[r16][x + 16]));
+                const f16x8 ka = h16::pack8(*reinterpret_cast<const f32x4 *>(&sKt[r16][x]),
+                                                 *reinterpret_cast<const f32x4 *>(&sKt[r16][x + 16]));
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    aq[c] = mma(qa[i], sv[kb][i][c], aq[c]);
-                    ak[c] = mma(ka[i], sv[kb][i][c], ak[c]);
+                    const f16x8 sb = h16::pack8(f32x4{sv[2 * p][0][c], sv[2 * p][1][c], sv[2 * p][2][c], sv[2 * p][3][c]},
+                                                     f32x4{sv[2 * p + 1][0][c], sv[2 * p + 1][1][c],
+                                                           sv[2 * p + 1][2][c], sv[2 * p + 1][3][c]});
+                    aq[c] = h16::mma32(qa, sb, aq[c]);
+                    ak[c] = h16::mma32(ka, sb, ak[c]);
                 }
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; ++kb) {
+                const int x = 16 * kb + 4 * kq;
+                const f32x4 qa = *reinterpret_cast<const f32x4 *>(&sQt[r16][x]);
+                const f32x4 ka = *reinterpret_cast<const f32x4 *>(&sKt[r16][x]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) {
+                        aq[c] = mma(qa[i], sv[kb][i][c], aq[c]);
+                        ak[c] = mma(ka[i], sv[kb][i][c], ak[c]);
+                    }
+            }
         }
         // aq[c], ak[c]: lane (kq, r16) holds draft rows 4 kq + i of column col0 + c.
         // X = V - K~ S to LDS (the B operand of the solve below).
@@ -171,14 +217,17 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         }
         __syncthreads();
         if (tid < KT) {   // column tid of N = (I + Diag(beta) A_kk0)^-1
+            // forward substitution by columns: once x_l is final, every later
+            // row takes its term at once (a dependent chain of KT steps)
             const int j = tid;
             float xs[KT];
 #pragma unroll
-            for (int i = 0; i < KT; ++i) {
-                float s = i == j ? 1.f : 0.f;
+            for (int i = 0; i < KT; ++i) xs[i] = i == j ? 1.f : 0.f;
 #pragma unroll
-                for (int l = 0; l < i; ++l) s -= sbeta[i] * sL[i][l] * xs[l];
-                xs[i] = s;
+            for (int l = 0; l < KT - 1; ++l) {
+                const float nx = -xs[l];
+#pragma unroll
+                for (int i = l + 1; i < KT; ++i) xs[i] += (sbeta[i] * sL[i][l]) * nx;
             }
 #pragma unroll
             for (int i = 0; i < KT; ++i) sN[i][j] = xs[i];
