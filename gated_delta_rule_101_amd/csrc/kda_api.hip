@@ -228,7 +228,10 @@ kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const 
     if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // the token-loop kernel
         kda::SpecArgs a = spec_args(nullptr, k, v, g, beta, S, B, K, H, dk, dv, qkv_dtype, gate_dtype, KDA_F32);
         a.accepted = accepted;
-        return kda::launch_spec_step(a, (hipStream_t)stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+        // up to 16 drafts: one tile on the matrix cores; more: the token loop
+        const hipError_t e = K <= 16 ? kda::launch_verify_tile(a, (hipStream_t)stream)
+                                     : kda::launch_spec_step(a, (hipStream_t)stream);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
     }
     // the chunk kernels read a query row for every token; the keys stand in (no output is written)
     kda::ChunkFwdArgs a = chunk_args(k, k, v, g, beta, S, nullptr, S, B, K, H, dk, dv,

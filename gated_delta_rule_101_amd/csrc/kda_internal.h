@@ -78,7 +78,7 @@ hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        /
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_spec_step(const SpecArgs &a, hipStream_t stream);           // dk, dv in {64, 128}
-hipError_t launch_verify_tile(const SpecArgs &a, hipStream_t stream);         // verify, K <= 16
+hipError_t launch_verify_tile(const SpecArgs &a, hipStream_t stream);         // K <= 16: verify, or commit if accepted is set
 hipError_t launch_output_gate(const OutputGateArgs &a, hipStream_t stream);
 hipError_t launch_chunk_bwd(const ChunkBwdArgs &a, hipStream_t stream);       // dk, dv in {64, 128}
 size_t chunk_bwd_workspace_floats(int B, int T, int H, int dk, int dv);

@@ -48,11 +48,12 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int DK, int DV, typename QT, typename GT, typename OT>
-__global__ void __launch_bounds__(NTH)
+// At most 168 VGPRs, so three workgroups share a CU.
+template <int DK, int DV, typename QT, typename GT, typename OT, bool COMMIT>
+__global__ void __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(3)))
 kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT *__restrict__ v,
-                       const GT *__restrict__ g, const GT *__restrict__ beta, const float *__restrict__ S,
-                       OT *__restrict__ o, int K, int H)
+                       const GT *__restrict__ g, const GT *__restrict__ beta, float *__restrict__ S,
+                       OT *__restrict__ o, const int *__restrict__ accepted, int K, int H)
 {
     constexpr int CW = DV / 4;      // value columns per wave
     constexpr int NC = CW / 16;     // columns per lane (1 or 2)
@@ -61,6 +62,11 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
     __shared__ alignas(16) float sX[KT][LV];    // V - K~ S, then U
     __shared__ float sA[KT][KT + 4], sL[KT][KT + 4], sN[KT][KT + 4];
     __shared__ float sbeta[KT];
+    __shared__ float sGam[DK];   // commit: decay of the whole accepted prefix, per key channel
+    // commit: K-bar^T (keys decayed to the end of the accepted prefix), channel-major,
+    // in the storage of the queries, which commit does not read
+    static_assert(DK * KT <= KT * LK, "K-bar^T fits where the queries would go");
+    float(*sKbT)[KT] = reinterpret_cast<float(*)[KT]>(&sQt[0][0]);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
@@ -91,6 +97,9 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
     load_state(bh);
     {
         const int b = bh / H, h = bh % H;
+        // drafts applied: all K (verify), the accepted prefix (commit); the
+        // others enter as identity tokens (zero key, value, decay and beta)
+        const int n = COMMIT ? max(0, min(accepted[b], K)) : K;
         auto row = [&](int t) { return ((size_t)b * K + t) * H + h; };   // draft token t of (b, h)
 
         // this lane's draft values for X = V - K~ S (C layout: drafts 4 kq + i)
@@ -99,7 +108,7 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * kq + i;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) vv[i][c] = ld_live(v, row(t < K ? t : K - 1) * DV + col0 + c, t < K);
+            for (int c = 0; c < NC; ++c) vv[i][c] = ld_live(v, row(t < K ? t : K - 1) * DV + col0 + c, t < n);
         }
         // drafts: raw q, k, g into LDS by the whole workgroup (g parked in sKh),
         // then the cumsum of g down each key channel and the scaled rows
@@ -110,11 +119,12 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
 #pragma unroll
         for (int it = 0; it < KT * DK / (4 * NTH); ++it) {
             const int e = tid + NTH * it, t = e / (DK / 4), x = 4 * (e % (DK / 4));
-            const bool live = t < K;
-            const size_t i = row(live ? t : 0) * DK + x;
+            const bool live = t < n;
+            const size_t i = row(t < K ? t : 0) * DK + x;
             Raw4<QT> rq, rk;
             Raw4<GT> rg;
-            rq.load(q + i);
+            if constexpr (!COMMIT) rq.load(q + i);
+            else rq.zero();
             rk.load(k + i);
             rg.load(g + i);
             float fq[4], fk[4], fg[4];
@@ -128,11 +138,11 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
                 vk[j] = live ? fk[j] : 0.f;
                 vg[j] = live ? fg[j] : 0.f;
             }
-            *reinterpret_cast<f32x4 *>(&sQt[t][x]) = vq;
+            if constexpr (!COMMIT) *reinterpret_cast<f32x4 *>(&sQt[t][x]) = vq;
             *reinterpret_cast<f32x4 *>(&sKt[t][x]) = vk;
             *reinterpret_cast<f32x4 *>(&sKh[t][x]) = vg;
         }
-        if (tid < KT) sbeta[tid] = ld_live(beta, row(tid < K ? tid : K - 1), tid < K);
+        if (tid < KT) sbeta[tid] = ld_live(beta, row(tid < K ? tid : K - 1), tid < n);
         __syncthreads();
         if (tid < DK) {
             const int x = tid;
@@ -142,9 +152,16 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
                 acc += sKh[t][x];
                 const float e = __builtin_amdgcn_exp2f(acc * LOG2E), ei = __builtin_amdgcn_exp2f(-acc * LOG2E);
                 const float kv = sKt[t][x];
-                sQt[t][x] *= e;
+                if constexpr (!COMMIT) sQt[t][x] *= e;
                 sKt[t][x] = kv * e;
                 sKh[t][x] = kv * ei;
+            }
+            if constexpr (COMMIT) {
+                // acc is the log-decay of the whole prefix (identity tokens add 0)
+                const float ge = __builtin_amdgcn_exp2f(acc * LOG2E);
+                sGam[x] = ge;
+#pragma unroll
+                for (int t = 0; t < KT; ++t) sKbT[x][t] = sKh[t][x] * ge;   // k e^{b_end - b_t} <= |k|
             }
         }
         __syncthreads();
@@ -155,7 +172,8 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         for (int c = 0; c < NC; ++c) aq[c] = ak[c] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (sizeof(QT) == 2) {
             // bfloat16 drafts: fp16 operands (Q~, K~ <= |q|, |k|; the state
-            // below the fp16 limit), 16x16x32 products.  k-items of block pair
+            // below the fp16 limit), 16x16x32 products; single terms for
+            // verify's outputs, two-term for the state commit keeps.  k-items of block pair
             // p: key channels 32p + 4kq + (0..3) and 32p + 16 + 4kq + (0..3),
             // which are exactly this lane's state rows of blocks 2p and 2p + 1.
 #pragma unroll
@@ -163,15 +181,26 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
                 const int x = 32 * p + 4 * kq;
                 const f16x8 qa = h16::pack8(*reinterpret_cast<const f32x4 *>(&sQt[r16][x]),
                                                  *reinterpret_cast<const f32x4 *>(&sQt[r16][x + 16]));
-                const f16x8 ka = h16::pack8(*reinterpret_cast<const f32x4 *>(&sKt[r16][x]),
-                                                 *reinterpret_cast<const f32x4 *>(&sKt[r16][x + 16]));
+                const f32x4 k0 = *reinterpret_cast<const f32x4 *>(&sKt[r16][x]);
+                const f32x4 k1 = *reinterpret_cast<const f32x4 *>(&sKt[r16][x + 16]);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const f16x8 sb = h16::pack8(f32x4{sv[2 * p][0][c], sv[2 * p][1][c], sv[2 * p][2][c], sv[2 * p][3][c]},
-                                                     f32x4{sv[2 * p + 1][0][c], sv[2 * p + 1][1][c],
-                                                           sv[2 * p + 1][2][c], sv[2 * p + 1][3][c]});
-                    aq[c] = h16::mma32(qa, sb, aq[c]);
-                    ak[c] = h16::mma32(ka, sb, ak[c]);
+                    const f32x4 s0 = {sv[2 * p][0][c], sv[2 * p][1][c], sv[2 * p][2][c], sv[2 * p][3][c]};
+                    const f32x4 s1 = {sv[2 * p + 1][0][c], sv[2 * p + 1][1][c], sv[2 * p + 1][2][c], sv[2 * p + 1][3][c]};
+                    if constexpr (!COMMIT) {
+                        const f16x8 sb = h16::pack8(s0, s1);
+                        aq[c] = h16::mma32(qa, sb, aq[c]);
+                        ak[c] = h16::mma32(h16::pack8(k0, k1), sb, ak[c]);
+                    } else {
+                        // the committed state persists: two-term fp16 on both
+                        // sides (about 22 significant bits), three products
+                        f16x8 kh, kl, sh, sl;
+                        h16::split8(k0, k1, kh, kl);
+                        h16::split8(s0, s1, sh, sl);
+                        ak[c] = h16::mma32(kh, sh, ak[c]);
+                        ak[c] = h16::mma32(kh, sl, ak[c]);
+                        ak[c] = h16::mma32(kl, sh, ak[c]);
+                    }
                 }
             }
         } else {
@@ -184,7 +213,7 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int c = 0; c < NC; ++c) {
-                        aq[c] = mma(qa[i], sv[kb][i][c], aq[c]);
+                        if constexpr (!COMMIT) aq[c] = mma(qa[i], sv[kb][i][c], aq[c]);
                         ak[c] = mma(ka[i], sv[kb][i][c], ak[c]);
                     }
             }
@@ -195,8 +224,8 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int c = 0; c < NC; ++c) sX[4 * kq + i][col0 + c] = vv[i][c] - ak[c][i];
-        // Gram tiles: wave 0 A_qk = tril(Q~ K^T), wave 1 A_kk0 = strict_tril(K~ K^T)
-        if (wave < 2) {
+        // Gram tiles: wave 0 A_qk = tril(Q~ K^T) (verify only), wave 1 A_kk0 = strict_tril(K~ K^T)
+        if (COMMIT ? wave == 1 : wave < 2) {
             const float(*L)[LK] = wave == 0 ? sQt : sKt;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -245,38 +274,86 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
 #pragma unroll
             for (int c = 0; c < NC; ++c) au[c] = mma(a, sX[s][col0 + c], au[c]);
         }
-        __syncthreads();   // every wave has read its X before U overwrites it
+        if constexpr (COMMIT) {
+            // S' = Diag(Gamma_end) S + K-bar^T U, accumulated in the registers
+            // that hold S: output tile (channel block kb, column tile c) has lane
+            // (kq, r16) on channels 16 kb + 4 kq + i of column tile c's column
+            // r16, which is sv[kb][i][c].  The k-items are the drafts 4 kq +
+            // (0..3), as U's accumulator layout gives them, so au[c] is the B
+            // operand as it stands; A is read from K-bar^T's rows.
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int kb = 0; kb < DK / 16; ++kb) {
+                const f32x4 gam = *reinterpret_cast<const f32x4 *>(&sGam[16 * kb + 4 * kq]);
+                const f32x4 kbt = *reinterpret_cast<const f32x4 *>(&sKbT[16 * kb + r16][4 * kq]);
 #pragma unroll
-            for (int c = 0; c < NC; ++c) sX[4 * kq + i][col0 + c] = au[c][i];
-        __syncthreads();
-        // O = Q~ S + A_qk U, accumulated onto aq
+                for (int c = 0; c < NC; ++c) {
+                    f32x4 acc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 4 * kq + i;
-            const float a = sA[r16][s];
+                    for (int i = 0; i < 4; ++i) acc[i] = gam[i] * sv[kb][i][c];
+                    if constexpr (sizeof(QT) == 2) {
+                        // two-term fp16 K-bar (<= |k|) and U, three products
+                        f16x4 kh, kl, uh, ul;
+                        h16::split4(kbt, kh, kl);
+                        h16::split4(au[c], uh, ul);
+                        acc = h16::mma16(kh, uh, acc);
+                        acc = h16::mma16(kh, ul, acc);
+                        acc = h16::mma16(kl, uh, acc);
+                    } else {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) aq[c] = mma(a, sX[s][col0 + c], aq[c]);
-        }
+                        for (int i = 0; i < 4; ++i) acc = mma(kbt[i], au[c][i], acc);
+                    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * kq + i;
-            if (t < K) {
-                OT *op = o + row(t) * DV + col0;
+                    for (int i = 0; i < 4; ++i) sv[kb][i][c] = acc[i];
+                }
+            }
+            // written back where it was read; no accepted draft leaves S untouched
+            if (n > 0) {
+                float *Sp = S + (size_t)bh * DK * DV;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) op[c] = from_f32<OT>(aq[c][i]);
+                for (int kb = 0; kb < DK / 16; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float *p = Sp + (size_t)(16 * kb + 4 * kq + i) * DV + col0;
+                        if constexpr (NC == 2)
+                            __builtin_nontemporal_store(f32x2{sv[kb][i][0], sv[kb][i][1]}, reinterpret_cast<f32x2 *>(p));
+                        else
+                            __builtin_nontemporal_store(sv[kb][i][0], p);
+                    }
+            }
+        } else {
+            __syncthreads();   // every wave has read its X before U overwrites it
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) sX[4 * kq + i][col0 + c] = au[c][i];
+            __syncthreads();
+            // O = Q~ S + A_qk U, accumulated onto aq
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s = 4 * kq + i;
+                const float a = sA[r16][s];
+#pragma unroll
+                for (int c = 0; c < NC; ++c) aq[c] = mma(a, sX[s][col0 + c], aq[c]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 4 * kq + i;
+                if (t < K) {
+                    OT *op = o + row(t) * DV + col0;
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) op[c] = from_f32<OT>(aq[c][i]);
+                }
             }
         }
     }
 }
 
-template <int DK, int DV, typename QT, typename GT, typename OT>
+template <int DK, int DV, typename QT, typename GT, typename OT, bool COMMIT>
 hipError_t launch(const SpecArgs &a, hipStream_t s)
 {
-    kda_verify_tile_kernel<DK, DV, QT, GT, OT><<<(unsigned)(a.B * a.H), NTH, 0, s>>>(
+    kda_verify_tile_kernel<DK, DV, QT, GT, OT, COMMIT><<<(unsigned)(a.B * a.H), NTH, 0, s>>>(
         (const QT *)a.q, (const QT *)a.k, (const QT *)a.v, (const GT *)a.g, (const GT *)a.beta, a.S, (OT *)a.o,
-        a.K, a.H);
+        a.accepted, a.K, a.H);
     return hipGetLastError();
 }
 
@@ -284,12 +361,19 @@ template <int DK, int DV>
 hipError_t dispatch(const SpecArgs &a, hipStream_t s)
 {
     typedef uint16_t b16;
-    if (a.qkv_bf16) {
-        if (a.gate_bf16) return a.out_bf16 ? launch<DK, DV, b16, b16, b16>(a, s) : launch<DK, DV, b16, b16, float>(a, s);
-        return a.out_bf16 ? launch<DK, DV, b16, float, b16>(a, s) : launch<DK, DV, b16, float, float>(a, s);
+    if (a.accepted) {   // commit: no outputs
+        if (a.qkv_bf16)
+            return a.gate_bf16 ? launch<DK, DV, b16, b16, float, true>(a, s) : launch<DK, DV, b16, float, float, true>(a, s);
+        return a.gate_bf16 ? launch<DK, DV, float, b16, float, true>(a, s) : launch<DK, DV, float, float, float, true>(a, s);
     }
-    if (a.gate_bf16) return a.out_bf16 ? launch<DK, DV, float, b16, b16>(a, s) : launch<DK, DV, float, b16, float>(a, s);
-    return a.out_bf16 ? launch<DK, DV, float, float, b16>(a, s) : launch<DK, DV, float, float, float>(a, s);
+    if (a.qkv_bf16) {
+        if (a.gate_bf16)
+            return a.out_bf16 ? launch<DK, DV, b16, b16, b16, false>(a, s) : launch<DK, DV, b16, b16, float, false>(a, s);
+        return a.out_bf16 ? launch<DK, DV, b16, float, b16, false>(a, s) : launch<DK, DV, b16, float, float, false>(a, s);
+    }
+    if (a.gate_bf16)
+        return a.out_bf16 ? launch<DK, DV, float, b16, b16, false>(a, s) : launch<DK, DV, float, b16, float, false>(a, s);
+    return a.out_bf16 ? launch<DK, DV, float, float, b16, false>(a, s) : launch<DK, DV, float, float, float, false>(a, s);
 }
 
 }  // namespace

@@ -187,7 +187,10 @@ kda_status_t kda_decode_step_gate(const void *q, const void *k, const void *v,
  *
  * Equivalent to kda_chunk_fwd(q, k, v, g, beta, S0 = S, o, S_final = NULL)
  * over T = K tokens; same sizes, dtypes and errors.  S must not be NULL and
- * must not overlap o.
+ * must not overlap o.  Up to 16 drafts run as one tile of the chunkwise form
+ * on the matrix cores; with KDA_BF16 drafts its two products with the state
+ * take single fp16 operands (so |S| must stay below 65504, as for
+ * kda_chunk_fwd), with KDA_F32 drafts float32 operands.
  */
 kda_status_t kda_verify_step(const void *q, const void *k, const void *v,
                              const void *g, const void *beta, const float *S, void *o,
@@ -206,7 +209,11 @@ kda_status_t kda_verify_step(const void *q, const void *k, const void *v,
  *
  * Afterwards S is the state kda_chunk_fwd would reach over the first
  * accepted[b] tokens of each sequence.  No output is written.  S must not
- * overlap k, v, g, beta or accepted.
+ * overlap k, v, g, beta or accepted.  A sequence with no accepted token
+ * keeps its state bit for bit.  Up to 16 drafts run as one tile on the
+ * matrix cores (S read once, updated in registers, written once); with
+ * KDA_BF16 drafts the products take two-term fp16 operands (about 22
+ * significant bits; |S| below 65504), with KDA_F32 drafts float32 operands.
  */
 kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const void *beta,
                              const int *accepted, float *S,
