@@ -209,14 +209,17 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
     gram_rows(std::integral_constant<int, 1>{});
     __syncthreads();
     if (tid < BC) {   // column tid of N = (I + Diag(beta) A_kk0)^-1 by forward substitution
+        // by columns: once x_l is final every later row takes its term at
+        // once, a dependent chain of BC steps instead of BC^2 / 2
         const int j = tid;
         float x[BC];
 #pragma unroll
-        for (int i = 0; i < BC; ++i) {
-            float s = i == j ? 1.f : 0.f;
+        for (int i = 0; i < BC; ++i) x[i] = i == j ? 1.f : 0.f;
 #pragma unroll
-            for (int l = 0; l < i; ++l) s -= sbeta[i] * sL[i][l] * x[l];
-            x[i] = s;
+        for (int l = 0; l < BC - 1; ++l) {
+            const float nx = -x[l];
+#pragma unroll
+            for (int i = l + 1; i < BC; ++i) x[i] += (sbeta[i] * sL[i][l]) * nx;
         }
 #pragma unroll
         for (int i = 0; i < BC; ++i) sN[i][j] = x[i];
