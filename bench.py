@@ -10,7 +10,9 @@ token carrying all H heads).  The decode path is timed on its own workload
 "decode" in GB/s.  Speculative decoding on the same states (verify 16 draft
 tokens, commit 8 of them) is reported under "speculative", the output
 epilogue (alone over the training-shape reads, and fused into decode) under
-"epilogue", the chunkwise backward under "backward".  Each carries a
+"epilogue", the chunkwise backward under "backward", and two secondary
+forward workloads (one head group B1 H8 T4096, a latency figure; the long
+sequence B1 H96 T131072) under "forward_secondary".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
 by HIP events on the launch stream.
 
@@ -180,6 +182,36 @@ def bench_fwd(kda, steps, warmup):
         "kernel_ms": round(ker * 1e3, 4),
     }
     return w, d, ms, tok_s, rf, extra
+
+
+def bench_fwd_secondary(kda, w, steps, warmup):
+    """Secondary forward workloads, timed like the headline one: the single
+    head group (B1 H8 T4096: eight sequential carries, a latency figure) and
+    the long single sequence (B1 H96 T131072: 2048 chunks per carry)."""
+    import torch
+    from kda_workloads import gen_torch
+    log(f"[bench] generating {w.name} on the device")
+    d = gen_torch.fwd_inputs(w)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o=o, S_final=Sf)
+
+    wall, ker = time_launches(step, steps, warmup, stream)
+    s_q, s_g = (2 if w.qkv == "bf16" else 4), (2 if w.gate == "bf16" else 4)
+    nbytes = fwd_bytes(w.B, w.T, w.H, w.dk, w.dv, s_q, s_g, 4, s0=d["S0"] is not None, sfinal=True)
+    flops = fwd_flops(w.B, w.T, w.H, w.dk, w.dv)
+    ms = wall / steps * 1e3
+    log(f"[bench] {w.name} {ms:.3f} ms/step (kernel {ker * 1e3:.3f} ms)")
+    out = {"workload": w.name, "ms": round(ms, 4), "kernel_ms": round(ker * 1e3, 4),
+           "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+           "tflops": round(flops / (wall / steps) / 1e12, 2),
+           "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}
+    del d, o, Sf
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode(kda, reps):
@@ -479,6 +511,9 @@ def main():
         "roofline": rf,
     }
     if not args.no_decode:
+        from kda_workloads import configs
+        out["forward_secondary"] = [bench_fwd_secondary(kda, configs.HEADGROUP_BF16, 20, 3),
+                                    bench_fwd_secondary(kda, configs.LONG_BF16, 3, 1)]
         out["decode"] = bench_decode(kda, args.decode_reps)
         out["speculative"] = bench_speculative(kda, 10)
         out["epilogue"] = bench_epilogue(kda)
