@@ -57,6 +57,9 @@ SPEC_CASES = [
     configs.TINY_F32.scaled(B=2, H=2, T=1, s0_sd=0.3, name="spec_f32_K1"),
     configs.HEADGROUP_BF16.scaled(B=2, H=3, T=37, dk=64, dv=128, name="spec_bf16_K37_dk64"),
     configs.TINY_F32.scaled(B=2, H=2, T=7, dv=256, s0_sd=0.3, name="spec_f32_K7_dv256"),  # chunk-kernel route
+    # up to 16 drafts with dk = 64 (the matrix-core tile, two 32-channel pairs)
+    configs.HEADGROUP_BF16.scaled(B=3, H=2, T=12, dk=64, dv=64, name="spec_bf16_K12_dk64_dv64"),
+    configs.TINY_F32.scaled(B=3, H=2, T=9, dk=64, dv=128, s0_sd=0.3, name="spec_f32_K9_dk64_dv128"),
 ]
 
 
