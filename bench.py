@@ -384,9 +384,20 @@ def cpu_baseline(w, d, batch=32):
         del x
     tok_s = w.B * w.T / dt
     log(f"[bench] cpu baseline: {dt:.2f} s -> {tok_s:.3e} tokens/s")
+    # the per-core rate: one head over the whole sequence on one thread
+    x1 = {nm: f64(d[nm][0:1, :, 0:1]) for nm in ("q", "k", "v", "g", "beta")}
+    t0 = time.perf_counter()
+    orc.fwd(x1["q"], x1["k"], x1["v"], x1["g"], x1["beta"], None, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    flop_head_tok = 7 * w.dk * w.dv   # fade, the two state-vector products and the rank-one update
+    log(f"[bench] cpu baseline, one thread: {w.T} tokens of one head in {dt1:.2f} s")
     return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"all {n_all} heads x {w.T} tokens of {w.name} (the full step), float64 "
-                      f"token recurrence, {batch} heads per call, {dt:.2f} s wall"}
+                      f"token recurrence, {batch} heads per call, {dt:.2f} s wall",
+            "gflops_f64": round(w.B * w.T * w.H * flop_head_tok / dt / 1e9, 2),
+            "one_thread": {"token_heads_per_s": round(w.T / dt1, 1),
+                           "gflops_f64": round(w.T * flop_head_tok / dt1 / 1e9, 3),
+                           "sample": f"one head x {w.T} tokens, {dt1:.2f} s"}}
 
 
 # ------------------------------------------------------------ counter passes
