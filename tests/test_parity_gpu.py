@@ -60,6 +60,8 @@ SMALL_CASES = [
     T.scaled(B=1, H=2, T=300, dk=128, dv=64, name="bf16_dk128_dv64"),
     T.scaled(B=1, H=2, T=192, dk=128, dv=192, name="bf16_dk128_dv192"),
     T.scaled(B=1, H=2, T=256, dk=64, dv=64, name="bf16_d64"),
+    T.scaled(B=1, H=1, T=150, dk=128, dv=512, name="bf16_dk128_dv512"),   # largest dv: 8 value slabs
+    BF.scaled(B=1, H=1, T=70, dk=64, dv=512, name="f32_dk64_dv512"),
     H8.scaled(H=2, T=333, gate="bf16", name="bf16_gates_S0"),
     BF.scaled(H=2, T=300, qkv="f32", gate="bf16", s0_sd=0.5, name="f32_qkv_bf16_gates_S0"),
 ] + [BF.scaled(B=1, H=2, T=t, name=f"f32_T{t}") for t in (1, 15, 16, 17, 63, 64, 65)] \
