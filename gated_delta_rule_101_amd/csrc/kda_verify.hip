@@ -1,4 +1,5 @@
-// Speculative verify of up to 16 draft tokens per state on the matrix cores.
+// Speculative verify and commit of up to 16 draft tokens per state on the
+// matrix cores.
 //
 // "K3 Architecture Illustrated", speculative decoding: the target verifies a
 // batch of draft tokens; KDA's state must be rolled back after rejections, so
@@ -11,7 +12,13 @@
 //   U = (I + Diag(beta) A_kk)^-1 Diag(beta) (V - K~ S),
 //   O = Q~ S + A_qk U.
 // Only the two products with the state are large: [Q~; K~] S is 32 x dk x dv
-// per state, against the token loop's per-token state update.
+// per state, against the token loop's per-token state update.  Commit applies
+// the first n = accepted[b] drafts (the rest enter as identity tokens) and
+// needs no queries: with Gamma_n the decay of the whole prefix and
+// K-bar = e^{b_n - b} k the keys decayed to its end,
+//   S' = Diag(Gamma_n) S + K-bar^T U
+// (the chunk-end state update of the chunkwise form), accumulated in the
+// registers that loaded S and written back once.
 //
 // One 4-wave workgroup per state; wave w owns value columns
 // [w dv/4, (w+1) dv/4) and streams its dk x dv/4 slice of S from HBM straight
@@ -20,8 +27,10 @@
 // never passes through LDS and the state is read exactly once.  For
 // bfloat16 drafts the two state products take fp16 operands
 // (v_mfma_f32_16x16x32_f16; the state must stay below the fp16 limit 65504,
-// as in the bfloat16 chunk kernel); everything else, and the whole float32
-// draft path, uses float32 operands (v_mfma_f32_16x16x4_f32).
+// as in the bfloat16 chunk kernel), single fp16 terms for verify's
+// outputs and two-term fp16 on both sides for the state commit keeps;
+// everything else, and the whole float32 draft path, uses float32 operands
+// (v_mfma_f32_16x16x4_f32).
 #include "kda_device.h"
 #include "kda_internal.h"
 
