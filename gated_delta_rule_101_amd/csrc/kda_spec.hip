@@ -8,7 +8,9 @@
 // through a register copy of S and writes their outputs; S in memory is not
 // touched.  Commit runs the first accepted[b] drafts of each sequence and
 // writes the state back; the rest are never applied.  Either way S is read
-// once from HBM (and written once by commit), like a decode step.
+// once from HBM (and written once by commit), like a decode step.  The
+// library runs this token loop for more than 16 drafts; up to 16 go through
+// one tile of the chunkwise form on the matrix cores instead.
 //
 // Layout as the decode kernel: one 256-thread workgroup per state (dk x dv,
 // float32, dv contiguous); thread (row group rg, column group cg) holds
