@@ -202,7 +202,7 @@ kda_status_t kda_verify_step(const void *q, const void *k, const void *v, const 
                                         qkv_dtype, gate_dtype, out_dtype, true, true);
     if (st != KDA_OK) return st;
     if (K == 0 || B == 0 || H == 0) return KDA_OK;
-    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // the token-loop kernel
+    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // one workgroup per state
         kda::SpecArgs a = spec_args(q, k, v, g, beta, const_cast<float *>(S), B, K, H, dk, dv,
                                     qkv_dtype, gate_dtype, out_dtype);
         a.o = o;
@@ -225,7 +225,7 @@ kda_status_t kda_commit_step(const void *k, const void *v, const void *g, const 
                                         dk, dv, qkv_dtype, gate_dtype, KDA_F32, false, false);
     if (st != KDA_OK) return st;
     if (K == 0 || B == 0 || H == 0) return KDA_OK;
-    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // the token-loop kernel
+    if ((dk == 64 || dk == 128) && (dv == 64 || dv == 128)) {   // one workgroup per state
         kda::SpecArgs a = spec_args(nullptr, k, v, g, beta, S, B, K, H, dk, dv, qkv_dtype, gate_dtype, KDA_F32);
         a.accepted = accepted;
         // up to 16 drafts: one tile on the matrix cores; more: the token loop
