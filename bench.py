@@ -103,8 +103,11 @@ def kernel_source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk_pipe.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
-DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_rule_101_amd/csrc/kda_device.h"]
+# the kernel's source, its device helpers and the build script (compile flags)
+CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk_pipe.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
+                 "gated_delta_rule_101_amd/build_lib.py"]
+DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
+                  "gated_delta_rule_101_amd/build_lib.py"]
 
 
 def stored_traffic(kernel: str, sources) -> "dict | None":
