@@ -25,6 +25,27 @@
 namespace kda {
 namespace {
 
+// o and z are read once and y written once: non-temporal accesses keep the
+// stream from displacing cache lines that other work reuses (0.47 -> 0.44 ms
+// over the training-shape reads).
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void nt_load4(Raw4<float> &r, const float *p) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    r.a = make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void nt_load4(Raw4<uint16_t> &r, const uint16_t *p) {
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+    r.a = make_uint2(t[0], t[1]);
+}
+__device__ __forceinline__ void nt_store4(float *p, const float (&x)[4]) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4 *>(p));
+}
+__device__ __forceinline__ void nt_store4(uint16_t *p, const float (&x)[4]) {
+    const uint32_t lo = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(p));
+}
+
 constexpr int NTHREADS = 256;
 constexpr int ROW_LANES = 16;
 constexpr int ROWS_PER_BLOCK = NTHREADS / ROW_LANES;
@@ -59,8 +80,8 @@ kda_output_gate_kernel(const OT *o, const ZT *__restrict__ z, const float *__res
         for (int j = 0; j < NJ; ++j) {
             Raw4<OT> ro;
             Raw4<ZT> rz;
-            ro.load(o + base + 64 * j);
-            rz.load(z + base + 64 * j);
+            nt_load4(ro, o + base + 64 * j);
+            nt_load4(rz, z + base + 64 * j);
             ro.to_f32(ov[j]);
             rz.to_f32(zv[j]);
         }
@@ -79,7 +100,7 @@ kda_output_gate_kernel(const OT *o, const ZT *__restrict__ z, const float *__res
                 float yv[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) yv[c] = ov[j][c] * inv * w[j][c] * sigmoid_f32(zv[j][c]);
-                store4(y + base + 64 * j, yv);
+                nt_store4(y + base + 64 * j, yv);
             }
         }
     }
