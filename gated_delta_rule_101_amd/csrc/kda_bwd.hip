@@ -42,6 +42,7 @@ constexpr int TL = 16;        // tokens per tile (reference granularity)
 constexpr int NTH = 256;
 constexpr int NW = NTH / 64;
 constexpr int SW = 32;        // value columns per slab in the carries
+static_assert((BC + 4) % 4 == 0, "LDS rows of BC + 4 floats are whole 16-byte units");
 
 // Cooperative GEMM over the workgroup: out(i, j) = sum_kk A(i, kk) B(kk, j),
 // i < M, j < N (multiples of 16), kk < K (multiple of 4), all compile-time so
@@ -100,6 +101,20 @@ __device__ __forceinline__ void for_elems(F &&f)
     for (int i = 0; i < COUNT / NTH; ++i) f((int)threadIdx.x + NTH * i);
 }
 
+
+// Runs f(e) over this thread's 4-element groups 4 tid, 4 (tid + NTH), ... of a
+// COUNT-element block (whole workgroup rounds, so the loop unrolls).
+template <int COUNT, typename F>
+__device__ __forceinline__ void for_elems4(F &&f)
+{
+    static_assert(COUNT % (4 * NTH) == 0, "whole rounds of the workgroup");
+#pragma unroll
+    for (int i = 0; i < COUNT / (4 * NTH); ++i) f(4 * ((int)threadIdx.x + NTH * i));
+}
+
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+
 // e^x through the hardware base-2 exponential.  The arguments are
 // differences of chunk-local log-decay sums: tile-local factors stay within
 // [-80, 80] (g >= -5 over 16 tokens), where rounding x log2(e) costs at most
@@ -121,6 +136,18 @@ __device__ __forceinline__ float ld_live(const X *p, size_t i, bool live)
 {
     const float v = to_f32(p[i]);
     return live ? v : 0.f;
+}
+
+// The same for elements i..i+3 (i a multiple of 4, rows 16-byte aligned): one
+// 8- or 16-byte load.
+template <typename X>
+__device__ __forceinline__ f32x4 ld_live4(const X *p, size_t i, bool live)
+{
+    Raw4<X> raw;
+    raw.load(p + i);
+    float x[4];
+    raw.to_f32(x);
+    return live ? f32x4{x[0], x[1], x[2], x[3]} : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Workgroup -> (head, value slab) for the two carries.  Workgroups are dealt
@@ -149,24 +176,25 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
                     const GT *__restrict__ g, const GT *__restrict__ beta, BwdWorkspace ws, int T, int H, int NC)
 {
     constexpr int LK = DK + 4, LV = DV + 4, LC = BC + 4;
-    __shared__ float sq[BC][LK], sk[BC][LK], sb[BC][LK], sv[BC][LV];
-    __shared__ float sA[BC][LC], sL[BC][LC], sN[BC][LC];
+    // rows are whole 16-byte units and the arrays 16-byte aligned: 4-element LDS accesses
+    __shared__ alignas(16) float sq[BC][LK], sk[BC][LK], sb[BC][LK], sv[BC][LV];
+    __shared__ alignas(16) float sA[BC][LC], sL[BC][LC], sN[BC][LC];
     __shared__ float sbeta[BC];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
-    for_elems<BC * DK>([&](int e) {
+    for_elems4<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK, t = c * BC + r;
         const bool live = t < T;
         const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
-        sq[r][x] = ld_live(q, i, live);
-        sk[r][x] = ld_live(k, i, live);
-        sb[r][x] = ld_live(g, i, live);
+        st4(&sq[r][x], ld_live4(q, i, live));
+        st4(&sk[r][x], ld_live4(k, i, live));
+        st4(&sb[r][x], ld_live4(g, i, live));
     });
-    for_elems<BC * DV>([&](int e) {
+    for_elems4<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
-        sv[r][x] = ld_live(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T);
+        st4(&sv[r][x], ld_live4(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T));
     });
     if (tid < BC) {
         const int t = c * BC + tid;
@@ -420,19 +448,24 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
     // S and dS' are taken half of their dk rows at a time, so the workgroup
     // fits twice per CU.
     constexpr int LV = DV + 4, DH = DK / 2;
-    __shared__ float sS[DH][LV], sY1[BC][LV], sY2[BC][LV];
+    __shared__ alignas(16) float sS[DH][LV], sY1[BC][LV], sY2[BC][LV];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
-    for_elems<BC * DV>([&](int e) {
+    for_elems4<BC * DV>([&](int e) {
         const int r = e / DV, j = e % DV, t = c * BC + r;
-        sY1[r][j] = ld_live(dO, tix(bb, t < T ? t : T - 1, h, j, T, H, DV), t < T);
-        sY2[r][j] = ws.dU[ch * BC * DV + e];
+        Raw4<OT> rd;
+        rd.load(dO + tix(bb, t < T ? t : T - 1, h, j, T, H, DV));
+        float dv4[4];
+        rd.to_f32(dv4);
+        const bool live = t < T;
+        st4(&sY1[r][j], live ? f32x4{dv4[0], dv4[1], dv4[2], dv4[3]} : f32x4{0.f, 0.f, 0.f, 0.f});
+        st4(&sY2[r][j], ld4(&ws.dU[ch * BC * DV + e]));
     });
     for (int half = 0; half < 2; ++half) {
         const int x0 = half * DH;
-        for_elems<DH * DV>([&](int e) { sS[e / DV][e % DV] = ws.h[ch * DK * DV + (size_t)x0 * DV + e]; });
+        for_elems4<DH * DV>([&](int e) { st4(&sS[e / DV][e % DV], ld4(&ws.h[ch * DK * DV + (size_t)x0 * DV + e])); });
         __syncthreads();
         // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1), key columns x0..x0+DH-1
         wg_gemm<2 * BC, DH, DV>([&](int i, int j) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
@@ -444,7 +477,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         __syncthreads();
         if (half == 0) continue;
         // U replaces dU (both halves of dW are done)
-        for_elems<BC * DV>([&](int e) { sY2[e / DV][e % DV] = ws.U[ch * BC * DV + e]; });
+        for_elems4<BC * DV>([&](int e) { st4(&sY2[e / DV][e % DV], ld4(&ws.U[ch * BC * DV + e])); });
         __syncthreads();
         // dA_qk = tril(dO U^T)
         wg_gemm<BC, BC, DV>([&](int i, int j) { return sY1[i][j]; }, [&](int j, int s) { return sY2[s][j]; },
@@ -454,7 +487,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         // the upper half of S is still in LDS; the lower half is reloaded
         const int half = 1 - hh, x0 = half * DH;
         if (half == 0) {
-            for_elems<DH * DV>([&](int e) { sS[e / DV][e % DV] = ws.h[ch * DK * DV + e]; });
+            for_elems4<DH * DV>([&](int e) { st4(&sS[e / DV][e % DV], ld4(&ws.h[ch * DK * DV + e])); });
             __syncthreads();
         }
         // dGamma_C = rowsum(S . dS') with TPR threads per row; dS' replaces S
@@ -493,24 +526,24 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
                      BwdWorkspace ws, int T, int H, int NC)
 {
     constexpr int LK = DK + 4, LM = (DK > DV ? DK : DV) + 4, LC = BC + 4;
-    __shared__ float sq[BC][LK], sk[BC][LK], sb[BC][LK];
-    __shared__ float sP[BC][LM];    // dW, then the dq accumulator
-    __shared__ float sV[BC][LM];    // v, then the dk accumulator
-    __shared__ float sU[BC][LM];    // dU, then the db accumulator
-    __shared__ float sN[BC][LC], sAk[BC][LC], sdA[BC][LC], sT[BC][LC], sX[BC][LC];
+    __shared__ alignas(16) float sq[BC][LK], sk[BC][LK], sb[BC][LK];
+    __shared__ alignas(16) float sP[BC][LM];    // dW, then the dq accumulator
+    __shared__ alignas(16) float sV[BC][LM];    // v, then the dk accumulator
+    __shared__ alignas(16) float sU[BC][LM];    // dU, then the db accumulator
+    __shared__ alignas(16) float sN[BC][LC], sAk[BC][LC], sdA[BC][LC], sT[BC][LC], sX[BC][LC];
     __shared__ float sbeta[BC], sdb1[BC];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
 
-    for_elems<BC * DK>([&](int e) {
+    for_elems4<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK, t = c * BC + r;
         const bool live = t < T;
         const size_t i = tix(bb, live ? t : 0, h, x, T, H, DK);
-        sq[r][x] = ld_live(q, i, live);
-        sk[r][x] = ld_live(k, i, live);
-        sb[r][x] = ws.b[ch * BC * DK + e];
-        sP[r][x] = ws.dW[ch * BC * DK + e];
+        st4(&sq[r][x], ld_live4(q, i, live));
+        st4(&sk[r][x], ld_live4(k, i, live));
+        st4(&sb[r][x], ld4(&ws.b[ch * BC * DK + e]));
+        st4(&sP[r][x], ld4(&ws.dW[ch * BC * DK + e]));
     });
     // dQ~ and dK-bar for the element pass further down, requested now (this
     // kernel runs one workgroup per CU, so registers are plentiful)
@@ -521,16 +554,16 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         pdq[i] = ws.dQt[ch * BC * DK + tid + NTH * i];
         pdk[i] = ws.dKb[ch * BC * DK + tid + NTH * i];
     }
-    for_elems<BC * DV>([&](int e) {
+    for_elems4<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
-        sV[r][x] = ld_live(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T);
-        sU[r][x] = ws.dU[ch * BC * DV + e];
+        st4(&sV[r][x], ld_live4(v, tix(bb, t < T ? t : T - 1, h, x, T, H, DV), t < T));
+        st4(&sU[r][x], ld4(&ws.dU[ch * BC * DV + e]));
     });
-    for_elems<BC * BC>([&](int e) {
+    for_elems4<BC * BC>([&](int e) {
         const int r = e / BC, s = e % BC;
-        sN[r][s] = ws.N[ch * BC * BC + e];
-        sAk[r][s] = ws.Akk0[ch * BC * BC + e];
-        sdA[r][s] = ws.dAqk[ch * BC * BC + e];
+        st4(&sN[r][s], ld4(&ws.N[ch * BC * BC + e]));
+        st4(&sAk[r][s], ld4(&ws.Akk0[ch * BC * BC + e]));
+        st4(&sdA[r][s], ld4(&ws.dAqk[ch * BC * BC + e]));
     });
     if (tid < BC) {
         const int t = c * BC + tid;
