@@ -276,56 +276,63 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
                       int T, int H, int NC, int nslab)
 {
     constexpr int LK = DK + 4, LS = SW + 4;
-    constexpr int PE = BC * DK / NTH, PU = BC * SW / NTH;   // per-thread elements of a chunk block
-    __shared__ float sS[DK][LS], sW[BC][LK], sKb[BC][LK], sU[BC][LS], sG[DK];
+    // per-thread 4-element groups of a chunk block
+    constexpr int PE = BC * DK / (4 * NTH), PU = BC * SW / (4 * NTH);
+    static_assert(PE * 4 * NTH == BC * DK && PU * 4 * NTH == BC * SW, "whole groups per thread");
+    __shared__ alignas(16) float sS[DK][LS], sW[BC][LK], sKb[BC][LK], sU[BC][LS], sG[DK];
     const int tid = threadIdx.x;
     int bh, slab;
     head_and_slab(nslab, bh, slab);
     const int col0 = slab * SW, bb = bh / H, h = bh % H;
 
     // the next chunk's inputs, loaded one chunk ahead into registers
-    float pw[PE], pk[PE], pb[PE], pbl[PE], pu[PU];
+    f32x4 pw[PE], pk[PE], pb[PE], pbl[PE], pu[PU];
     auto fetch = [&](int c) {
         const size_t ch = (size_t)bh * NC + c;
 #pragma unroll
         for (int i = 0; i < PE; ++i) {
-            const int e = tid + NTH * i, r = e / DK, x = e % DK, t = c * BC + r;
-            pw[i] = ws.W[ch * BC * DK + e];
-            pb[i] = ws.b[ch * BC * DK + e];
-            pbl[i] = ws.b[(ch * BC + BC - 1) * DK + x];
-            pk[i] = ld_live(k, tix(bb, t < T ? t : T - 1, h, x, T, H, DK), t < T);
+            const int e = 4 * (tid + NTH * i), r = e / DK, x = e % DK, t = c * BC + r;
+            pw[i] = ld4(&ws.W[ch * BC * DK + e]);
+            pb[i] = ld4(&ws.b[ch * BC * DK + e]);
+            pbl[i] = ld4(&ws.b[(ch * BC + BC - 1) * DK + x]);
+            pk[i] = ld_live4(k, tix(bb, t < T ? t : T - 1, h, x, T, H, DK), t < T);
         }
 #pragma unroll
         for (int i = 0; i < PU; ++i) {
-            const int e = tid + NTH * i, r = e / SW, j = e % SW;
-            pu[i] = ws.U[(ch * BC + r) * DV + col0 + j];
+            const int e = 4 * (tid + NTH * i), r = e / SW, j = e % SW;
+            pu[i] = ld4(&ws.U[(ch * BC + r) * DV + col0 + j]);
         }
     };
 
-    for_elems<DK * SW>([&](int e) {
+    for_elems4<DK * SW>([&](int e) {
         const int r = e / SW, j = e % SW;
-        sS[r][j] = S0 ? S0[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
+        st4(&sS[r][j], S0 ? ld4(&S0[((size_t)bh * DK + r) * DV + col0 + j]) : f32x4{0.f, 0.f, 0.f, 0.f});
     });
     if (NC > 0) fetch(0);
     for (int c = 0; c < NC; ++c) {
         const size_t ch = (size_t)bh * NC + c;
 #pragma unroll
         for (int i = 0; i < PE; ++i) {
-            const int e = tid + NTH * i, r = e / DK, x = e % DK;
-            sW[r][x] = pw[i];
-            sKb[r][x] = pk[i] * ex(pbl[i] - pb[i]);
-            if (i == 0 && tid < DK) sG[x] = ex(pbl[i]);   // element 0 of threads < DK is channel tid
+            const int e = 4 * (tid + NTH * i), r = e / DK, x = e % DK;
+            st4(&sW[r][x], pw[i]);
+            f32x4 kb;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kb[u] = pk[i][u] * ex(pbl[i][u] - pb[i][u]);
+            st4(&sKb[r][x], kb);
+            if (i == 0 && tid < DK / 4)   // group 0 of threads < DK / 4 is channels 4 tid .. 4 tid + 3
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sG[x + u] = ex(pbl[i][u]);
         }
 #pragma unroll
         for (int i = 0; i < PU; ++i) {
-            const int e = tid + NTH * i;
-            sU[e / SW][e % SW] = pu[i];
+            const int e = 4 * (tid + NTH * i);
+            st4(&sU[e / SW][e % SW], pu[i]);
         }
         __syncthreads();
         if (c + 1 < NC) fetch(c + 1);
-        for_elems<DK * SW>([&](int e) {
+        for_elems4<DK * SW>([&](int e) {
             const int r = e / SW, j = e % SW;
-            ws.h[(ch * DK + r) * DV + col0 + j] = sS[r][j];
+            *reinterpret_cast<f32x4 *>(&ws.h[(ch * DK + r) * DV + col0 + j]) = ld4(&sS[r][j]);
         });
         // U = U_v - W S  (U_v is replaced by U in the workspace)
         wg_gemm<BC, SW, DK>([&](int i, int x) { return sW[i][x]; }, [&](int x, int j) { return sS[x][j]; },
@@ -351,66 +358,74 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
                        int T, int H, int NC, int nslab)
 {
     constexpr int LK = DK + 4, LS = SW + 4, LC = BC + 4;
-    constexpr int PE = BC * DK / NTH, PO = BC * SW / NTH, PA = BC * BC / NTH;
-    __shared__ float sD[DK][LS], sX1[BC][LK], sX2[BC][LK], sA[BC][LC], sO[BC][LS], sdU[BC][LS], sG[DK];
+    // per-thread 4-element groups of a chunk block
+    constexpr int PE = BC * DK / (4 * NTH), PO = BC * SW / (4 * NTH), PA = BC * BC / (4 * NTH);
+    static_assert(PE * 4 * NTH == BC * DK && PO * 4 * NTH == BC * SW && PA * 4 * NTH == BC * BC,
+                  "whole groups per thread");
+    __shared__ alignas(16) float sD[DK][LS], sX1[BC][LK], sX2[BC][LK], sA[BC][LC], sO[BC][LS], sdU[BC][LS], sG[DK];
     const int tid = threadIdx.x;
     int bh, slab;
     head_and_slab(nslab, bh, slab);
     const int col0 = slab * SW, bb = bh / H, h = bh % H;
 
     // the previous chunk's inputs (the pass runs backwards), one chunk ahead
-    float pk[PE], pq[PE], pb[PE], pbl[PE], pw[PE], po[PO], pa[PA];
+    f32x4 pk[PE], pq[PE], pb[PE], pbl[PE], pw[PE], po[PO], pa[PA];
     auto fetch = [&](int c) {
         const size_t ch = (size_t)bh * NC + c;
 #pragma unroll
         for (int i = 0; i < PE; ++i) {
-            const int e = tid + NTH * i, r = e / DK, x = e % DK, t = c * BC + r;
+            const int e = 4 * (tid + NTH * i), r = e / DK, x = e % DK, t = c * BC + r;
             const bool live = t < T;
             const size_t ti = tix(bb, live ? t : 0, h, x, T, H, DK);
-            pk[i] = ld_live(k, ti, live);
-            pq[i] = ld_live(q, ti, live);
-            pb[i] = ws.b[ch * BC * DK + e];
-            pbl[i] = ws.b[(ch * BC + BC - 1) * DK + x];
-            pw[i] = ws.W[ch * BC * DK + e];
+            pk[i] = ld_live4(k, ti, live);
+            pq[i] = ld_live4(q, ti, live);
+            pb[i] = ld4(&ws.b[ch * BC * DK + e]);
+            pbl[i] = ld4(&ws.b[(ch * BC + BC - 1) * DK + x]);
+            pw[i] = ld4(&ws.W[ch * BC * DK + e]);
         }
 #pragma unroll
         for (int i = 0; i < PO; ++i) {
-            const int e = tid + NTH * i, r = e / SW, j = e % SW, t = c * BC + r;
-            po[i] = ld_live(dO, tix(bb, t < T ? t : T - 1, h, col0 + j, T, H, DV), t < T);
+            const int e = 4 * (tid + NTH * i), r = e / SW, j = e % SW, t = c * BC + r;
+            po[i] = ld_live4(dO, tix(bb, t < T ? t : T - 1, h, col0 + j, T, H, DV), t < T);
         }
 #pragma unroll
-        for (int i = 0; i < PA; ++i) pa[i] = ws.Aqk[ch * BC * BC + tid + NTH * i];
+        for (int i = 0; i < PA; ++i) pa[i] = ld4(&ws.Aqk[ch * BC * BC + 4 * (tid + NTH * i)]);
     };
 
-    for (int e = tid; e < DK * SW; e += NTH) {
+    for_elems4<DK * SW>([&](int e) {
         const int r = e / SW, j = e % SW;
-        sD[r][j] = dS_T ? dS_T[((size_t)bh * DK + r) * DV + col0 + j] : 0.f;
-    }
+        st4(&sD[r][j], dS_T ? ld4(&dS_T[((size_t)bh * DK + r) * DV + col0 + j]) : f32x4{0.f, 0.f, 0.f, 0.f});
+    });
     if (NC > 0) fetch(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const size_t ch = (size_t)bh * NC + c;
 #pragma unroll
         for (int i = 0; i < PE; ++i) {
-            const int e = tid + NTH * i, r = e / DK, x = e % DK;
-            sX1[r][x] = pk[i] * ex(pbl[i] - pb[i]);       // K-bar
-            sX2[r][x] = pw[i];
-            if (i == 0 && tid < DK) sG[x] = ex(pbl[i]);
+            const int e = 4 * (tid + NTH * i), r = e / DK, x = e % DK;
+            f32x4 kb;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kb[u] = pk[i][u] * ex(pbl[i][u] - pb[i][u]);   // K-bar
+            st4(&sX1[r][x], kb);
+            st4(&sX2[r][x], pw[i]);
+            if (i == 0 && tid < DK / 4)   // group 0 of threads < DK / 4 is channels 4 tid .. 4 tid + 3
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sG[x + u] = ex(pbl[i][u]);
         }
 #pragma unroll
         for (int i = 0; i < PO; ++i) {
-            const int e = tid + NTH * i;
-            sO[e / SW][e % SW] = po[i];
+            const int e = 4 * (tid + NTH * i);
+            st4(&sO[e / SW][e % SW], po[i]);
         }
 #pragma unroll
         for (int i = 0; i < PA; ++i) {
-            const int e = tid + NTH * i;
-            sA[e / BC][e % BC] = pa[i];
+            const int e = 4 * (tid + NTH * i);
+            st4(&sA[e / BC][e % BC], pa[i]);
         }
         __syncthreads();
-        for (int e = tid; e < DK * SW; e += NTH) {
+        for_elems4<DK * SW>([&](int e) {
             const int r = e / SW, j = e % SW;
-            ws.dh[(ch * DK + r) * DV + col0 + j] = sD[r][j];
-        }
+            *reinterpret_cast<f32x4 *>(&ws.dh[(ch * DK + r) * DV + col0 + j]) = ld4(&sD[r][j]);
+        });
         // dU = K-bar dS' + A_qk^T dO
         wg_gemm<BC, SW, DK + BC>([&](int i, int x) { return x < DK ? sX1[i][x] : sA[x - DK][i]; },
                                  [&](int x, int j) { return x < DK ? sD[x][j] : sO[x - DK][j]; },
@@ -421,8 +436,11 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < PE; ++i) {   // Gamma . Q replaces K-bar
-            const int e = tid + NTH * i;
-            sX1[e / DK][e % DK] = pq[i] * ex(pb[i]);
+            const int e = 4 * (tid + NTH * i);
+            f32x4 qg;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) qg[u] = pq[i][u] * ex(pb[i][u]);
+            st4(&sX1[e / DK][e % DK], qg);
         }
         __syncthreads();
         if (c > 0) fetch(c - 1);
@@ -433,10 +451,10 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         __syncthreads();
     }
     if (dS0)
-        for (int e = tid; e < DK * SW; e += NTH) {
+        for_elems4<DK * SW>([&](int e) {
             const int r = e / SW, j = e % SW;
-            dS0[((size_t)bh * DK + r) * DV + col0 + j] = sD[r][j];
-        }
+            *reinterpret_cast<f32x4 *>(&dS0[((size_t)bh * DK + r) * DV + col0 + j]) = ld4(&sD[r][j]);
+        });
 }
 
 // ------------------------------------------- products with S and dS'
