@@ -213,7 +213,7 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
         }
     }
     __syncthreads();
-    for (int e = tid; e < BC * DK; e += NTH) { ws.b[ch * BC * DK + e] = sb[e / DK][e % DK]; }
+    for_elems4<BC * DK>([&](int e) { st4(&ws.b[ch * BC * DK + e], ld4(&sb[e / DK][e % DK])); });
 
     // Gram matrices, one row tile at a time: rows scaled by e^{b - rho},
     // keys by e^{rho - b}, rho = b at the end of the previous tile.
@@ -253,12 +253,12 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
         for (int i = 0; i < BC; ++i) sN[i][j] = x[i];
     }
     __syncthreads();
-    for (int e = tid; e < BC * BC; e += NTH) {
+    for_elems4<BC * BC>([&](int e) {
         const int r = e / BC, s = e % BC;
-        ws.Aqk[ch * BC * BC + e] = sA[r][s];
-        ws.Akk0[ch * BC * BC + e] = sL[r][s];
-        ws.N[ch * BC * BC + e] = sN[r][s];
-    }
+        st4(&ws.Aqk[ch * BC * BC + e], ld4(&sA[r][s]));
+        st4(&ws.Akk0[ch * BC * BC + e], ld4(&sL[r][s]));
+        st4(&ws.N[ch * BC * BC + e], ld4(&sN[r][s]));
+    });
     // W = N Diag(beta) (Gamma . K),  U_v = N Diag(beta) V
     wg_gemm<BC, DK, BC>([&](int i, int s) { return sN[i][s]; },
             [&](int s, int x) { return sbeta[s] * ex(sb[s][x]) * sk[s][x]; },
@@ -565,12 +565,13 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     });
     // dQ~ and dK-bar for the element pass further down, requested now (this
     // kernel runs one workgroup per CU, so registers are plentiful)
-    constexpr int PE = BC * DK / NTH;
-    float pdq[PE], pdk[PE];
+    constexpr int PE = BC * DK / (4 * NTH);   // 4-element groups per thread
+    static_assert(PE * 4 * NTH == BC * DK, "whole groups per thread");
+    f32x4 pdq[PE], pdk[PE];
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
-        pdq[i] = ws.dQt[ch * BC * DK + tid + NTH * i];
-        pdk[i] = ws.dKb[ch * BC * DK + tid + NTH * i];
+        pdq[i] = ld4(&ws.dQt[ch * BC * DK + 4 * (tid + NTH * i)]);
+        pdk[i] = ld4(&ws.dKb[ch * BC * DK + 4 * (tid + NTH * i)]);
     }
     for_elems4<BC * DV>([&](int e) {
         const int r = e / DV, x = e % DV, t = c * BC + r;
@@ -615,12 +616,20 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     for_elems<BC * BC>([&](int e) { sT[e / BC][e % BC] *= sbeta[e % BC]; });   // dN = dT Diag(beta)
 #pragma unroll
     for (int ii = 0; ii < PE; ++ii) {
-        const int e = tid + NTH * ii, r = e / DK, x = e % DK;
-        const float eb = ex(sb[r][x]), ekb = ex(sb[BC - 1][x] - sb[r][x]);
-        const float dqt = pdq[ii], dkb = pdk[ii];
-        sP[r][x] = eb * dqt;
-        sV[r][x] += ekb * dkb;
-        sU[r][x] += eb * sq[r][x] * dqt - ekb * sk[r][x] * dkb;
+        const int e = 4 * (tid + NTH * ii), r = e / DK, x = e % DK;
+        const f32x4 bv = ld4(&sb[r][x]), blv = ld4(&sb[BC - 1][x]), qv = ld4(&sq[r][x]), kv = ld4(&sk[r][x]);
+        f32x4 pv, vv = ld4(&sV[r][x]), uv = ld4(&sU[r][x]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float eb = ex(bv[u]), ekb = ex(blv[u] - bv[u]);
+            const float dqt = pdq[ii][u], dkb = pdk[ii][u];
+            pv[u] = eb * dqt;
+            vv[u] += ekb * dkb;
+            uv[u] += eb * qv[u] * dqt - ekb * kv[u] * dkb;
+        }
+        st4(&sP[r][x], pv);
+        st4(&sV[r][x], vv);
+        st4(&sU[r][x], uv);
     }
     __syncthreads();
     // dA_kk = -strict_tril(N^T dN N^T)
@@ -701,13 +710,13 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         }
     }
     __syncthreads();
-    for_elems<BC * DK>([&](int e) {
+    for_elems4<BC * DK>([&](int e) {
         const int r = e / DK, x = e % DK, t = c * BC + r;
         if (t < T) {
             const size_t i = tix(bb, t, h, x, T, H, DK);
-            dq[i] = sP[r][x];
-            dk[i] = sV[r][x];
-            dg[i] = sU[r][x];
+            st4(&dq[i], ld4(&sP[r][x]));
+            st4(&dk[i], ld4(&sV[r][x]));
+            st4(&dg[i], ld4(&sU[r][x]));
         }
     });
 }
