@@ -50,9 +50,12 @@ static_assert((BC + 4) % 4 == 0, "LDS rows of BC + 4 floats are whole 16-byte un
 // 16 x 16 tiles are dealt to the waves round-robin, two at a time (two
 // independent accumulation chains); lane (r16, kq) feeds A(i0 + r16, kk + kq)
 // and B(kk + kq, j0 + r16) and receives rows i0 + 4 kq + 0..3 of column
-// j0 + r16.  epi(i, j, value) is called once per result.
+// j0 + r16.  epi4(i, j, v) is called once per lane and tile with the four
+// results of rows i..i+3 of column j (v[r] is row i + r); computing the
+// transposed product puts four consecutive columns of a row-major result
+// in one lane, ready for one 16-byte store.
 template <int M, int N, int K, typename FA, typename FB, typename FE>
-__device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
+__device__ __forceinline__ void wg_gemm4(FA A, FB B, FE epi4)
 {
     static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "tile shape");
     constexpr int TN = N / 16, NT = (M / 16) * TN;
@@ -69,8 +72,7 @@ __device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + kq), B(kk + kq, j0 + r16), acc0, 0, 0, 0);
                 acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i1 + r16, kk + kq), B(kk + kq, j1 + r16), acc1, 0, 0, 0);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) epi(i1 + 4 * kq + r, j1 + r16, acc1[r]);
+            epi4(i1 + 4 * kq, j1 + r16, acc1);
         } else if constexpr (K % 8 == 0) {   // one tile: even and odd k-steps in two chains
             f32x4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -84,9 +86,18 @@ __device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
             for (int kk = 0; kk < K; kk += 4)
                 acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(A(i0 + r16, kk + kq), B(kk + kq, j0 + r16), acc0, 0, 0, 0);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) epi(i0 + 4 * kq + r, j0 + r16, acc0[r]);
+        epi4(i0 + 4 * kq, j0 + r16, acc0);
     }
+}
+
+// The same with epi(i, j, value) called once per result.
+template <int M, int N, int K, typename FA, typename FB, typename FE>
+__device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
+{
+    wg_gemm4<M, N, K>(A, B, [&](int i, int j, f32x4 v) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) epi(i + r, j, v[r]);
+    });
 }
 
 // Runs f(e) over this thread's elements tid, tid + NTH, ... of a COUNT-element
@@ -260,12 +271,13 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
         st4(&ws.N[ch * BC * BC + e], ld4(&sN[r][s]));
     });
     // W = N Diag(beta) (Gamma . K),  U_v = N Diag(beta) V
-    wg_gemm<BC, DK, BC>([&](int i, int s) { return sN[i][s]; },
-            [&](int s, int x) { return sbeta[s] * ex(sb[s][x]) * sk[s][x]; },
-            [&](int i, int x, float val) { ws.W[(ch * BC + i) * DK + x] = val; });
-    wg_gemm<BC, DV, BC>([&](int i, int s) { return sN[i][s]; },
-            [&](int s, int x) { return sbeta[s] * sv[s][x]; },
-            [&](int i, int x, float val) { ws.U[(ch * BC + i) * DV + x] = val; });
+    // (computed transposed: each lane stores four consecutive columns of a row)
+    wg_gemm4<DK, BC, BC>([&](int x, int s) { return sbeta[s] * ex(sb[s][x]) * sk[s][x]; },
+            [&](int s, int i) { return sN[i][s]; },
+            [&](int x, int i, f32x4 v) { st4(&ws.W[(ch * BC + i) * DK + x], v); });
+    wg_gemm4<DV, BC, BC>([&](int x, int s) { return sbeta[s] * sv[s][x]; },
+            [&](int s, int i) { return sN[i][s]; },
+            [&](int x, int i, f32x4 v) { st4(&ws.U[(ch * BC + i) * DV + x], v); });
 }
 
 // --------------------------------------------------------- forward carry
@@ -486,20 +498,26 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         for_elems4<DH * DV>([&](int e) { st4(&sS[e / DV][e % DV], ld4(&ws.h[ch * DK * DV + (size_t)x0 * DV + e])); });
         __syncthreads();
         // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1), key columns x0..x0+DH-1
-        wg_gemm<2 * BC, DH, DV>([&](int i, int j) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
-                                [&](int j, int x) { return sS[x][j]; },
-                                [&](int i, int x, float val) {
-                                    if (i < BC) ws.dQt[(ch * BC + i) * DK + x0 + x] = val;
-                                    else ws.dW[(ch * BC + i - BC) * DK + x0 + x] = -val;
-                                });
+        // computed transposed (key columns as rows) so each lane stores four
+        // consecutive key columns of one token row
+        wg_gemm4<DH, 2 * BC, DV>([&](int x, int j) { return sS[x][j]; },
+                                 [&](int j, int i) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
+                                 [&](int x, int i, f32x4 v) {
+                                     if (i < BC) st4(&ws.dQt[(ch * BC + i) * DK + x0 + x], v);
+                                     else st4(&ws.dW[(ch * BC + i - BC) * DK + x0 + x], -v);
+                                 });
         __syncthreads();
         if (half == 0) continue;
         // U replaces dU (both halves of dW are done)
         for_elems4<BC * DV>([&](int e) { st4(&sY2[e / DV][e % DV], ld4(&ws.U[ch * BC * DV + e])); });
         __syncthreads();
         // dA_qk = tril(dO U^T)
-        wg_gemm<BC, BC, DV>([&](int i, int j) { return sY1[i][j]; }, [&](int j, int s) { return sY2[s][j]; },
-                            [&](int i, int s, float val) { ws.dAqk[(ch * BC + i) * BC + s] = s <= i ? val : 0.f; });
+        wg_gemm4<BC, BC, DV>([&](int s, int j) { return sY2[s][j]; }, [&](int j, int i) { return sY1[i][j]; },
+                             [&](int s, int i, f32x4 v) {
+#pragma unroll
+                                 for (int u = 0; u < 4; ++u) v[u] = s + u <= i ? v[u] : 0.f;
+                                 st4(&ws.dAqk[(ch * BC + i) * BC + s], v);
+                             });
     }
     for (int hh = 0; hh < 2; ++hh) {
         // the upper half of S is still in LDS; the lower half is reloaded
@@ -528,8 +546,8 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         }
         __syncthreads();
         // dK-bar = U dS'^T, key columns x0..x0+DH-1
-        wg_gemm<BC, DH, DV>([&](int i, int j) { return sY2[i][j]; }, [&](int j, int x) { return sS[x][j]; },
-                            [&](int i, int x, float val) { ws.dKb[(ch * BC + i) * DK + x0 + x] = val; });
+        wg_gemm4<DH, BC, DV>([&](int x, int j) { return sS[x][j]; }, [&](int j, int i) { return sY2[i][j]; },
+                             [&](int x, int i, f32x4 v) { st4(&ws.dKb[(ch * BC + i) * DK + x0 + x], v); });
         __syncthreads();
     }
 }
@@ -594,10 +612,11 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
             [&](int x, int s) { return x < DK ? sk[s][x] * ex(sb[s][x]) : sV[s][x - DK]; },
             [&](int i, int s, float val) { sT[i][s] = s <= i ? val : 0.f; });
     // dv = Diag(beta) N^T dU
-    wg_gemm<BC, DV, BC>([&](int i, int s) { return sbeta[i] * sN[s][i]; }, [&](int s, int j) { return sU[s][j]; },
-            [&](int i, int j, float val) {
+    // (computed transposed: each lane stores four consecutive value columns)
+    wg_gemm4<DV, BC, BC>([&](int j, int s) { return sU[s][j]; }, [&](int s, int i) { return sbeta[i] * sN[s][i]; },
+            [&](int j, int i, f32x4 v) {
                 const int t = c * BC + i;
-                if (t < T) dv[tix(bb, t, h, j, T, H, DV)] = val;
+                if (t < T) st4(&dv[tix(bb, t, h, j, T, H, DV)], v);
             });
     __syncthreads();
     // dK~ = Diag(beta) N^T dW: dk accumulator <- Gamma . dK~, db accumulator <- K~ . dK~
