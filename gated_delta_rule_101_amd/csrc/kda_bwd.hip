@@ -90,6 +90,52 @@ __device__ __forceinline__ void wg_gemm4(FA A, FB B, FE epi4)
     }
 }
 
+// As wg_gemm4, with the operands fetched four k-items at a time: within each
+// block of 16 k-items lane group kq supplies items 16 g + 4 kq + (0..3) over
+// four consecutive matrix-core steps, so A4(i, k) returns A(i, k..k+3) and
+// B4(k, j) returns B(k..k+3, j) (k a multiple of 4): one 16-byte LDS read
+// when the operand is stored contiguously along k.  Branches on k at a
+// multiple of 16 stay uniform across the wave.
+template <int M, int N, int K, typename FA4, typename FB4, typename FE>
+__device__ __forceinline__ void wg_gemm_v(FA4 A4, FB4 B4, FE epi4)
+{
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "tile shape");
+    constexpr int TN = N / 16, NT = (M / 16) * TN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    for (int t = wave; t < NT; t += 2 * NW) {
+        const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        if (t + NW < NT) {   // two tiles: two independent chains
+            const int u = t + NW, i1 = (u / TN) * 16, j1 = (u % TN) * 16;
+#pragma unroll
+            for (int g = 0; g < K / 16; ++g) {
+                const int k = 16 * g + 4 * kq;
+                const f32x4 a0 = A4(i0 + r16, k), b0 = B4(k, j0 + r16);
+                const f32x4 a1 = A4(i1 + r16, k), b1 = B4(k, j1 + r16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[e], b0[e], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[e], b1[e], acc1, 0, 0, 0);
+                }
+            }
+            epi4(i1 + 4 * kq, j1 + r16, acc1);
+        } else {   // one tile: alternate steps in two chains
+#pragma unroll
+            for (int g = 0; g < K / 16; ++g) {
+                const int k = 16 * g + 4 * kq;
+                const f32x4 a0 = A4(i0 + r16, k), b0 = B4(k, j0 + r16);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[0], b0[0], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[1], b0[1], acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[2], b0[2], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[3], b0[3], acc1, 0, 0, 0);
+            }
+            acc0 += acc1;
+        }
+        epi4(i0 + 4 * kq, j0 + r16, acc0);
+    }
+}
+
 // The same with epi(i, j, value) called once per result.
 template <int M, int N, int K, typename FA, typename FB, typename FE>
 __device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
@@ -231,17 +277,32 @@ kda_bwd_prep_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const QT
     static_assert(BC == 2 * TL, "two row tiles per chunk");
     auto gram_rows = [&](auto mc) {
         constexpr int m = decltype(mc)::value;
-        auto rho = [&](int x) { if constexpr (m == 0) return 0.f; else return sb[TL * m - 1][x]; };
-        wg_gemm<2 * TL, TL * (m + 1), DK>([&](int i, int x) {
+        // rho at channels x..x+3
+        auto rho4 = [&](int x) {
+            if constexpr (m == 0) return f32x4{0.f, 0.f, 0.f, 0.f}; else return ld4(&sb[TL * m - 1][x]);
+        };
+        wg_gemm_v<2 * TL, TL * (m + 1), DK>([&](int i, int x) {
                     const int r = TL * m + (i & (TL - 1));
-                    const float f = ex(sb[r][x] - rho(x));
-                    return (i < TL ? sq[r][x] : sk[r][x]) * f;
+                    const f32x4 bv = ld4(&sb[r][x]), rv = rho4(x), xv = i < TL ? ld4(&sq[r][x]) : ld4(&sk[r][x]);
+                    f32x4 out;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) out[u] = xv[u] * ex(bv[u] - rv[u]);
+                    return out;
                 },
-                [&](int x, int s) { return sk[s][x] * ex(rho(x) - sb[s][x]); },
-                [&](int i, int s, float val) {
-                    const int r = TL * m + (i & (TL - 1));
-                    if (i < TL) sA[r][s] = s <= r ? val : 0.f;
-                    else sL[r][s] = s < r ? val : 0.f;
+                [&](int x, int s) {
+                    const f32x4 kv = ld4(&sk[s][x]), bv = ld4(&sb[s][x]), rv = rho4(x);
+                    f32x4 out;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) out[u] = kv[u] * ex(rv[u] - bv[u]);
+                    return out;
+                },
+                [&](int i, int s, f32x4 v) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = TL * m + ((i + u) & (TL - 1));
+                        if (i + u < TL) sA[r][s] = s <= r ? v[u] : 0.f;
+                        else sL[r][s] = s < r ? v[u] : 0.f;
+                    }
                 });
     };
     gram_rows(std::integral_constant<int, 0>{});
@@ -500,8 +561,8 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1), key columns x0..x0+DH-1
         // computed transposed (key columns as rows) so each lane stores four
         // consecutive key columns of one token row
-        wg_gemm4<DH, 2 * BC, DV>([&](int x, int j) { return sS[x][j]; },
-                                 [&](int j, int i) { return i < BC ? sY1[i][j] : sY2[i - BC][j]; },
+        wg_gemm_v<DH, 2 * BC, DV>([&](int x, int j) { return ld4(&sS[x][j]); },
+                                  [&](int j, int i) { return i < BC ? ld4(&sY1[i][j]) : ld4(&sY2[i - BC][j]); },
                                  [&](int x, int i, f32x4 v) {
                                      if (i < BC) st4(&ws.dQt[(ch * BC + i) * DK + x0 + x], v);
                                      else st4(&ws.dW[(ch * BC + i - BC) * DK + x0 + x], -v);
@@ -512,7 +573,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         for_elems4<BC * DV>([&](int e) { st4(&sY2[e / DV][e % DV], ld4(&ws.U[ch * BC * DV + e])); });
         __syncthreads();
         // dA_qk = tril(dO U^T)
-        wg_gemm4<BC, BC, DV>([&](int s, int j) { return sY2[s][j]; }, [&](int j, int i) { return sY1[i][j]; },
+        wg_gemm_v<BC, BC, DV>([&](int s, int j) { return ld4(&sY2[s][j]); }, [&](int j, int i) { return ld4(&sY1[i][j]); },
                              [&](int s, int i, f32x4 v) {
 #pragma unroll
                                  for (int u = 0; u < 4; ++u) v[u] = s + u <= i ? v[u] : 0.f;
@@ -546,7 +607,7 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         }
         __syncthreads();
         // dK-bar = U dS'^T, key columns x0..x0+DH-1
-        wg_gemm4<DH, BC, DV>([&](int x, int j) { return sS[x][j]; }, [&](int j, int i) { return sY2[i][j]; },
+        wg_gemm_v<DH, BC, DV>([&](int x, int j) { return ld4(&sS[x][j]); }, [&](int j, int i) { return ld4(&sY2[i][j]); },
                              [&](int x, int i, f32x4 v) { st4(&ws.dKb[(ch * BC + i) * DK + x0 + x], v); });
         __syncthreads();
     }
@@ -608,9 +669,19 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     }
     __syncthreads();
     // dT = tril(dW (Gamma . K)^T + dU V^T)
-    wg_gemm<BC, BC, DK + DV>([&](int i, int x) { return x < DK ? sP[i][x] : sU[i][x - DK]; },
-            [&](int x, int s) { return x < DK ? sk[s][x] * ex(sb[s][x]) : sV[s][x - DK]; },
-            [&](int i, int s, float val) { sT[i][s] = s <= i ? val : 0.f; });
+    wg_gemm_v<BC, BC, DK + DV>([&](int i, int x) { return x < DK ? ld4(&sP[i][x]) : ld4(&sU[i][x - DK]); },
+            [&](int x, int s) {
+                if (x >= DK) return ld4(&sV[s][x - DK]);
+                const f32x4 kv = ld4(&sk[s][x]), bv = ld4(&sb[s][x]);
+                f32x4 r;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) r[u] = kv[u] * ex(bv[u]);
+                return r;
+            },
+            [&](int i, int s, f32x4 v) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sT[i + u][s] = s <= i + u ? v[u] : 0.f;
+            });
     // dv = Diag(beta) N^T dU
     // (computed transposed: each lane stores four consecutive value columns)
     wg_gemm4<DV, BC, BC>([&](int j, int s) { return sU[s][j]; }, [&](int s, int i) { return sbeta[i] * sN[s][i]; },
