@@ -136,6 +136,14 @@ __device__ __forceinline__ void wg_gemm_v(FA4 A4, FB4 B4, FE epi4)
     }
 }
 
+// Four consecutive rows k..k+3 of column c of a row-major LDS array: the
+// operand of wg_gemm_v when it is stored with k along the rows.
+template <int L>
+__device__ __forceinline__ f32x4 down4(const float (*a)[L], int k, int c)
+{
+    return f32x4{a[k][c], a[k + 1][c], a[k + 2][c], a[k + 3][c]};
+}
+
 // The same with epi(i, j, value) called once per result.
 template <int M, int N, int K, typename FA, typename FB, typename FE>
 __device__ __forceinline__ void wg_gemm(FA A, FB B, FE epi)
@@ -408,12 +416,15 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
             *reinterpret_cast<f32x4 *>(&ws.h[(ch * DK + r) * DV + col0 + j]) = ld4(&sS[r][j]);
         });
         // U = U_v - W S  (U_v is replaced by U in the workspace)
-        wg_gemm<BC, SW, DK>([&](int i, int x) { return sW[i][x]; }, [&](int x, int j) { return sS[x][j]; },
-                            [&](int i, int j, float val) {
-                                const float u = sU[i][j] - val;
-                                sU[i][j] = u;
-                                ws.U[(ch * BC + i) * DV + col0 + j] = u;
-                            });
+        wg_gemm_v<BC, SW, DK>([&](int i, int x) { return ld4(&sW[i][x]); }, [&](int x, int j) { return down4<LS>(sS, x, j); },
+                              [&](int i, int j, f32x4 v) {
+#pragma unroll
+                                  for (int e = 0; e < 4; ++e) {
+                                      const float u = sU[i + e][j] - v[e];
+                                      sU[i + e][j] = u;
+                                      ws.U[(ch * BC + i + e) * DV + col0 + j] = u;
+                                  }
+                              });
         __syncthreads();
         // S <- Diag(Gamma_C) S + K-bar^T U
         wg_gemm<DK, SW, BC>([&](int x, int r) { return sKb[r][x]; }, [&](int r, int j) { return sU[r][j]; },
@@ -500,12 +511,15 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
             *reinterpret_cast<f32x4 *>(&ws.dh[(ch * DK + r) * DV + col0 + j]) = ld4(&sD[r][j]);
         });
         // dU = K-bar dS' + A_qk^T dO
-        wg_gemm<BC, SW, DK + BC>([&](int i, int x) { return x < DK ? sX1[i][x] : sA[x - DK][i]; },
-                                 [&](int x, int j) { return x < DK ? sD[x][j] : sO[x - DK][j]; },
-                                 [&](int i, int j, float val) {
-                                     sdU[i][j] = val;
-                                     ws.dU[(ch * BC + i) * DV + col0 + j] = val;
-                                 });
+        wg_gemm_v<BC, SW, DK + BC>([&](int i, int x) { return x < DK ? ld4(&sX1[i][x]) : down4<LC>(sA, x - DK, i); },
+                                   [&](int x, int j) { return x < DK ? down4<LS>(sD, x, j) : down4<LS>(sO, x - DK, j); },
+                                   [&](int i, int j, f32x4 v) {
+#pragma unroll
+                                       for (int e = 0; e < 4; ++e) {
+                                           sdU[i + e][j] = v[e];
+                                           ws.dU[(ch * BC + i + e) * DV + col0 + j] = v[e];
+                                       }
+                                   });
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < PE; ++i) {   // Gamma . Q replaces K-bar
@@ -726,8 +740,11 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     wg_gemm<BC, BC, BC>([&](int i, int l) { return sN[l][i]; }, [&](int l, int s) { return sT[l][s]; },
             [&](int i, int s, float val) { sX[i][s] = val; });
     __syncthreads();
-    wg_gemm<BC, BC, BC>([&](int i, int l) { return sX[i][l]; }, [&](int l, int s) { return sN[s][l]; },
-            [&](int i, int s, float val) { sT[i][s] = s < i ? -val : 0.f; });
+    wg_gemm_v<BC, BC, BC>([&](int i, int l) { return ld4(&sX[i][l]); }, [&](int l, int s) { return ld4(&sN[s][l]); },
+            [&](int i, int s, f32x4 v) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sT[i + u][s] = s < i + u ? -v[u] : 0.f;
+            });
     __syncthreads();
     if (tid < BC) {   // dbeta from A_kk = Diag(beta) A_kk0; then dA_kk0 = Diag(beta) dA_kk (row tid)
         const int r = tid, t = c * BC + r;
@@ -744,43 +761,65 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
     auto pair_grads = [&](auto mc) {
         constexpr int m = decltype(mc)::value;
         auto rho = [&](int x) { if constexpr (m == 0) return 0.f; else return sb[TL * m - 1][x]; };
+        // keys of rows s..s+3 at channel x scaled by e^{rho - b}
+        auto kcol4 = [&](int s, int x) {
+            const float rx = rho(x);
+            f32x4 out;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) out[u] = sk[s + u][x] * ex(rx - sb[s + u][x]);
+            return out;
+        };
         // dq += row(dA_qk, k);  db += q . row(dA_qk, k)
-        wg_gemm<TL, DK, TL * (m + 1)>([&](int i, int s) { return sdA[TL * m + i][s]; },
-                [&](int s, int x) { return sk[s][x] * ex(rho(x) - sb[s][x]); },
-                [&](int i, int x, float val) {
-                    const int r = TL * m + i;
-                    const float y = ex(sb[r][x] - rho(x)) * val;
-                    sP[r][x] += y;
-                    sU[r][x] += sq[r][x] * y;
+        wg_gemm_v<TL, DK, TL * (m + 1)>([&](int i, int s) { return ld4(&sdA[TL * m + i][s]); }, kcol4,
+                [&](int i, int x, f32x4 v) {
+                    const float rx = rho(x);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = TL * m + i + u;
+                        const float y = ex(sb[r][x] - rx) * v[u];
+                        sP[r][x] += y;
+                        sU[r][x] += sq[r][x] * y;
+                    }
                 });
         __syncthreads();
         // dk += row(dA_kk0, k);  db += k . row(dA_kk0, k)
-        wg_gemm<TL, DK, TL * (m + 1)>([&](int i, int s) { return sT[TL * m + i][s]; },
-                [&](int s, int x) { return sk[s][x] * ex(rho(x) - sb[s][x]); },
-                [&](int i, int x, float val) {
-                    const int r = TL * m + i;
-                    const float y = ex(sb[r][x] - rho(x)) * val;
-                    sV[r][x] += y;
-                    sU[r][x] += sk[r][x] * y;
+        wg_gemm_v<TL, DK, TL * (m + 1)>([&](int i, int s) { return ld4(&sT[TL * m + i][s]); }, kcol4,
+                [&](int i, int x, f32x4 v) {
+                    const float rx = rho(x);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = TL * m + i + u;
+                        const float y = ex(sb[r][x] - rx) * v[u];
+                        sV[r][x] += y;
+                        sU[r][x] += sk[r][x] * y;
+                    }
                 });
         __syncthreads();
+        // rows TL m + i..i+3 of X at channel x scaled by e^{b - rho}
+        auto xcol4 = [&](const float (*X)[LK], int i, int x) {
+            const float rx = rho(x);
+            f32x4 out;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) out[u] = X[TL * m + i + u][x] * ex(sb[TL * m + i + u][x] - rx);
+            return out;
+        };
+        // the column-role epilogue: rows s..s+3 at channel x
+        auto col_epi = [&](int s, int x, f32x4 v) {
+            const float rx = rho(x);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float y = ex(rx - sb[s + u][x]) * v[u];
+                sV[s + u][x] += y;
+                sU[s + u][x] -= sk[s + u][x] * y;
+            }
+        };
         // dk += col(dA_qk, q);  db -= k . col(dA_qk, q)
-        wg_gemm<TL * (m + 1), DK, TL>([&](int s, int i) { return sdA[TL * m + i][s]; },
-                [&](int i, int x) { return sq[TL * m + i][x] * ex(sb[TL * m + i][x] - rho(x)); },
-                [&](int s, int x, float val) {
-                    const float y = ex(rho(x) - sb[s][x]) * val;
-                    sV[s][x] += y;
-                    sU[s][x] -= sk[s][x] * y;
-                });
+        wg_gemm_v<TL * (m + 1), DK, TL>([&](int s, int i) { return down4<LC>(&sdA[TL * m], i, s); },
+                [&](int i, int x) { return xcol4(sq, i, x); }, col_epi);
         __syncthreads();
         // dk += col(dA_kk0, k);  db -= k . col(dA_kk0, k)
-        wg_gemm<TL * (m + 1), DK, TL>([&](int s, int i) { return sT[TL * m + i][s]; },
-                [&](int i, int x) { return sk[TL * m + i][x] * ex(sb[TL * m + i][x] - rho(x)); },
-                [&](int s, int x, float val) {
-                    const float y = ex(rho(x) - sb[s][x]) * val;
-                    sV[s][x] += y;
-                    sU[s][x] -= sk[s][x] * y;
-                });
+        wg_gemm_v<TL * (m + 1), DK, TL>([&](int s, int i) { return down4<LC>(&sT[TL * m], i, s); },
+                [&](int i, int x) { return xcol4(sk, i, x); }, col_epi);
         __syncthreads();
     };
     pair_grads(std::integral_constant<int, 0>{});
