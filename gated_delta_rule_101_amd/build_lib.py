@@ -28,14 +28,15 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source scheduling strategies of the AMDGPU backend, chosen by
-# measurement (identical results in every case).  The pipelined chunk kernel
-# and the decode kernel run faster under max-ILP (B4 H32 T16384 forward
-# 1.52 -> 1.47 ms, 256 x 96 decode step 0.559 -> 0.530 ms); the backward
-# kernels run much slower under it (21 -> 29 ms) but faster under
-# max-memory-clause (21.0 -> 20.1 ms).  The others keep the default.
+# Per-source optimisation level and scheduling strategy of the AMDGPU
+# backend, chosen by measurement (identical results in every case).  The
+# pipelined chunk kernel and the decode kernel run faster under max-ILP
+# (B4 H32 T16384 forward 1.52 -> 1.47 ms, 256 x 96 decode step 0.559 -> 0.530
+# ms), and the chunk kernel again at -O2 (1.48 -> 1.43 ms; -O1 is slower);
+# the backward kernels run much slower under max-ILP (21 -> 29 ms) but faster
+# under max-memory-clause (21.0 -> 20.1 ms).  The others keep the defaults.
 SOURCE_FLAGS = {
-    "kda_chunk_pipe.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "kda_chunk_pipe.hip": ["-O2", "-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "kda_decode.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
     "kda_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
 }
