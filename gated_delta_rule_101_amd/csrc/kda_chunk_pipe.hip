@@ -61,6 +61,18 @@ constexpr int NCONS = 4;          // consumer waves: 16 value columns each
 constexpr int NTHREADS = 64 * (NPROD + NCONS);
 constexpr int WV = 16 * NCONS;    // value columns per workgroup
 constexpr int LDT = TILE;         // row stride (elements) of a stored 16x16 tile
+
+// Element offset of the four-element group c (0..3) of row t of a stored
+// 16x16 fp16 tile.  Rows are 32 bytes, so rows t and t + 8 fall in the same
+// banks; rows 8..15 hold their groups in the order c ^ 2, so a half-wave
+// writing rows 0..15 (groups 0,1 or 2,3) touches every bank once, and a
+// transposed read (rows 4g + a, all four groups of each) still does.
+__device__ __forceinline__ int tile_at(int t, int c) { return t * LDT + 4 * (c ^ ((t >> 2) & 2)); }
+// The lane's address for a transposed read of such a tile (the offset
+// h16::tr_offset gives for an unpermuted one, with the groups permuted).
+__device__ __forceinline__ int tile_tr_offset(int lane) {
+    return tile_at(4 * (lane >> 4) + ((lane & 15) >> 2), lane & 3);
+}
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr unsigned SPIN_LIMIT = 1u << 20;   // bound on every producer wait
 
@@ -99,7 +111,10 @@ struct alignas(16) PipeSmem {
     // beta of chunks c, c + 1, c + 2 (slot = chunk mod 3): written by a consumer
     // two iterations ahead, read by the producers one iteration ahead.
     alignas(16) float betas[3][C];
-    alignas(16) float LdT[NT][TILE][TILE];      // diagonal blocks of L (fp32): [m][col][row]
+    // diagonal blocks of L (fp32): [m][col][row]; rows padded to 80 bytes so
+    // that the 16 lanes of a quarter-wave reading 16 bytes of rows 0..15 hit
+    // distinct banks
+    alignas(16) float LdT[NT][TILE][TILE + 4];
     unsigned arrivals;                          // producer meeting counter
 };
 
@@ -239,21 +254,23 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 if constexpr (GBF && !GL) {
                     // as a matrix-core product: b^T = g^T Tri, Tri(s, t) = [s <= t].
                     // g goes through this tile's rows of the Qt staging area (rewritten
-                    // below), read back transposed: channels as rows, tokens as k-items.
+                    // below) as KT stored 16x16 tiles, read back transposed: channels
+                    // as rows, tokens as k-items.
+                    static_assert(KT * TILE * LDT <= TILE * LDK, "g staging fits the tile's Qt rows");
                     uint16_t *gs = reinterpret_cast<uint16_t *>(&st.Qt[TILE * m * LDK]);
 #pragma unroll
                     for (int blk = 0; blk < KT; ++blk)
-                        *reinterpret_cast<uint2 *>(&gs[r * LDK + 16 * blk + 4 * gq]) =
+                        *reinterpret_cast<uint2 *>(&gs[TILE * LDT * blk + tile_at(r, gq)]) =
                             live ? in.g[blk].a : make_uint2(0, 0);
                     lds_wave_sync();
                     i16x4 tri;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) tri[i] = (4 * gq + i <= r) ? (short)0x3F80 : (short)0;   // bf16 1.0
-                    const int tro = h16::tr_offset(lane, LDK);
+                    const int tro = tile_tr_offset(lane);
 #pragma unroll
                     for (int blk = 0; blk < KT; ++blk) {
                         const i16x4 gt = __builtin_bit_cast(
-                            i16x4, h16::tr4(reinterpret_cast<const _Float16 *>(&gs[16 * blk + tro])));
+                            i16x4, h16::tr4(reinterpret_cast<const _Float16 *>(&gs[TILE * LDT * blk + tro])));
                         const f32x4 bsum = BF::mma16(gt, tri, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                         for (int i = 0; i < 4; ++i) f[blk][i] = fast_exp2(bsum[i] * LOG2E);
@@ -430,15 +447,15 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             aq[i] = (r > row) ? 0.f : gq_d[i];             // keep s <= t
                             ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
                         }
-                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, M)][r * LDT + 4 * gq]) = h16::pack4(aq);
+                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, M)][tile_at(r, gq)]) = h16::pack4(aq);
                         *reinterpret_cast<f32x4 *>(&sm.LdT[M][r][4 * gq]) = ak;
                     }
 #pragma unroll
                     for (int d = 1; d <= M; ++d) {
                         const int n = M - d;
-                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, n)][r * LDT + 4 * gq]) =
+                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, n)][tile_at(r, gq)]) =
                             h16::pack4(gq_o[d - 1]);
-                        *reinterpret_cast<f16x4 *>(&st.LT[strict_index(M, n)][r * LDT + 4 * gq]) =
+                        *reinterpret_cast<f16x4 *>(&st.LT[strict_index(M, n)][tile_at(r, gq)]) =
                             h16::pack4(gk_o[d - 1] * bet);
                     }
                     lds_wave_sync();
@@ -473,7 +490,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
-                    *reinterpret_cast<f16x4 *>(&st.InvT[m][r * LDT + 4 * gq]) = h16::pack4(part);
+                    *reinterpret_cast<f16x4 *>(&st.InvT[m][tile_at(r, gq)]) = h16::pack4(part);
                 }
             }
             lds_barrier();
@@ -558,7 +575,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 if (w == 0 && c + 2 < nchunks) sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
 
                 // U = (I + L)^-1 Diag(beta) X, one tile at a time
-                const int tro = h16::tr_offset(lane, LDT);
+                const int tro = tile_tr_offset(lane);
                 f16x4 Uh[NT], Ul[NT];
                 f32x4 U[NT];
 #pragma unroll
