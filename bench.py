@@ -14,7 +14,10 @@ epilogue (alone over the training-shape reads, and fused into decode) under
 forward workloads (one head group B1 H8 T4096, a latency figure; the long
 sequence B1 H96 T131072) under "forward_secondary".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
-by HIP events on the launch stream.
+by HIP events on the launch stream, and `traffic`: the HBM bytes per launch
+that the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
+profiles/traffic.json, or null when the kernel's source has changed since
+(for the backward, one launch is one call: the sum over its five kernels).
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -108,6 +111,11 @@ CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk_pipe.hip", "gated_delt
                  "gated_delta_rule_101_amd/build_lib.py"]
 DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
                   "gated_delta_rule_101_amd/build_lib.py"]
+BWD_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_bwd.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
+               "gated_delta_rule_101_amd/build_lib.py"]
+# the five kernels of one backward call, in launch order
+BWD_KERNELS = ("kda_bwd_prep_kernel", "kda_bwd_states_kernel", "kda_bwd_dstates_kernel",
+               "kda_bwd_sgrads_kernel", "kda_bwd_intra_kernel")
 
 
 def stored_traffic(kernel: str, sources) -> "dict | None":
@@ -348,17 +356,23 @@ def bench_backward(kda, reps=3):
     stream = torch.cuda.current_stream()
     fn = lambda: kda.kda_chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None, dO, None,  # noqa: E731
                                    want_dS0=False, workspace=ws)
+    if reps == 0:   # the counter pass: one call, nothing timed
+        fn()
+        torch.cuda.synchronize()
+        return None
     wall, ker = time_launches(fn, reps, 1, stream)
     flops = bwd_flops(w.B, w.T, w.H, w.dk, w.dv)
     nbytes = bwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 4)
     tfs = flops / ker / 1e12
     log(f"[bench] backward {wall / reps * 1e3:.3f} ms (kernels {ker * 1e3:.3f} ms), {tfs:.1f} TFLOP/s, "
         f"{w.B * w.T / (wall / reps):.3e} tokens/s")
+    rec = stored_traffic("kda_chunk_bwd", BWD_SOURCES)
     return {"workload": w.name + "_bwd", "ms": round(wall / reps * 1e3, 4),
             "tokens_per_s": round(w.B * w.T / (wall / reps), 1),
             "algorithmic_flop": flops, "algorithmic_bytes": nbytes,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(tfs / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": rec["hbm_bytes_per_launch"] if rec else None}}
 
 
 def cpu_baseline(w, d, batch=32):
@@ -411,7 +425,8 @@ COPY_BYTES = 1 << 30   # the calibration copy moves 1 GiB each way
 def profile_pass(kda, reps=3):
     """A short run for `rocprofv3 --pmc`: a plain device copy of known size
     (calibrates the byte counters), then the chunked forward and the decode
-    step of the benchmark workloads, `reps` launches each."""
+    step of the benchmark workloads, `reps` launches each, and one backward
+    call (its five kernels) on the training shape."""
     import torch
     from kda_workloads import configs, gen_torch
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -425,6 +440,8 @@ def profile_pass(kda, reps=3):
     torch.cuda.empty_cache()
     bench_decode(kda, 1)
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    bench_backward(kda, reps=0)
 
 
 def _counter_rows(directory, counter):
@@ -471,6 +488,20 @@ def counters_to_traffic(fetch_dir, write_dir, out=TRAFFIC_FILE):
         rec[kernel] = {"source_hash": kernel_source_hash(sources), "fetch_bytes_per_launch": round(fb),
                        "write_bytes_per_launch": round(wb), "hbm_bytes_per_launch": round(fb + wb),
                        "dispatches": len(f)}
+    # the backward: bytes of one call, the sum over its five kernels
+    parts = {}
+    for part in BWD_KERNELS:
+        f, w_ = _per_dispatch(fr, part), _per_dispatch(wr, part)
+        if f and w_:
+            parts[part] = (sum(f) / len(f) * 1024.0 * cf, sum(w_) / len(w_) * 1024.0 * cw)
+    if len(parts) == len(BWD_KERNELS):
+        fb = sum(x[0] for x in parts.values())
+        wb = sum(x[1] for x in parts.values())
+        rec["kda_chunk_bwd"] = {"source_hash": kernel_source_hash(BWD_SOURCES),
+                                "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                                "hbm_bytes_per_launch": round(fb + wb),
+                                "per_kernel": {k: {"fetch_bytes": round(a), "write_bytes": round(b)}
+                                               for k, (a, b) in parts.items()}}
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec, indent=1))

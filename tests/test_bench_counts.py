@@ -49,3 +49,52 @@ def test_backward_counts():
     # bf16 q, k, v, g, beta and fp32 dO read; fp32 dq, dk, dg (d each), dv (d), dbeta written
     per = 2 * 384 + 2 * 129 + 4 * 128 + 4 * (3 * 128 + 128 + 1)
     assert bench.bwd_bytes(4, 16384, 32, 128, 128, 2, 2, 4) == 4 * 16384 * 32 * per
+
+
+def _write_counters(path, counter, rows):
+    """A rocprofv3 counter_collection.csv with the columns the benchmark reads."""
+    import csv
+    path.mkdir(parents=True, exist_ok=True)
+    with open(path / "p_counter_collection.csv", "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for disp, name, kib in rows:
+            # counters are reported per shader engine: split each value in two rows
+            wr.writerow([disp, name, counter, kib / 2])
+            wr.writerow([disp, name, counter, kib / 2])
+
+
+def test_counters_to_traffic(tmp_path):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch, summed over rows) become
+    bytes per launch, scaled by what the calibration copy of 1 GiB reads, and
+    the backward's five kernels add up to one call."""
+    import json
+    copy = "void copyBuffer(...)"
+    fwd = "kda_chunk_pipe_kernel<128, true, false, false>"
+    fetch = [(1, copy, 524288.0), (2, fwd, 1000.0), (3, fwd, 3000.0)]
+    write = [(1, copy, 1048576.0), (2, fwd, 500.0), (3, fwd, 500.0)]
+    for i, part in enumerate(bench.BWD_KERNELS):
+        fetch.append((10 + i, part + "<128, 128>", 100.0 * (i + 1)))
+        write.append((10 + i, part + "<128, 128>", 10.0 * (i + 1)))
+    _write_counters(tmp_path / "f", "FETCH_SIZE", fetch)
+    _write_counters(tmp_path / "w", "WRITE_SIZE", write)
+    out = tmp_path / "traffic.json"
+    bench.counters_to_traffic(str(tmp_path / "f"), str(tmp_path / "w"), out=str(out))
+    rec = json.loads(out.read_text())
+    assert rec["calibration"]["fetch_scale"] == 2.0 and rec["calibration"]["write_scale"] == 1.0
+    f = rec["kda_chunk_fwd"]
+    assert f["fetch_bytes_per_launch"] == 2 * 2000 * 1024 and f["write_bytes_per_launch"] == 500 * 1024
+    assert f["dispatches"] == 2 and f["source_hash"] == bench.kernel_source_hash(bench.CHUNK_SOURCES)
+    assert "kda_decode_step" not in rec   # no decode dispatch in these files
+    b = rec["kda_chunk_bwd"]
+    assert b["fetch_bytes_per_launch"] == 2 * 1500 * 1024 and b["write_bytes_per_launch"] == 150 * 1024
+    assert b["hbm_bytes_per_launch"] == (3000 + 150) * 1024
+    assert b["source_hash"] == bench.kernel_source_hash(bench.BWD_SOURCES)
+    # a stored record counts only while the source hash matches
+    orig = bench.TRAFFIC_FILE
+    try:
+        bench.TRAFFIC_FILE = str(out)
+        assert bench.stored_traffic("kda_chunk_bwd", bench.BWD_SOURCES)["hbm_bytes_per_launch"] == 3150 * 1024
+        assert bench.stored_traffic("kda_chunk_bwd", bench.DECODE_SOURCES) is None
+    finally:
+        bench.TRAFFIC_FILE = orig
