@@ -550,10 +550,12 @@ template <int DK, int DV, typename OT>
 __global__ void __launch_bounds__(NTH)
 kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, int NC)
 {
-    // S and dS' are taken half of their dk rows at a time, so the workgroup
-    // fits twice per CU.
-    constexpr int LV = DV + 4, DH = DK / 2;
-    __shared__ alignas(16) float sS[DH][LV], sY1[BC][LV], sY2[BC][LV];
+    // dO, dU and U stay in LDS for the whole chunk; S and then dS' pass
+    // through DQ of their dk rows at a time, so that each row of both is read
+    // from memory once and the workgroup fits twice per CU.
+    constexpr int LV = DV + 4, DQ = 32;
+    static_assert(DK % DQ == 0, "row slices of S");
+    __shared__ alignas(16) float sS[DQ][LV], sY1[BC][LV], sY2[BC][LV], sY3[BC][LV];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, bb = bh / H, h = bh % H;
     const size_t ch = (size_t)bh * NC + c;
@@ -567,61 +569,67 @@ kda_bwd_sgrads_kernel(const OT *__restrict__ dO, BwdWorkspace ws, int T, int H, 
         const bool live = t < T;
         st4(&sY1[r][j], live ? f32x4{dv4[0], dv4[1], dv4[2], dv4[3]} : f32x4{0.f, 0.f, 0.f, 0.f});
         st4(&sY2[r][j], ld4(&ws.dU[ch * BC * DV + e]));
+        st4(&sY3[r][j], ld4(&ws.U[ch * BC * DV + e]));
     });
-    for (int half = 0; half < 2; ++half) {
-        const int x0 = half * DH;
-        for_elems4<DH * DV>([&](int e) { st4(&sS[e / DV][e % DV], ld4(&ws.h[ch * DK * DV + (size_t)x0 * DV + e])); });
-        __syncthreads();
-        // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1), key columns x0..x0+DH-1
-        // computed transposed (key columns as rows) so each lane stores four
-        // consecutive key columns of one token row
-        wg_gemm_v<DH, 2 * BC, DV>([&](int x, int j) { return ld4(&sS[x][j]); },
-                                  [&](int j, int i) { return i < BC ? ld4(&sY1[i][j]) : ld4(&sY2[i - BC][j]); },
-                                 [&](int x, int i, f32x4 v) {
-                                     if (i < BC) st4(&ws.dQt[(ch * BC + i) * DK + x0 + x], v);
-                                     else st4(&ws.dW[(ch * BC + i - BC) * DK + x0 + x], -v);
-                                 });
-        __syncthreads();
-        if (half == 0) continue;
-        // U replaces dU (both halves of dW are done)
-        for_elems4<BC * DV>([&](int e) { st4(&sY2[e / DV][e % DV], ld4(&ws.U[ch * BC * DV + e])); });
-        __syncthreads();
-        // dA_qk = tril(dO U^T)
-        wg_gemm_v<BC, BC, DV>([&](int s, int j) { return ld4(&sY2[s][j]); }, [&](int j, int i) { return ld4(&sY1[i][j]); },
-                             [&](int s, int i, f32x4 v) {
+    for_elems4<DQ * DV>([&](int e) { st4(&sS[e / DV][e % DV], ld4(&ws.h[ch * DK * DV + e])); });
+    __syncthreads();
+    // dA_qk = tril(dO U^T)
+    wg_gemm_v<BC, BC, DV>([&](int s, int j) { return ld4(&sY3[s][j]); }, [&](int j, int i) { return ld4(&sY1[i][j]); },
+                         [&](int s, int i, f32x4 v) {
 #pragma unroll
-                                 for (int u = 0; u < 4; ++u) v[u] = s + u <= i ? v[u] : 0.f;
-                                 st4(&ws.dAqk[(ch * BC + i) * BC + s], v);
-                             });
-    }
-    for (int hh = 0; hh < 2; ++hh) {
-        // the upper half of S is still in LDS; the lower half is reloaded
-        const int half = 1 - hh, x0 = half * DH;
-        if (half == 0) {
-            for_elems4<DH * DV>([&](int e) { st4(&sS[e / DV][e % DV], ld4(&ws.h[ch * DK * DV + e])); });
+                             for (int u = 0; u < 4; ++u) v[u] = s + u <= i ? v[u] : 0.f;
+                             st4(&ws.dAqk[(ch * BC + i) * BC + s], v);
+                         });
+    // each slice's dS' rows, and the next slice's S rows, are requested into
+    // registers when the slice starts, ahead of the products that precede their use
+    constexpr int TPR = NTH / DQ, CPT = DV / TPR, PS = DQ * DV / (4 * NTH);
+    static_assert(CPT % 4 == 0, "whole 16-byte units per thread");
+    const int rr = tid / TPR, j0 = (tid % TPR) * CPT;
+    f32x4 pS[PS];
+    for (int x0 = 0; x0 < DK; x0 += DQ) {
+        if (x0 > 0) {
+#pragma unroll
+            for (int i = 0; i < PS; ++i) {
+                const int e = 4 * (tid + NTH * i);
+                st4(&sS[e / DV][e % DV], pS[i]);
+            }
             __syncthreads();
         }
+        f32x4 pD[CPT / 4];
+#pragma unroll
+        for (int j = 0; j < CPT / 4; ++j) pD[j] = ld4(ws.dh + ch * DK * DV + (size_t)(x0 + rr) * DV + j0 + 4 * j);
+        if (x0 + DQ < DK) {
+#pragma unroll
+            for (int i = 0; i < PS; ++i)
+                pS[i] = ld4(&ws.h[ch * DK * DV + (size_t)(x0 + DQ) * DV + 4 * (tid + NTH * i)]);
+        }
+        // dQ~ = dO S^T (rows 0..BC-1), dW = -dU S^T (rows BC..2BC-1), key columns x0..x0+DQ-1
+        // computed transposed (key columns as rows) so each lane stores four
+        // consecutive key columns of one token row
+        wg_gemm_v<DQ, 2 * BC, DV>([&](int x, int j) { return ld4(&sS[x][j]); },
+                                  [&](int j, int i) { return i < BC ? ld4(&sY1[i][j]) : ld4(&sY2[i - BC][j]); },
+                                  [&](int x, int i, f32x4 v) {
+                                      if (i < BC) st4(&ws.dQt[(ch * BC + i) * DK + x0 + x], v);
+                                      else st4(&ws.dW[(ch * BC + i - BC) * DK + x0 + x], -v);
+                                  });
+        __syncthreads();
         // dGamma_C = rowsum(S . dS') with TPR threads per row; dS' replaces S
         // element by element
         {
-            constexpr int TPR = NTH / DH, CPT = DV / TPR;
-            const int r = tid / TPR, j0 = (tid % TPR) * CPT;
-            const float4 *src = reinterpret_cast<const float4 *>(ws.dh + ch * DK * DV + (size_t)(x0 + r) * DV + j0);
             float p = 0.f;
 #pragma unroll
             for (int j = 0; j < CPT / 4; ++j) {
-                const float4 d = src[j];
-                float *sp = &sS[r][j0 + 4 * j];
-                p += sp[0] * d.x + sp[1] * d.y + sp[2] * d.z + sp[3] * d.w;
-                sp[0] = d.x; sp[1] = d.y; sp[2] = d.z; sp[3] = d.w;
+                const f32x4 sv = ld4(&sS[rr][j0 + 4 * j]);
+                p += sv[0] * pD[j][0] + sv[1] * pD[j][1] + sv[2] * pD[j][2] + sv[3] * pD[j][3];
+                st4(&sS[rr][j0 + 4 * j], pD[j]);
             }
 #pragma unroll
             for (int m = 1; m < TPR; m <<= 1) p += __shfl_xor(p, m, TPR);
-            if (tid % TPR == 0) ws.dGam[ch * DK + x0 + r] = p;
+            if (tid % TPR == 0) ws.dGam[ch * DK + x0 + rr] = p;
         }
         __syncthreads();
-        // dK-bar = U dS'^T, key columns x0..x0+DH-1
-        wg_gemm_v<DH, BC, DV>([&](int x, int j) { return ld4(&sS[x][j]); }, [&](int j, int i) { return ld4(&sY2[i][j]); },
+        // dK-bar = U dS'^T, key columns x0..x0+DQ-1
+        wg_gemm_v<DQ, BC, DV>([&](int x, int j) { return ld4(&sS[x][j]); }, [&](int j, int i) { return ld4(&sY3[i][j]); },
                              [&](int x, int i, f32x4 v) { st4(&ws.dKb[(ch * BC + i) * DK + x0 + x], v); });
         __syncthreads();
     }
