@@ -136,6 +136,34 @@ __device__ __forceinline__ void wg_gemm_v(FA4 A4, FB4 B4, FE epi4)
     }
 }
 
+// As wg_gemm_v for two products that share their B operand, A(i, k) B(k, j)
+// and A2(i, k) B(k, j): each B fetch feeds both, one tile per wave at a time
+// with the two products as its two accumulation chains, and epi4(i, j, v, w)
+// receives both results for rows i..i+3 of column j.
+template <int M, int N, int K, typename FA4, typename FA24, typename FB4, typename FE>
+__device__ __forceinline__ void wg_gemm_v2(FA4 A4, FA24 A24, FB4 B4, FE epi4)
+{
+    static_assert(M % 16 == 0 && N % 16 == 0 && K % 16 == 0, "tile shape");
+    constexpr int TN = N / 16, NT = (M / 16) * TN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    for (int t = wave; t < NT; t += NW) {
+        const int i0 = (t / TN) * 16, j0 = (t % TN) * 16;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < K / 16; ++g) {
+            const int k = 16 * g + 4 * kq;
+            const f32x4 a0 = A4(i0 + r16, k), a1 = A24(i0 + r16, k), b = B4(k, j0 + r16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[e], b[e], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[e], b[e], acc1, 0, 0, 0);
+            }
+        }
+        epi4(i0 + 4 * kq, j0 + r16, acc0, acc1);
+    }
+}
+
 // Four consecutive rows k..k+3 of column c of a row-major LDS array: the
 // operand of wg_gemm_v when it is stored with k along the rows.
 template <int L>
@@ -777,29 +805,19 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
             for (int u = 0; u < 4; ++u) out[u] = sk[s + u][x] * ex(rx - sb[s + u][x]);
             return out;
         };
-        // dq += row(dA_qk, k);  db += q . row(dA_qk, k)
-        wg_gemm_v<TL, DK, TL * (m + 1)>([&](int i, int s) { return ld4(&sdA[TL * m + i][s]); }, kcol4,
-                [&](int i, int x, f32x4 v) {
+        // dq += row(dA_qk, k), dk += row(dA_kk0, k), db += q . row(dA_qk, k) +
+        // k . row(dA_kk0, k): both products share the scaled keys
+        wg_gemm_v2<TL, DK, TL * (m + 1)>([&](int i, int s) { return ld4(&sdA[TL * m + i][s]); },
+                [&](int i, int s) { return ld4(&sT[TL * m + i][s]); }, kcol4,
+                [&](int i, int x, f32x4 v, f32x4 w) {
                     const float rx = rho(x);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int r = TL * m + i + u;
-                        const float y = ex(sb[r][x] - rx) * v[u];
+                        const float e = ex(sb[r][x] - rx), y = e * v[u], z = e * w[u];
                         sP[r][x] += y;
-                        sU[r][x] += sq[r][x] * y;
-                    }
-                });
-        __syncthreads();
-        // dk += row(dA_kk0, k);  db += k . row(dA_kk0, k)
-        wg_gemm_v<TL, DK, TL * (m + 1)>([&](int i, int s) { return ld4(&sT[TL * m + i][s]); }, kcol4,
-                [&](int i, int x, f32x4 v) {
-                    const float rx = rho(x);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int r = TL * m + i + u;
-                        const float y = ex(sb[r][x] - rx) * v[u];
-                        sV[r][x] += y;
-                        sU[r][x] += sk[r][x] * y;
+                        sV[r][x] += z;
+                        sU[r][x] += sq[r][x] * y + sk[r][x] * z;
                     }
                 });
         __syncthreads();
@@ -821,13 +839,13 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
                 sU[s + u][x] -= sk[s + u][x] * y;
             }
         };
-        // dk += col(dA_qk, q);  db -= k . col(dA_qk, q)
-        wg_gemm_v<TL * (m + 1), DK, TL>([&](int s, int i) { return down4<LC>(&sdA[TL * m], i, s); },
-                [&](int i, int x) { return xcol4(sq, i, x); }, col_epi);
-        __syncthreads();
-        // dk += col(dA_kk0, k);  db -= k . col(dA_kk0, k)
-        wg_gemm_v<TL * (m + 1), DK, TL>([&](int s, int i) { return down4<LC>(&sT[TL * m], i, s); },
-                [&](int i, int x) { return xcol4(sk, i, x); }, col_epi);
+        // dk += col(dA_qk, q) + col(dA_kk0, k);  db -= k . (the same): one
+        // product over the two k-ranges (items 0..TL-1 from dA_qk and q,
+        // TL..2TL-1 from dA_kk0 and k; a branch at a multiple of 16, uniform)
+        static_assert(TL == 16, "one 16-item block per k-range");
+        wg_gemm_v<TL * (m + 1), DK, 2 * TL>(
+                [&](int s, int i) { return i < TL ? down4<LC>(&sdA[TL * m], i, s) : down4<LC>(&sT[TL * m], i - TL, s); },
+                [&](int i, int x) { return i < TL ? xcol4(sq, i, x) : xcol4(sk, i - TL, x); }, col_epi);
         __syncthreads();
     };
     pair_grads(std::integral_constant<int, 0>{});
