@@ -843,9 +843,21 @@ kda_bwd_intra_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const Q
         // product over the two k-ranges (items 0..TL-1 from dA_qk and q,
         // TL..2TL-1 from dA_kk0 and k; a branch at a multiple of 16, uniform)
         static_assert(TL == 16, "one 16-item block per k-range");
-        wg_gemm_v<TL * (m + 1), DK, 2 * TL>(
-                [&](int s, int i) { return i < TL ? down4<LC>(&sdA[TL * m], i, s) : down4<LC>(&sT[TL * m], i - TL, s); },
-                [&](int i, int x) { return i < TL ? xcol4(sq, i, x) : xcol4(sk, i - TL, x); }, col_epi);
+        auto colA = [&](int s, int i) {
+            return i < TL ? down4<LC>(&sdA[TL * m], i, s) : down4<LC>(&sT[TL * m], i - TL, s);
+        };
+        auto colB = [&](int i, int x) { return i < TL ? xcol4(sq, i, x) : xcol4(sk, i - TL, x); };
+        if constexpr (m == 0) {
+            wg_gemm_v<TL, DK, 2 * TL>(colA, colB, col_epi);
+        } else {
+            // the two 16-row blocks of the output share the scaled operand
+            static_assert(m == 1, "two row tiles per chunk");
+            wg_gemm_v2<TL, DK, 2 * TL>(colA, [&](int s, int i) { return colA(s + TL, i); }, colB,
+                    [&](int s, int x, f32x4 v, f32x4 w) {
+                        col_epi(s, x, v);
+                        col_epi(s + TL, x, w);
+                    });
+        }
         __syncthreads();
     };
     pair_grads(std::integral_constant<int, 0>{});
