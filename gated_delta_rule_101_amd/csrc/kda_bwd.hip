@@ -454,9 +454,12 @@ kda_bwd_states_kernel(const float *__restrict__ S0, const QT *__restrict__ k, Bw
                                   }
                               });
         __syncthreads();
-        // S <- Diag(Gamma_C) S + K-bar^T U
-        wg_gemm<DK, SW, BC>([&](int x, int r) { return sKb[r][x]; }, [&](int r, int j) { return sU[r][j]; },
-                            [&](int x, int j, float val) { sS[x][j] = sG[x] * sS[x][j] + val; });
+        // S <- Diag(Gamma_C) S + K-bar^T U (both operands gathered four token rows at a time)
+        wg_gemm_v<DK, SW, BC>([&](int x, int r) { return down4<LK>(sKb, r, x); }, [&](int r, int j) { return down4<LS>(sU, r, j); },
+                              [&](int x, int j, f32x4 v) {
+#pragma unroll
+                                  for (int u = 0; u < 4; ++u) sS[x + u][j] = sG[x + u] * sS[x + u][j] + v[u];
+                              });
         __syncthreads();
     }
 }
@@ -559,10 +562,15 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         }
         __syncthreads();
         if (c > 0) fetch(c - 1);
-        // dS = Diag(Gamma_C) dS' + (Gamma . Q)^T dO - W^T dU
-        wg_gemm<DK, SW, 2 * BC>([&](int x, int r) { return r < BC ? sX1[r][x] : -sX2[r - BC][x]; },
-                                [&](int r, int j) { return r < BC ? sO[r][j] : sdU[r - BC][j]; },
-                                [&](int x, int j, float val) { sD[x][j] = sG[x] * sD[x][j] + val; });
+        // dS = Diag(Gamma_C) dS' + (Gamma . Q)^T dO - W^T dU (operands gathered four
+        // token rows at a time; the branch at BC, a multiple of 16, is uniform)
+        static_assert(BC % 16 == 0, "uniform k-range branch");
+        wg_gemm_v<DK, SW, 2 * BC>([&](int x, int r) { return r < BC ? down4<LK>(sX1, r, x) : -down4<LK>(sX2, r - BC, x); },
+                                  [&](int r, int j) { return r < BC ? down4<LS>(sO, r, j) : down4<LS>(sdU, r - BC, j); },
+                                  [&](int x, int j, f32x4 v) {
+#pragma unroll
+                                      for (int u = 0; u < 4; ++u) sD[x + u][j] = sG[x + u] * sD[x + u][j] + v[u];
+                                  });
         __syncthreads();
     }
     if (dS0)
