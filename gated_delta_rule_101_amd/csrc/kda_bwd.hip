@@ -514,12 +514,18 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
     if (NC > 0) fetch(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const size_t ch = (size_t)bh * NC + c;
+        // Gamma . Q is staged after the dU product (it replaces K-bar in LDS);
+        // computed now, it frees the prefetch registers for the next chunk's loads
+        f32x4 qg[PE];
 #pragma unroll
         for (int i = 0; i < PE; ++i) {
             const int e = 4 * (tid + NTH * i), r = e / DK, x = e % DK;
             f32x4 kb;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) kb[u] = pk[i][u] * ex(pbl[i][u] - pb[i][u]);   // K-bar
+            for (int u = 0; u < 4; ++u) {
+                kb[u] = pk[i][u] * ex(pbl[i][u] - pb[i][u]);   // K-bar
+                qg[i][u] = pq[i][u] * ex(pb[i][u]);
+            }
             st4(&sX1[r][x], kb);
             st4(&sX2[r][x], pw[i]);
             if (i == 0 && tid < DK / 4)   // group 0 of threads < DK / 4 is channels 4 tid .. 4 tid + 3
@@ -537,6 +543,7 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
             st4(&sA[e / BC][e % BC], pa[i]);
         }
         __syncthreads();
+        if (c > 0) fetch(c - 1);
         for_elems4<DK * SW>([&](int e) {
             const int r = e / SW, j = e % SW;
             *reinterpret_cast<f32x4 *>(&ws.dh[(ch * DK + r) * DV + col0 + j]) = ld4(&sD[r][j]);
@@ -555,13 +562,9 @@ kda_bwd_dstates_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
 #pragma unroll
         for (int i = 0; i < PE; ++i) {   // Gamma . Q replaces K-bar
             const int e = 4 * (tid + NTH * i);
-            f32x4 qg;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) qg[u] = pq[i][u] * ex(pb[i][u]);
-            st4(&sX1[e / DK][e % DK], qg);
+            st4(&sX1[e / DK][e % DK], qg[i]);
         }
         __syncthreads();
-        if (c > 0) fetch(c - 1);
         // dS = Diag(Gamma_C) dS' + (Gamma . Q)^T dO - W^T dU (operands gathered four
         // token rows at a time; the branch at BC, a multiple of 16, is uniform)
         static_assert(BC % 16 == 0, "uniform k-range branch");
