@@ -113,6 +113,20 @@ DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_r
                   "gated_delta_rule_101_amd/build_lib.py"]
 BWD_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_bwd.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
                "gated_delta_rule_101_amd/build_lib.py"]
+VERIFY_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_verify.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
+                  "gated_delta_rule_101_amd/build_lib.py"]
+EPILOGUE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_epilogue.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
+                    "gated_delta_rule_101_amd/build_lib.py"]
+# kernel record -> (substrings its rocprofv3 kernel name must all contain, sources);
+# verify and commit are the two instantiations of one tile kernel (its last
+# template argument), the output epilogue is the stand-alone one
+SINGLE_KERNELS = (
+    ("kda_chunk_fwd", ("kda_chunk_pipe_kernel",), CHUNK_SOURCES),
+    ("kda_decode_step", ("kda_decode_kernel",), DECODE_SOURCES),
+    ("kda_verify_step", ("kda_verify_tile_kernel<", "false>("), VERIFY_SOURCES),
+    ("kda_commit_step", ("kda_verify_tile_kernel<", "true>("), VERIFY_SOURCES),
+    ("kda_output_gate", ("kda_output_gate_kernel",), EPILOGUE_SOURCES),
+)
 # the five kernels of one backward call, in launch order
 BWD_KERNELS = ("kda_bwd_prep_kernel", "kda_bwd_states_kernel", "kda_bwd_dstates_kernel",
                "kda_bwd_sgrads_kernel", "kda_bwd_intra_kernel")
@@ -288,14 +302,14 @@ def bench_speculative(kda, reps, K=16):
         wall, ker = time_launches(fn, reps, 2, stream)
         gbs = nbytes * reps / wall / 1e9
         log(f"[bench] {name} {wall / reps * 1e3:.3f} ms (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
-        out[name] = {"ms": round(wall / reps * 1e3, 4), "GB/s": round(gbs, 1),
-                     "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}
+        out[name] = {"ms": round(wall / reps * 1e3, 4), "GB/s": round(gbs, 1), "algorithmic_bytes": nbytes,
+                     "roofline": roofline(nbytes, ker, stored_traffic(f"kda_{name}_step", VERIFY_SOURCES))}
     return out
 
 
-def bench_epilogue(kda, reps=10):
+def bench_epilogue(kda, reps=10, fused=True):
     """The output epilogue over the training-shape reads (float32 o, bf16
-    logits, float32 y), and the decode step with the epilogue fused."""
+    logits, float32 y), and (`fused`) the decode step with the epilogue fused."""
     import torch
     from kda_workloads import configs, gen_torch
     w = configs.TRAIN_BF16
@@ -314,8 +328,11 @@ def bench_epilogue(kda, reps=10):
     log(f"[bench] output_gate {wall / reps * 1e3:.3f} ms (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
     out = {"output_gate": {"workload": f"kda_output_gate_B{w.B}_T{w.T}_H{w.H}_dv{w.dv}_f32o_bf16z",
                            "ms": round(wall / reps * 1e3, 4), "GB/s": round(gbs, 1),
-                           "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}}
+                           "algorithmic_bytes": nbytes,
+                           "roofline": roofline(nbytes, ker, stored_traffic("kda_output_gate", EPILOGUE_SOURCES))}}
     del o, z, y
+    if not fused:
+        return out
 
     dw = configs.DECODE_BF16
     S = gen_torch.decode_initial_state(dw)
@@ -425,8 +442,9 @@ COPY_BYTES = 1 << 30   # the calibration copy moves 1 GiB each way
 def profile_pass(kda, reps=3):
     """A short run for `rocprofv3 --pmc`: a plain device copy of known size
     (calibrates the byte counters), then the chunked forward and the decode
-    step of the benchmark workloads, `reps` launches each, and one backward
-    call (its five kernels) on the training shape."""
+    step of the benchmark workloads, `reps` launches each, verify and commit
+    of the speculative workload and the output epilogue (three launches
+    each), and one backward call (its five kernels) on the training shape."""
     import torch
     from kda_workloads import configs, gen_torch
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -439,6 +457,8 @@ def profile_pass(kda, reps=3):
     del d
     torch.cuda.empty_cache()
     bench_decode(kda, 1)
+    bench_speculative(kda, 1)
+    bench_epilogue(kda, reps=1, fused=False)   # the fused decode would mix into the decode record
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     bench_backward(kda, reps=0)
@@ -456,10 +476,10 @@ def _counter_rows(directory, counter):
     return rows
 
 
-def _per_dispatch(rows, name_part):
+def _per_dispatch(rows, *name_parts):
     acc = {}
     for r in rows:
-        if name_part in r["Kernel_Name"]:
+        if all(p in r["Kernel_Name"] for p in name_parts):
             acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
     return list(acc.values())
 
@@ -478,9 +498,8 @@ def counters_to_traffic(fetch_dir, write_dir, out=TRAFFIC_FILE):
     cw = COPY_BYTES / (max(copy_w) * 1024.0)
     rec = {"calibration": {"copy_bytes": COPY_BYTES, "fetch_KiB": max(copy_f), "write_KiB": max(copy_w),
                            "fetch_scale": round(cf, 4), "write_scale": round(cw, 4)}}
-    for kernel, part, sources in (("kda_chunk_fwd", "kda_chunk_pipe_kernel", CHUNK_SOURCES),
-                                  ("kda_decode_step", "kda_decode_kernel", DECODE_SOURCES)):
-        f, w_ = _per_dispatch(fr, part), _per_dispatch(wr, part)
+    for kernel, parts, sources in SINGLE_KERNELS:
+        f, w_ = _per_dispatch(fr, *parts), _per_dispatch(wr, *parts)
         if not f or not w_:
             continue
         fb = sum(f) / len(f) * 1024.0 * cf

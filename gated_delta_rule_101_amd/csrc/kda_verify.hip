@@ -110,6 +110,11 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         // others enter as identity tokens (zero key, value, decay and beta)
         const int n = COMMIT ? max(0, min(accepted[b], K)) : K;
         auto row = [&](int t) { return ((size_t)b * K + t) * H + h; };   // draft token t of (b, h)
+        // drafts past the applied ones load the last applied draft's row (row 0
+        // when none is applied; K >= 1) and are zeroed: their lines are already
+        // being fetched, so commit reads only the accepted prefix from memory
+        const int t_last = n > 0 ? n - 1 : 0;
+        auto live_row = [&](int t) { return row(t < n ? t : t_last); };
 
         // this lane's draft values for X = V - K~ S (C layout: drafts 4 kq + i)
         float vv[4][NC];
@@ -117,7 +122,7 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         for (int i = 0; i < 4; ++i) {
             const int t = 4 * kq + i;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) vv[i][c] = ld_live(v, row(t < K ? t : K - 1) * DV + col0 + c, t < n);
+            for (int c = 0; c < NC; ++c) vv[i][c] = ld_live(v, live_row(t) * DV + col0 + c, t < n);
         }
         // drafts: raw q, k, g into LDS by the whole workgroup (g parked in sKh),
         // then the cumsum of g down each key channel and the scaled rows
@@ -129,7 +134,7 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
         for (int it = 0; it < KT * DK / (4 * NTH); ++it) {
             const int e = tid + NTH * it, t = e / (DK / 4), x = 4 * (e % (DK / 4));
             const bool live = t < n;
-            const size_t i = row(t < K ? t : 0) * DK + x;
+            const size_t i = live_row(t) * DK + x;
             Raw4<QT> rq, rk;
             Raw4<GT> rg;
             if constexpr (!COMMIT) rq.load(q + i);
@@ -151,7 +156,7 @@ kda_verify_tile_kernel(const QT *__restrict__ q, const QT *__restrict__ k, const
             *reinterpret_cast<f32x4 *>(&sKt[t][x]) = vk;
             *reinterpret_cast<f32x4 *>(&sKh[t][x]) = vg;
         }
-        if (tid < KT) sbeta[tid] = ld_live(beta, row(tid < K ? tid : K - 1), tid < n);
+        if (tid < KT) sbeta[tid] = ld_live(beta, live_row(tid), tid < n);
         __syncthreads();
         if (tid < DK) {
             const int x = tid;

@@ -211,7 +211,8 @@ kda_status_t kda_verify_step(const void *q, const void *k, const void *v,
  * accepted[b] tokens of each sequence.  No output is written.  S must not
  * overlap k, v, g, beta or accepted.  A sequence with no accepted token
  * keeps its state bit for bit.  Up to 16 drafts run as one tile on the
- * matrix cores (S read once, updated in registers, written once); with
+ * matrix cores (S read once, updated in registers, written once; of the
+ * drafts only the accepted prefix is read from memory); with
  * KDA_BF16 drafts the products take two-term fp16 operands (about 22
  * significant bits; |S| below 65504), with KDA_F32 drafts float32 operands.
  */

@@ -73,6 +73,10 @@ def test_counters_to_traffic(tmp_path):
     fwd = "kda_chunk_pipe_kernel<128, true, false, false>"
     fetch = [(1, copy, 524288.0), (2, fwd, 1000.0), (3, fwd, 3000.0)]
     write = [(1, copy, 1048576.0), (2, fwd, 500.0), (3, fwd, 500.0)]
+    ver = "void kda::kda_verify_tile_kernel<128, 128, unsigned short, unsigned short, float, false>(float*)"
+    com = "void kda::kda_verify_tile_kernel<128, 128, unsigned short, unsigned short, float, true>(float*)"
+    fetch += [(4, ver, 100.0), (5, com, 300.0), (6, "kda_output_gate_kernel<float>", 50.0)]
+    write += [(4, ver, 10.0), (5, com, 30.0), (6, "kda_output_gate_kernel<float>", 5.0)]
     for i, part in enumerate(bench.BWD_KERNELS):
         fetch.append((10 + i, part + "<128, 128>", 100.0 * (i + 1)))
         write.append((10 + i, part + "<128, 128>", 10.0 * (i + 1)))
@@ -86,6 +90,11 @@ def test_counters_to_traffic(tmp_path):
     assert f["fetch_bytes_per_launch"] == 2 * 2000 * 1024 and f["write_bytes_per_launch"] == 500 * 1024
     assert f["dispatches"] == 2 and f["source_hash"] == bench.kernel_source_hash(bench.CHUNK_SOURCES)
     assert "kda_decode_step" not in rec   # no decode dispatch in these files
+    # the two instantiations of the tile kernel are told apart by their last template argument
+    assert rec["kda_verify_step"]["hbm_bytes_per_launch"] == (2 * 100 + 10) * 1024
+    assert rec["kda_commit_step"]["hbm_bytes_per_launch"] == (2 * 300 + 30) * 1024
+    assert rec["kda_verify_step"]["source_hash"] == bench.kernel_source_hash(bench.VERIFY_SOURCES)
+    assert rec["kda_output_gate"]["hbm_bytes_per_launch"] == (2 * 50 + 5) * 1024
     b = rec["kda_chunk_bwd"]
     assert b["fetch_bytes_per_launch"] == 2 * 1500 * 1024 and b["write_bytes_per_launch"] == 150 * 1024
     assert b["hbm_bytes_per_launch"] == (3000 + 150) * 1024
