@@ -9,21 +9,20 @@
  *
  *   fade   S <- Diag(alpha_t) S,   alpha_t = exp(g_t), one factor per key
  *          channel (row of S).  "Review A - Sequence and depth", Free recall,
- *          the question on KDA's three operations: every channel is multiplied
- *          by its own retention factor; "K3 Architecture Illustrated",
- *          "Combining KDA and MLA", FIG 21: channel-wise retention first.
+ *          the question on KDA's three operations (fade comes first and acts
+ *          per channel); "K3 Architecture Illustrated", "Combining KDA and
+ *          MLA", FIG 21 (per-channel retention precedes the delta update).
  *          g is a natural-log decay ("Kimi K3 - Lesson 3 of 14 - Sequence
  *          axis": log-decay bounded in (-5, 0), tile bound stated as e^80).
- *   erase  p = S^T k_t, what the key already retrieves (same Free recall
- *          answer; FIG 21 text: the delta update retrieves the old
- *          prediction for the current key) ...
+ *   erase  p = S^T k_t, the value the faded state currently returns for the
+ *          key (same Free recall answer; FIG 21 text on the delta update) ...
  *   write  S <- S + beta_t k_t (v_t - p)^T, i.e. S <- (I - beta_t k_t k_t^T) S
- *          + beta_t k_t v_t^T: the correction by the difference between the new
- *          value and the prediction, with strength beta ("K3 Architecture
- *          Illustrated", section "Under what conditions are RoPE, PaTH, and
- *          KDA related?": the delta rule contains I - beta k k^T).
- *   read   o_t = S^T q_t from the updated state ("Then the read, S^T q";
- *          FIG 21: a Query read follows the update).
+ *          + beta_t k_t v_t^T: the stored association moves toward v_t by beta_t
+ *          times the gap between v_t and p ("K3 Architecture Illustrated",
+ *          section "Under what conditions are RoPE, PaTH, and KDA related?":
+ *          the delta rule's transition has the factor I - beta k k^T).
+ *   read   o_t = S^T q_t from the updated state (the Free recall answer puts
+ *          the query product after the write; FIG 21 likewise).
  *
  * The final state after the last token is S_final.  Nothing is blocked,
  * fused or reordered: each token is the four steps above in plain loops.
@@ -53,7 +52,7 @@ static void kda_token(double *S, int dk, int dv,
         for (int j = 0; j < dv; ++j)
             S[(size_t)i * dv + j] *= alpha;
     }
-    /* erase: what the key already retrieves from the faded state, p = S^T k */
+    /* erase: the value the faded state returns for the key, p = S^T k */
     for (int j = 0; j < dv; ++j)
         p[j] = 0.0;
     for (int i = 0; i < dk; ++i)
