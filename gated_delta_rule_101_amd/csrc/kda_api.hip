@@ -92,6 +92,43 @@ kda::ChunkFwdArgs chunk_args(const void *q, const void *k, const void *v, const 
     return a;
 }
 
+// kda_chunk_fwd / kda_chunk_fwd_gate with a workspace: the prep/state kernel
+// where it applies, otherwise (or with no workspace) the same kernels as
+// without one.
+kda_status_t chunk_ws(const void *q, const void *k, const void *v, const void *g, const float *A_log,
+                      const void *beta, const float *S0, void *o, float *S_final, void *workspace,
+                      size_t workspace_bytes, int B, int T, int H, int dk, int dv,
+                      kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype, void *stream)
+{
+    const kda_status_t st = check_chunk(q, k, v, g, beta, S0, o, S_final, A_log, nullptr, B, T, H, dk, dv,
+                                        qkv_dtype, gate_dtype, out_dtype, true, true);
+    if (st != KDA_OK) return st;
+    if (B == 0 || H == 0) return KDA_OK;
+    const size_t need = kda::chunk_ps_workspace_bytes(B, H, dk, dv);
+    if (workspace && T > 0) {
+        if (!aligned16(workspace) || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+        const size_t tok = (size_t)B * T * H;
+        const size_t sq = dsize(qkv_dtype), sg = dsize(gate_dtype), so = dsize(out_dtype);
+        const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+        const Span sp_w = span(workspace, workspace_bytes);
+        const Span others[] = {span(q, tok * dk * sq), span(k, tok * dk * sq), span(v, tok * dv * sq),
+                               span(g, tok * dk * sg), span(beta, tok * sg), span(o, tok * dv * so),
+                               span(S0, S0 ? state_bytes : 0), span(S_final, S_final ? state_bytes : 0),
+                               span(A_log, A_log ? (size_t)H * sizeof(float) : 0)};
+        for (const Span &x : others)
+            if (overlap(sp_w, x)) return KDA_ERR_INVALID_ARG;
+    }
+    kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S0, o, S_final, B, T, H, dk, dv,
+                                     qkv_dtype, gate_dtype, out_dtype);
+    a.A_log = A_log;
+    if (workspace && T > 0) {
+        bool used = false;
+        const hipError_t e = kda::launch_chunk_fwd_ps(a, workspace, workspace_bytes, (hipStream_t)stream, used);
+        if (used) return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+    return run_chunk(a, stream);
+}
+
 kda::SpecArgs spec_args(const void *q, const void *k, const void *v, const void *g, const void *beta,
                         float *S, int B, int K, int H, int dk, int dv,
                         kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype)
@@ -129,7 +166,8 @@ kda_status_t decode(const void *q, const void *k, const void *v, const void *g, 
     if (!q || !k || !v || !g || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
     if (!aligned16(S)) return KDA_ERR_INVALID_ARG;
     if (A_log && ((uintptr_t)A_log & 3u)) return KDA_ERR_INVALID_ARG;
-    if (gated && (!epilogue_args_ok(z_out, weight, eps) || !aligned16(z_out)))
+    // the fused epilogue stores y with 8- or 16-byte vector stores
+    if (gated && (!epilogue_args_ok(z_out, weight, eps) || !aligned16(z_out) || !aligned16(o)))
         return KDA_ERR_INVALID_ARG;
 
     const size_t n = (size_t)B * H;
@@ -190,6 +228,37 @@ kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v, con
     a.A_log = A_log;
     return run_chunk(a, stream);
 }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv)
+{
+    if (T <= 0) return 0;
+    return kda::chunk_ps_workspace_bytes(B, H, dk, dv);
+}
+
+kda_status_t kda_chunk_fwd_ws(const void *q, const void *k, const void *v, const void *g,
+                              const void *beta, const float *S0, void *o, float *S_final,
+                              void *workspace, size_t workspace_bytes,
+                              int B, int T, int H, int dk, int dv,
+                              kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                              void *stream)
+{
+    return chunk_ws(q, k, v, g, nullptr, beta, S0, o, S_final, workspace, workspace_bytes, B, T, H, dk, dv,
+                    qkv_dtype, gate_dtype, out_dtype, stream);
+}
+
+kda_status_t kda_chunk_fwd_gate_ws(const void *q, const void *k, const void *v, const void *z,
+                                   const float *A_log, const void *beta, const float *S0, void *o,
+                                   float *S_final, void *workspace, size_t workspace_bytes,
+                                   int B, int T, int H, int dk, int dv,
+                                   kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                   void *stream)
+{
+    if (!A_log && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
+    return chunk_ws(q, k, v, z, A_log, beta, S0, o, S_final, workspace, workspace_bytes, B, T, H, dk, dv,
+                    qkv_dtype, gate_dtype, out_dtype, stream);
+}
+
+unsigned kda_debug_set_spin_limit(unsigned limit) { return kda::set_spin_limit(limit); }
 
 kda_status_t kda_verify_step(const void *q, const void *k, const void *v, const void *g,
                              const void *beta, const float *S, void *o,

@@ -74,7 +74,6 @@ __device__ __forceinline__ int tile_tr_offset(int lane) {
     return tile_at(4 * (lane >> 4) + ((lane & 15) >> 2), lane & 3);
 }
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr unsigned SPIN_LIMIT = 1u << 20;   // bound on every producer wait
 
 // Tiles (m, n) of the lower block triangle, n <= m, and of the strict one, n < m.
 __host__ __device__ constexpr int lower_index(int m, int n) { return m * (m + 1) / 2 + n; }
@@ -116,6 +115,7 @@ struct alignas(16) PipeSmem {
     // distinct banks
     alignas(16) float LdT[NT][TILE][TILE + 4];
     unsigned arrivals;                          // producer meeting counter
+    unsigned failed;                            // some producer wait expired (read after the loop)
 };
 
 // Every array above is read with 8- or 16-byte LDS accesses.
@@ -136,17 +136,22 @@ struct RowIn {
 };
 
 // The four producer waves meet here; LDS writes before it are visible to all
-// four after it.  The wait is bounded, so a wave never spins forever.
-__device__ __forceinline__ void producer_meet(unsigned *arrivals, unsigned target, int lane) {
+// four after it.  The wait is bounded (at most spin_limit sleeps); the result
+// is false when it expired.  A launch in which any wait expired writes NaN
+// over every output of the affected heads and their final states once the
+// chunk loop is done, so an expired wait is never silent.
+__device__ __forceinline__ bool producer_meet(unsigned *arrivals, unsigned target, int lane, unsigned spin_limit) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     if (lane == 0) __hip_atomic_fetch_add(arrivals, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (unsigned it = 0; it < SPIN_LIMIT; ++it) {
+    bool ok = false;
+    for (unsigned it = 0; it <= spin_limit; ++it) {
         const unsigned seen = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(arrivals, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (seen >= target) break;
+        if (seen >= target) { ok = true; break; }
         __builtin_amdgcn_s_sleep(1);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    return ok;
 }
 
 template <int DK, bool GBF, bool OBF, bool GL>
@@ -156,7 +161,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                       const typename Store<GBF>::type *__restrict__ beta, const float *S0,
                       typename Store<OBF>::type *__restrict__ o, float *S_final,
                       const int *__restrict__ lengths, const float *__restrict__ A_log,
-                      int B, int T, int H, int dv, int nslab)
+                      int B, int T, int H, int dv, int nslab, unsigned spin_limit)
 {
     typedef typename Store<GBF>::type GT;
     typedef typename Store<OBF>::type OT;
@@ -227,7 +232,10 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             }
         };
 
-        if (threadIdx.x == 0) sm.arrivals = 0;
+        if (threadIdx.x == 0) {
+            sm.arrivals = 0;
+            sm.failed = 0;
+        }
         if (nchunks == 0) {
             lds_barrier();
             lds_barrier();
@@ -237,6 +245,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         load_qk(0, r, gq);
         lds_barrier();
         unsigned meetings = 0;   // producer meetings so far (uniform)
+        bool all_met = true;     // every meeting completed within its bound
         for (int cn = 0; cn < nchunks; ++cn) {
             {
                 Stage &st = sm.stage[cn & 1];
@@ -348,7 +357,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     }
                 }
                 meetings += 1;
-                producer_meet(&sm.arrivals, NPROD * meetings, lane);
+                all_met = producer_meet(&sm.arrivals, NPROD * meetings, lane, spin_limit) && all_met;
 
                 // ---------------------------------------------- staged operands and block row m of the Gram
                 // Instantiated once per tile: which Gram tiles exist and the
@@ -467,7 +476,6 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 case 2: block_row(TileIndex<2>{}); break;
                 default: block_row(TileIndex<3>{}); break;
                 }
-
                 // ------------------------------------------ (I + L_mm)^-1, lane column r
                 {
                     // column r of L_mm, and X = e_r; `one` is opaque so the 16 selects
@@ -495,6 +503,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             }
             lds_barrier();
         }
+        if (!all_met && lane == 0) sm.failed = 1u;
         lds_barrier();   // the consumers' last chunk
     } else {
         const int w = wave - NPROD;                 // column group
@@ -645,6 +654,19 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             }
             lds_barrier();
         }
+        if (__builtin_amdgcn_readfirstlane(sm.failed) != 0u) {
+            // a producer wait expired somewhere in the sequence: its operands may
+            // have been built from unfinished data, so nothing this workgroup
+            // wrote stands; every output of its columns and its state become NaN
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) S[kt] = f32x4{nan, nan, nan, nan};
+            if (o)
+                for (int t = 4 * gq; t < T; t += 16)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (t + i < T) o[(((size_t)b * T + t + i) * H + h) * dv + col0 + r] = from_f32<OT>(nan);
+        }
         if (S_final) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
@@ -664,7 +686,7 @@ hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
     const unsigned grid = (unsigned)(a.B * a.H * nslab);
     kda_chunk_pipe_kernel<DK, GBF, OBF, GL><<<grid, NTHREADS, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const GT *)a.g,
-        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.lengths, a.A_log, a.B, a.T, a.H, a.dv, nslab);
+        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.lengths, a.A_log, a.B, a.T, a.H, a.dv, nslab, spin_limit());
     return hipGetLastError();
 }
 

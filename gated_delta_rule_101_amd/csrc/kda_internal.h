@@ -75,6 +75,18 @@ struct ChunkBwdArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        // any dtypes
+// Prep/state workgroup pairs through a ring in the workspace (bfloat16 q, k, v,
+// dk = 128, dv a multiple of 64 up to 512, no per-sequence lengths).  `used` is
+// false when the call is not taken (shape, or a workspace that is missing or
+// too small): the caller then launches the other kernels.
+constexpr int PS_MAX_GROUP = 128;   // heads per launch, at most
+hipError_t launch_chunk_fwd_ps(const ChunkFwdArgs &a, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream, bool &used);
+size_t chunk_ps_workspace_bytes(int B, int H, int dk, int dv);   // 0: the pair kernel does not apply
+// Bound on every spin wait of the chunk kernels (sleeps between polls); the
+// previous value is returned.  A wait that runs out marks the call failed.
+unsigned set_spin_limit(unsigned limit);
+unsigned spin_limit();
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_spec_step(const SpecArgs &a, hipStream_t stream);           // dk, dv in {64, 128}

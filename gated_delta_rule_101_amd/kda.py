@@ -29,7 +29,8 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 
 # Every symbol include/kda.h declares.
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_verify_step", "kda_commit_step",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_chunk_fwd_ws", "kda_chunk_fwd_gate_ws",
+           "kda_chunk_fwd_workspace_bytes", "kda_debug_set_spin_limit", "kda_verify_step", "kda_commit_step",
            "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_status_string", "kda_abi_version")
 
@@ -58,6 +59,15 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_decode_step.restype = i
     lib.kda_chunk_fwd_gate.argtypes = [vp] * 9 + [i] * 8 + [vp]
     lib.kda_chunk_fwd_gate.restype = i
+    sz = ctypes.c_size_t
+    lib.kda_chunk_fwd_ws.argtypes = [vp] * 9 + [sz] + [i] * 8 + [vp]
+    lib.kda_chunk_fwd_ws.restype = i
+    lib.kda_chunk_fwd_gate_ws.argtypes = [vp] * 10 + [sz] + [i] * 8 + [vp]
+    lib.kda_chunk_fwd_gate_ws.restype = i
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 5
+    lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_debug_set_spin_limit.argtypes = [ctypes.c_uint]
+    lib.kda_debug_set_spin_limit.restype = ctypes.c_uint
     lib.kda_decode_step_gate.argtypes = [vp] * 8 + [i] * 7 + [vp]
     lib.kda_decode_step_gate.restype = i
     lib.kda_verify_step.argtypes = [vp] * 7 + [i] * 8 + [vp]
@@ -69,7 +79,6 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_output_gate.restype = i
     lib.kda_decode_step_gated.argtypes = [vp] * 9 + [f, vp] + [i] * 7 + [vp]
     lib.kda_decode_step_gated.restype = i
-    sz = ctypes.c_size_t
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [i] * 5
     lib.kda_chunk_bwd_workspace_bytes.restype = sz
     lib.kda_chunk_bwd.argtypes = [vp] * 15 + [sz] + [i] * 8 + [vp]
@@ -125,17 +134,45 @@ def _raise(status: int, what: str):
         raise KdaError(status, f"{what}: {status_string(status)}")
 
 
+def kda_chunk_fwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int) -> int:
+    """Bytes of device workspace kda_chunk_fwd_ws needs (0: it uses none)."""
+    return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv))
+
+
+def debug_set_spin_limit(limit: int) -> int:
+    """Test hook: bound on the chunk kernels' internal waits; returns the old bound."""
+    return int(load_library().kda_debug_set_spin_limit(int(limit)))
+
+
+def _workspace(lib, workspace, B, T, H, dk, dv, device):
+    need = int(lib.kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv))
+    if need == 0:
+        return None
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    return workspace
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                   beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
                   output_final_state: bool = True, o: Optional[torch.Tensor] = None,
                   S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  ring: bool = True, workspace: Optional[torch.Tensor] = None,
                   stream: Optional[torch.cuda.Stream] = None
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA forward.  Shapes as in include/kda.h:
     q, k, g [B,T,H,dk]; v [B,T,H,dv]; beta [B,T,H]; S0 [B,H,dk,dv] float32 or None.
     Returns (o [B,T,H,dv], S_final [B,H,dk,dv] float32 or None).  o is float32
     unless out_dtype (or a passed `o`) says bfloat16.  `S_final` may be passed
-    (and may be S0 itself for an in-place continuation)."""
+    (and may be S0 itself for an in-place continuation).  With ring=True the
+    call goes through kda_chunk_fwd_ws with `workspace` (device bytes; allocated
+    here when not given), ring=False calls kda_chunk_fwd."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -151,11 +188,18 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         raise ValueError("o must be [B,T,H,dv]")
     if S_final is None and output_final_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    dev = _check_dev(q, k, v, g, beta, S0, o, S_final)
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
-                           _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(g),
-                           _dtype_code(o), _stream_handle(stream, dev))
-    _raise(st, "kda_chunk_fwd")
+    ws = _workspace(lib, workspace, B, T, H, dk, dv, q.device) if ring else None
+    dev = _check_dev(q, k, v, g, beta, S0, o, S_final, ws)
+    if ring:
+        st = lib.kda_chunk_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                  _ptr(S_final), _ptr(ws), _nbytes(ws), B, T, H, dk, dv, _dtype_code(q),
+                                  _dtype_code(g), _dtype_code(o), _stream_handle(stream, dev))
+        _raise(st, "kda_chunk_fwd_ws")
+    else:
+        st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                               _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(g),
+                               _dtype_code(o), _stream_handle(stream, dev))
+        _raise(st, "kda_chunk_fwd")
     return o, S_final
 
 
@@ -207,10 +251,12 @@ def kda_chunk_fwd_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: tor
                        A_log: torch.Tensor, beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
                        output_final_state: bool = True, o: Optional[torch.Tensor] = None,
                        S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                       ring: bool = True, workspace: Optional[torch.Tensor] = None,
                        stream: Optional[torch.cuda.Stream] = None
                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """kda_chunk_fwd with the log-decay formed in the kernel from gate logits:
-    g = -5 sigmoid(exp(A_log[h]) z).  z [B,T,H,dk] (gate dtype), A_log [H] float32."""
+    g = -5 sigmoid(exp(A_log[h]) z).  z [B,T,H,dk] (gate dtype), A_log [H] float32.
+    ring / workspace as kda_chunk_fwd (kda_chunk_fwd_gate_ws or kda_chunk_fwd_gate)."""
     lib = load_library()
     B, T, H, dk, dv = _check_chunk_shapes(q, k, v, z, beta)
     _check_head_scale(A_log, H)
@@ -222,11 +268,18 @@ def kda_chunk_fwd_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: tor
         raise ValueError("o must be [B,T,H,dv]")
     if S_final is None and output_final_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    dev = _check_dev(q, k, v, z, A_log, beta, S0, o, S_final)
-    st = lib.kda_chunk_fwd_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(beta), _ptr(S0),
-                                _ptr(o), _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(z),
-                                _dtype_code(o), _stream_handle(stream, dev))
-    _raise(st, "kda_chunk_fwd_gate")
+    ws = _workspace(lib, workspace, B, T, H, dk, dv, q.device) if ring else None
+    dev = _check_dev(q, k, v, z, A_log, beta, S0, o, S_final, ws)
+    if ring:
+        st = lib.kda_chunk_fwd_gate_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(beta), _ptr(S0),
+                                       _ptr(o), _ptr(S_final), _ptr(ws), _nbytes(ws), B, T, H, dk, dv,
+                                       _dtype_code(q), _dtype_code(z), _dtype_code(o), _stream_handle(stream, dev))
+        _raise(st, "kda_chunk_fwd_gate_ws")
+    else:
+        st = lib.kda_chunk_fwd_gate(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(beta), _ptr(S0),
+                                    _ptr(o), _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(z),
+                                    _dtype_code(o), _stream_handle(stream, dev))
+        _raise(st, "kda_chunk_fwd_gate")
     return o, S_final
 
 

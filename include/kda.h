@@ -88,7 +88,7 @@ typedef enum {
 } kda_status_t;
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 /*
  * kda_chunk_fwd -- chunkwise forward over T tokens for B sequences x H heads.
@@ -165,6 +165,59 @@ kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
                                 int B, int T, int H, int dk, int dv,
                                 kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
                                 kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_chunk_fwd_ws, kda_chunk_fwd_gate_ws -- kda_chunk_fwd and
+ * kda_chunk_fwd_gate with a caller-owned workspace.  The workspace lets
+ * bfloat16 q, k, v with dk = 128 (dv a multiple of 64 up to 512) take the
+ * prep/state kernel: per head, one workgroup computes the state-independent
+ * part of every chunk of the chunkwise form ("Kimi K3 - Lesson 3 of 14 -
+ * Sequence axis", the chunkwise diagram: decays, 1/Gamma-rescaled operands,
+ * intra-chunk Gram tiles, the diagonal inverses) exactly once and hands it,
+ * through a three-slot ring held in the workspace, to the workgroups that
+ * carry the state.  Other inputs run the kernels of kda_chunk_fwd.
+ *
+ *   workspace        device memory of at least kda_chunk_fwd_workspace_bytes(B,
+ *                    T, H, dk, dv) bytes, 16-byte aligned, owned by the caller;
+ *                    it needs no initialisation, its contents are undefined
+ *                    afterwards, and it must not overlap any other argument.
+ *                    NULL makes the call kda_chunk_fwd (or _gate) exactly.
+ *   workspace_bytes  its size; a non-NULL workspace below the required size is
+ *                    KDA_ERR_INVALID_ARG.
+ *
+ * Everything else (shapes, dtypes, aliasing rules, preconditions, precision,
+ * errors) as kda_chunk_fwd / kda_chunk_fwd_gate; the arithmetic is the same,
+ * step for step.  Calls sharing one workspace must not overlap in time (use
+ * one stream, or one workspace per stream).  The kernel's workgroups wait
+ * for one another (bounded waits, at most kda_debug_set_spin_limit sleeps
+ * each); if a wait runs out, the call still completes and every output it
+ * writes from then on (o and S_final of the affected heads) is NaN.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv);   /* 0: no workspace is used */
+
+kda_status_t kda_chunk_fwd_ws(const void *q, const void *k, const void *v,
+                              const void *g, const void *beta, const float *S0,
+                              void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                              int B, int T, int H, int dk, int dv,
+                              kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                              kda_dtype_t out_dtype, void *stream);
+
+kda_status_t kda_chunk_fwd_gate_ws(const void *q, const void *k, const void *v,
+                                   const void *z, const float *A_log, const void *beta,
+                                   const float *S0, void *o, float *S_final,
+                                   void *workspace, size_t workspace_bytes,
+                                   int B, int T, int H, int dk, int dv,
+                                   kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                                   kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_debug_set_spin_limit -- test hook: the bound (sleeps between polls) on
+ * every wait inside the chunk kernels launched after the call, process-wide;
+ * returns the previous bound (default 2^20).  A small bound makes the waits
+ * give up, which lets a test check that a failed wait yields NaN outputs
+ * rather than wrong finite ones.  Not for production use.
+ */
+unsigned kda_debug_set_spin_limit(unsigned limit);
 
 /*
  * kda_decode_step_gate -- kda_decode_step with g = -5 sigmoid(exp(A_log[h]) z)

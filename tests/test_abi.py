@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     from gated_delta_rule_101_amd import kda
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for st in (kda.KDA_OK, kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_LAUNCH):
         assert lib.kda_status_string(st).decode().startswith("KDA_")
     assert lib.kda_status_string(77).decode() == "KDA_ERR_UNKNOWN"
@@ -196,6 +196,7 @@ def test_output_epilogue_validation(lib):
     assert dec(z=zo + 4) == INV                  # misaligned logits
     assert dec(y=zo + 128) == INV                # y over the logits
     assert dec(y=wt) == INV                      # y over the weight
+    assert dec(y=yy + 4) == INV                  # misaligned y (vector stores)
     assert dec(B=0) == OK
 
 
@@ -230,3 +231,43 @@ def test_backward_validation(lib):
     assert call(vdim=256) == UNS
     assert call(B=0) == OK
     assert call(T=0, dS0=None) == OK                     # nothing to write
+
+
+def test_workspace_forward_validation(lib):
+    """kda_chunk_fwd_ws / kda_chunk_fwd_gate_ws: the forward's own checks, plus
+    the workspace's size, alignment and overlap."""
+    from gated_delta_rule_101_amd import kda
+    INV, UNS, OK = kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_OK
+    big = 1 << 30
+    B, T, H, d = 2, 640, 3, 128
+    need = lib.kda_chunk_fwd_workspace_bytes(B, T, H, d, d)
+    assert need > 0 and need % 16 == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(B, 0, H, d, d) == 0     # nothing to run
+    assert lib.kda_chunk_fwd_workspace_bytes(B, T, H, 64, 64) == 0   # dk = 64: no workspace used
+    assert lib.kda_chunk_fwd_workspace_bytes(B, T, H, d, 96) == 0
+    # more heads than one launch holds: the ring is sized for one launch
+    assert lib.kda_chunk_fwd_workspace_bytes(4, T, 64, d, d) == lib.kda_chunk_fwd_workspace_bytes(4, T, 32, d, d)
+    names = ("q", "k", "v", "g", "beta", "S0", "o", "Sf", "ws")
+    base = {n: (i + 1) * big for i, n in enumerate(names)}
+    base["S0"] = base["Sf"] = None
+
+    def call(size=need, B=B, T=T, dk=d, dv=d, qd=1, **kw):
+        p = {**base, **kw}
+        return lib.kda_chunk_fwd_ws(*(p[n] for n in names), size, B, T, H, dk, dv, qd, 1, 0, None)
+
+    assert call(q=None) == INV
+    assert call(size=need - 16) == INV                   # workspace too small
+    assert call(ws=base["ws"] + 8) == INV                # misaligned workspace
+    assert call(ws=base["o"] + 4096) == INV              # workspace over the output
+    assert call(ws=base["q"]) == INV                     # workspace over an input
+    assert call(dk=96) == UNS
+    assert call(B=0) == OK
+    assert call(T=0) == OK                               # no S_final: nothing to write
+    gate = lambda A=FAKE, **kw: lib.kda_chunk_fwd_gate_ws(  # noqa: E731
+        *(kw.get(n, base[n]) for n in ("q", "k", "v", "g")), A, base["beta"], None, base["o"], None,
+        kw.get("ws", base["ws"]), kw.get("size", need), B, T, H, d, d, 1, 1, 0, None)
+    assert gate(A=None) == INV
+    assert gate(size=1) == INV
+    # the spin-bound hook returns the previous bound
+    old = lib.kda_debug_set_spin_limit(123)
+    assert lib.kda_debug_set_spin_limit(old) == 123

@@ -262,3 +262,97 @@ def test_full_decode(kda, orc):
     es = err_ratio(f64(S[idx_b, idx_h]).reshape(S_ref.shape), S_ref)
     say(f"      err/rms  o(worst step)={worst:.3e}  S after {w.steps} steps={es:.3e}")
     assert worst <= 2e-2 and es <= 2e-2
+
+
+# ------------------------------------------- prep/state ring kernel vs pipelined kernel
+
+BF16_CASES = [w for w in SMALL_CASES if w.qkv == "bf16"]
+
+
+@pytest.mark.parametrize("w", BF16_CASES, ids=[w.name for w in BF16_CASES])
+def test_fwd_matches_oracle_without_workspace(kda, orc, w):
+    """kda_chunk_fwd with no workspace (the single-workgroup pipelined kernel)."""
+    x = gen.fwd_inputs(w)
+    d = {n: to_dev(x[n]) for n in x}
+    say(f"[fwd no ring] {w.name}")
+    o, S = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], ring=False)
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.fwd(*[x[n].f64() for n in ("q", "k", "v", "g", "beta")],
+                           x["S0"].f64() if x["S0"] is not None else None)
+    eo, es = err_ratio(f64(o), o_ref), err_ratio(f64(S), S_ref)
+    say(f"      err/rms  o={eo:.3e}  S={es:.3e}")
+    assert eo <= tau_for(w.qkv) and es <= tau_for(w.qkv), (eo, es)
+
+
+RING_CASES = BF16_CASES + [
+    T.scaled(B=1, H=3, T=64 * 9 + 5, dk=128, dv=256, name="bf16_dv256_two_state_groups"),
+    T.scaled(B=3, H=50, T=200, name="bf16_BH150_two_launches"),     # more heads than one launch holds
+    H8.scaled(H=5, T=640, gate="bf16", name="bf16_gates_S0_T640"),
+]
+
+
+@pytest.mark.parametrize("w", RING_CASES, ids=[w.name for w in RING_CASES])
+def test_ring_kernel_equals_pipelined_kernel(kda, w):
+    """The workspace path runs the same steps as the pipelined kernel: the
+    outputs and final states agree bit for bit."""
+    _, d = _dev_inputs(w)
+    say(f"[ring vs pipe] {w.name} B={w.B} T={w.T} H={w.H} dv={w.dv} gate={w.gate}")
+    need = kda.kda_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    assert need > 0 or w.dk != 128
+    o1, S1 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], ring=True)
+    o2, S2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], ring=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_ring_kernel_gate_logits_equals_pipelined(kda):
+    w = T.scaled(B=2, H=4, T=333)
+    _, d = _dev_inputs(w)
+    A_log = torch.linspace(-1.0, 1.0, w.H, device="cuda")
+    z = d["g"].float().mul(-1.0).to(d["g"].dtype)
+    o1, S1 = kda.kda_chunk_fwd_gate(d["q"], d["k"], d["v"], z, A_log, d["beta"], ring=True)
+    o2, S2 = kda.kda_chunk_fwd_gate(d["q"], d["k"], d["v"], z, A_log, d["beta"], ring=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_ring_workspace_reuse_and_uninitialised(kda):
+    """One workspace reused across calls of different shapes, first filled with
+    bytes that look like flags: results stay those of the pipelined kernel."""
+    ws = torch.full((kda.kda_chunk_fwd_workspace_bytes(2, 1, 8, 128, 128),), 0xFF, dtype=torch.uint8, device="cuda")
+    for i, (B, H, T_) in enumerate([(2, 8, 700), (1, 3, 130), (2, 8, 64)]):
+        _, d = _dev_inputs(T.scaled(B=B, H=H, T=T_), seed=i)
+        o1, S1 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], workspace=ws)
+        o2, S2 = kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], ring=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(S1, S2), (B, H, T_)
+
+
+@pytest.mark.parametrize("ring", [True, False])
+def test_expired_wait_is_loud(kda, ring):
+    """A wait inside the chunk kernels that runs out of spins (forced from the
+    host with a zero bound) never yields finite wrong numbers: every finite
+    output equals the normal run's bit for bit, and the rest is NaN."""
+    w = T.scaled(B=2, H=4, T=64 * 12)
+    _, d = _dev_inputs(w)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"])
+    o_ref, S_ref = kda.kda_chunk_fwd(*args, ring=ring)
+    torch.cuda.synchronize()
+    old = kda.debug_set_spin_limit(0)
+    try:
+        say(f"[expired wait] ring={ring}: spin bound 0")
+        o, S = kda.kda_chunk_fwd(*args, ring=ring)
+        torch.cuda.synchronize()
+    finally:
+        kda.debug_set_spin_limit(old)
+    bad_o = ~torch.isfinite(o)
+    say(f"      NaN outputs: {int(bad_o.sum())} of {o.numel()}; NaN state: {int((~torch.isfinite(S)).sum())}")
+    assert bool(bad_o.any()), "a zero spin bound must make some wait expire"
+    assert bool(torch.isnan(o[bad_o]).all())
+    assert torch.equal(o[~bad_o], o_ref[~bad_o])
+    bad_s = ~torch.isfinite(S)
+    assert bool(bad_s.any()) and torch.equal(S[~bad_s], S_ref[~bad_s])
+    # the bound is restored: the next call is whole again
+    o2, S2 = kda.kda_chunk_fwd(*args, ring=ring)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_ref) and torch.equal(S2, S_ref)
