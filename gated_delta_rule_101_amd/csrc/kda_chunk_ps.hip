@@ -1,5 +1,6 @@
-// Chunkwise KDA forward for bfloat16 q, k, v on gfx950: prep and state
-// workgroups in pairs, joined through a ring of chunk slots held in L2.
+// Chunkwise KDA forward for bfloat16 q, k, v on gfx950: the workgroups of a
+// head share each chunk's state-independent work through a ring of chunk
+// slots held in L2.
 //
 // The chunkwise form ("Kimi K3 - Lesson 3 of 14 - Sequence axis": sequential
 // between chunks, parallel within; output = inter-chunk (Gamma . Q) S plus
@@ -7,30 +8,34 @@
 // which the g_min = -5 floor keeps below e^80) splits into work that does not
 // depend on the state (decays, scaled operands, Gram tiles, the diagonal
 // inverses: everything a chunk needs before it meets S) and the state
-// recurrence itself.  Here each head gets one prep workgroup, which computes
-// the state-independent part of every chunk exactly once, and 1..4 state
-// workgroups (128 value columns each), which run the recurrence.  The prep
-// workgroup writes each chunk's operands into a slot of a three-slot ring in
-// the caller's workspace; the state workgroups copy the slot into LDS with
-// LDS-direct loads one chunk ahead and hand the slot back.  The ring is small
-// (3 x 63 KB per head) and lives in the L2 of the XCD that runs the head.
+// recurrence itself.  A head's dv columns are split into 64-column slabs, one
+// workgroup each.  Every workgroup holds a prep team (four waves, one per
+// 16-token tile) and four state waves (16 value columns each, the state slab
+// in registers).  The prep teams of a head take turns: slab j prepares chunks
+// j, j + nslab, ..., so each chunk's state-independent work is done once per
+// head, not once per slab, and each CU carries an equal share of it.  A
+// prepared chunk goes into one slot of a four-slot ring in the caller's
+// workspace; the state waves of every slab copy the slot into LDS with
+// LDS-direct loads one chunk ahead and then hand the slot back.  The ring is
+// small (4 x 63 KB per head) and lives in the L2 of the XCD that runs the head.
 //
 // Synchronisation.  All workgroups of a head run on one XCD (workgroup i is
 // dispatched to XCD i mod 8; each workgroup checks this at run time), so the
-// XCD's L2 is the point where the two sides meet: slot data and flags are
+// XCD's L2 is the point where the workgroups meet: slot data and flags are
 // written with ordinary stores (complete once s_waitcnt vmcnt(0) returns) and
 // read with loads that bypass the CU's L1 (device scope, sc1).  Flags are
 // 64-bit: the launch's epoch in the high half (a per-process counter, started
 // at a random value and advanced per launch) and the chunk number + 1 in the
 // low half; a wait accepts only the exact value it expects, so flags of other
 // launches and uninitialised memory never satisfy it and the workspace needs
-// no clearing.  Every wait is bounded by `spin_limit` sleeps;
-// when a bound expires the waiting side marks the call failed (low half all
-// ones), never overwrites a slot the other side may still read, and the
-// state side sets its state to NaN, which carries into every output from then
-// on and the final state: a failed call is loud, and every wave still runs to
-// its end.  The launch is cooperative, so all
-// workgroups of the grid are resident together.
+// no clearing.  Inside a workgroup the two roles never wait for each other:
+// each role meets only its own four waves, at an LDS counter.  Every wait is
+// bounded by `spin_limit` sleeps; when a bound expires the waiting side marks
+// the launch failed (low half all ones), never overwrites a slot another
+// workgroup may still read, and the state waves set their state to NaN, which
+// carries into every output from then on and the final state: a failed launch
+// is loud, and every wave still runs to its end.  The launch is cooperative,
+// so all workgroups of the grid are resident together.
 //
 // Arithmetic and operand formats are those of kda_chunk_pipe.hip (the same
 // producer and consumer steps, in the same order), so the two kernels give
@@ -50,14 +55,16 @@ namespace {
 
 using namespace chunk;
 
-constexpr int NWAVE = 8;
-constexpr int NTHREADS = 64 * NWAVE;
-constexpr int NTEAM = 2;              // prep teams: team t prepares chunks t, t + 2, ...
-constexpr int NPROD = NT;             // waves per team: one per tile
-constexpr int SCOLS = 16 * NWAVE;     // value columns of one state workgroup
-constexpr int RING = 3;               // slots per head
-constexpr int MAXSTATE = 4;           // state workgroups per head (dv <= 512)
-constexpr size_t FLAG_BYTES = 512;    // per head: ready line, consumed line, info line
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NPROD = NT;             // prep waves: one per tile
+constexpr int NSTW = 4;               // state waves: 16 value columns each
+constexpr int NTHREADS = 64 * (NPROD + NSTW);
+constexpr int SLAB = 16 * NSTW;       // value columns of one workgroup
+constexpr int NSLOT = 4;              // ring slots per head
+constexpr int MAXSLAB = 8;            // workgroups per head (dv <= 512)
+constexpr size_t FLAG_BYTES = 1024;   // per head: ready line, consumed lines, info line
 constexpr uint32_t FAILED = 0xFFFFFFFFu;
 
 // What the state workgroups read for one chunk; the same bytes in the ring
@@ -81,13 +88,15 @@ struct alignas(16) Slot {
 };
 static_assert(sizeof(Slot<128>) % 16 == 0 && sizeof(Slot<64>) % 16 == 0, "slot copies move 16-byte units");
 
-// Scratch of one prep team (LDS).
+// Scratch of the prep team (LDS).
 template <int DK>
 struct alignas(16) TeamSmem {
     static constexpr int LDK = DK + 8;
     static constexpr int LDD = DK + 16;     // rows 64 bytes longer than DK floats (bank spread of the gathers)
-    _Float16 gst[NT][DK / 16][TILE * LDT];  // gates of each tile, staged for the transposed read
-    _Float16 Kh[NT - 1][TILE * LDK];        // keys of tiles 0..2 decayed to their tile end
+    // Keys of tiles 0..2 decayed to their tile end.  Before that, entry m holds
+    // tile m's gates staged for the transposed read of the in-tile cumulative
+    // sum (entry 3 serves only that).
+    _Float16 Kh[NT][TILE * LDK];
     float D[NT][LDD];                       // total decay of each tile
     float LdT[NT][TILE][TILE + 4];          // diagonal blocks of L (fp32): [m][col][row], 80-byte rows
     float betas[C];                         // beta of the chunk being prepared
@@ -96,21 +105,18 @@ struct alignas(16) TeamSmem {
 };
 
 template <int DK>
-struct alignas(16) StateSmem {
-    Slot<DK> stage[2];
-    unsigned failed;                        // set by any wave whose wait expired
-};
-
-template <int DK>
-union alignas(16) PsSmem {
-    StateSmem<DK> state;
-    TeamSmem<DK> team[NTEAM];
+struct alignas(16) PsSmem {
+    Slot<DK> stage[2];                      // the state waves' copies of two consecutive chunks
+    TeamSmem<DK> team;
+    unsigned state_arrivals;                // state waves' meeting counter
+    unsigned failed;                        // set by any state wave whose wait expired
 };
 static_assert(sizeof(PsSmem<128>) <= 160 * 1024, "LDS budget of one workgroup");
 static_assert(offsetof(Slot<128>, AqkT) % 16 == 0 && offsetof(Slot<128>, GamC) % 16 == 0 &&
               offsetof(Slot<128>, Kb) % 16 == 0 && offsetof(Slot<128>, beta) % 16 == 0, "slot alignment");
-static_assert(offsetof(TeamSmem<128>, Kh) % 16 == 0 && offsetof(TeamSmem<128>, D) % 16 == 0 &&
-              offsetof(TeamSmem<128>, LdT) % 16 == 0 && offsetof(TeamSmem<128>, betas) % 16 == 0, "team alignment");
+static_assert(offsetof(TeamSmem<128>, D) % 16 == 0 && offsetof(TeamSmem<128>, LdT) % 16 == 0 &&
+              offsetof(TeamSmem<128>, betas) % 16 == 0, "team alignment");
+static_assert((128 / 16) * TILE * LDT <= TILE * (128 + 8), "a tile's staged gates fit its key entry");
 
 // ------------------------------------------------------------ cross-workgroup flags
 
@@ -124,12 +130,24 @@ __device__ __forceinline__ uint64_t poll64(const uint64_t *p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return ((uint64_t)hi << 32) | lo;
 }
+// The same load without making the value uniform: issue it early, take
+// uniform() of the result where it is used, so nothing waits for it sooner.
+__device__ __forceinline__ uint64_t poll64_raw(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ void post64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Every vector-memory access of this wave issued so far has completed (for
-// stores: reached the L2).
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// stores: reached the L2).  The builtin form (vmcnt 0; expcnt and lgkmcnt at
+// their "no wait" maxima) lets the compiler's wait-count tracking see it, so it
+// adds no further waits for the same accesses later.
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Waits until *p holds `want` or `fail`, starting from an already polled
 // value; at most `limit` sleeps.  Returns the last value seen; `ok` is
@@ -167,7 +185,7 @@ struct PsArgs {
     const float *A_log;
     unsigned char *ws;       // flags, then slots
     size_t slot_off;         // byte offset of the slots in ws
-    int B, T, H, dv, nstate, h_begin, G;
+    int B, T, H, dv, nslab, h_begin, G;
     uint32_t epoch;
     unsigned spin_limit;
 };
@@ -183,7 +201,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
     constexpr int KT = DK / 16;   // 16-channel tiles
     constexpr int LDK = SL::LDK, LDKB = SL::LDKB;
     constexpr int SLOT_U4 = (int)(sizeof(SL) / 16);
-    constexpr int NCOPY = (SLOT_U4 + NTHREADS - 1) / NTHREADS;
 
     __shared__ PsSmem<DK> sm;
 
@@ -192,11 +209,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
     const int r = lane & 15;     // row / column inside a 16x16 tile
     const int gq = lane >> 4;    // lane group: k-items, or output rows 4gq..4gq+3
 
-    // Workgroup -> (head, role).  Workgroup i runs on XCD i mod 8; the 1 + nstate
-    // workgroups of a head are i = 8 (u P + role) + x, all on XCD x.
-    const int P = 1 + a.nstate;
+    // Workgroup -> (head, slab).  Workgroup i runs on XCD i mod 8; the nslab
+    // workgroups of a head are i = 8 (u nslab + slab) + x, all on XCD x.
+    const int nslab = a.nslab;
     const int x = blockIdx.x & 7, s = blockIdx.x >> 3;
-    const int u = s / P, role = s - u * P;
+    const int u = s / nslab, slab = s - u * nslab;
     const int hl = u * 8 + x;   // head within this launch's group
     if (hl >= a.G) return;
     const int bh = a.h_begin + hl;
@@ -207,27 +224,27 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
     const unsigned limit = a.spin_limit;
 
     uint64_t *flags = reinterpret_cast<uint64_t *>(a.ws + (size_t)hl * FLAG_BYTES);
-    uint64_t *ready = flags;              // [RING], written by the prep workgroup
-    uint64_t *consumed = flags + 16;      // [RING][MAXSTATE], written by the state workgroups
-    uint64_t *info = flags + 32;          // [0]: the prep workgroup's XCD, tagged with the epoch
-    SL *slots = reinterpret_cast<SL *>(a.ws + a.slot_off) + (size_t)hl * RING;
+    uint64_t *ready = flags;              // [NSLOT], written by the workgroup that prepared the slot
+    uint64_t *consumed = flags + 16;      // [NSLOT][MAXSLAB], written by each workgroup's state waves
+    uint64_t *info = flags + 64;          // [MAXSLAB]: each workgroup's XCD, tagged with the epoch
+    SL *slots = reinterpret_cast<SL *>(a.ws + a.slot_off) + (size_t)hl * NSLOT;
 
-    if (role == 0) {
-        // ====================================================== prep workgroup
+    if (threadIdx.x == 0) {
+        sm.team.arrivals = 0;
+        sm.state_arrivals = 0;
+        sm.failed = 0;
+        post64(&info[slab], tag(epoch, xcc_id()));
+    }
+    __syncthreads();
+
+    if (wave < NPROD) {
+        // ====================================================== prep team
         const GT *g = static_cast<const GT *>(a.g);
         const GT *beta = static_cast<const GT *>(a.beta);
-        const int team = wave / NPROD;
-        const int wt = wave % NPROD;
-        // the second team's waves take the tiles in rotated order, so each SIMD
-        // (wave i runs on SIMD i mod 4) holds a light and a heavy tile
-        const int m = team == 0 ? wt : (wt + 2) % NT;
-        const bool leader = wt == 0;
-        TeamSmem<DK> &ts = sm.team[team];
+        const int m = wave;          // tile
+        const bool leader = m == 0;
+        TeamSmem<DK> &ts = sm.team;
         const float gate_scale = GL ? __expf(a.A_log[h]) : 1.f;
-
-        if (threadIdx.x == 0) post64(info, tag(epoch, xcc_id()));
-        if (lane == 0 && wt == 0) ts.arrivals = 0;
-        __syncthreads();
 
         RowIn<DK, GT> in;    // inputs of the team's next chunk
         GT bnext = GT(0);    // its beta (tile-0 wave: lane = token)
@@ -255,28 +272,29 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
 
         unsigned meetings = 0;
         bool ok = true;
-        if (team < nchunks) {
-            load_g(team);
-            load_qk(team);
-            if (m == 0) bnext = load_beta(team);
+        // this workgroup prepares chunks slab, slab + nslab, ...
+        if (slab < nchunks) {
+            load_g(slab);
+            load_qk(slab);
+            if (m == 0) bnext = load_beta(slab);
         }
-        for (int cn = team; cn < nchunks && ok; cn += NTEAM) {
-            const int slot = cn % RING;
+        for (int cn = slab; cn < nchunks && ok; cn += nslab) {
+            // Nothing is in flight here (the previous chunk ended with wait_vm);
+            // saying so lets the compiler's wait tracking treat this chunk's
+            // inputs as arrived, so it never waits for the prefetches issued below.
+            wait_vm();
+            const int slot = cn % NSLOT;
             SL *st = slots + slot;
             int r = lane & 15, gq = lane >> 4;
             asm volatile("" : "+v"(r), "+v"(gq));
             const bool live = cn * C + TILE * m + r < T;   // else: identity token
-            const int cnext = cn + NTEAM < nchunks ? cn + NTEAM : cn;
-            // the leader's poll of the slot's consumers, issued early
-            uint64_t seen[MAXSTATE] = {0, 0, 0, 0};
-            const uint64_t want = tag(epoch, (uint32_t)(cn - RING + 1));
-            if (leader && cn >= RING)
-                for (int j = 0; j < a.nstate; ++j) seen[j] = poll64(&consumed[slot * MAXSTATE + j]);
+            const int cnext = cn + nslab < nchunks ? cn + nslab : cn;
+            const uint64_t want = tag(epoch, (uint32_t)(cn - NSLOT + 1));
 
             // ---------------------------------------------- decays within tile m
             float f[KT][4];   // f = e^b in [e^-80, 1]
             if constexpr (GBF && !GL) {
-                uint16_t *gs = reinterpret_cast<uint16_t *>(&ts.gst[m][0][0]);
+                uint16_t *gs = reinterpret_cast<uint16_t *>(&ts.Kh[m][0]);
 #pragma unroll
                 for (int blk = 0; blk < KT; ++blk)
                     *reinterpret_cast<uint2 *>(&gs[TILE * LDT * blk + tile_at(r, gq)]) =
@@ -339,12 +357,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
 #pragma unroll
                 for (int blk = 0; blk < KT; ++blk) {
                     const int ch = 16 * blk + 4 * gq;
-                    const f32x4 dm = *reinterpret_cast<const f32x4 *>(&ts.D[m][ch]);
                     float kv[4];
                     in.k[blk].to_f32(kv);
                     f32x4 kh;
+                    // the tile's total decay of these channels is lane 15's f in this row
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) kh[i] = kv[i] * fast_rcp(f[blk][i]) * dm[i];
+                    for (int i = 0; i < 4; ++i) kh[i] = kv[i] * fast_rcp(f[blk][i]) * row_bcast<15>(f[blk][i]);
                     *reinterpret_cast<f16x4 *>(&ts.Kh[m][r * LDK + ch]) = h16::pack4(kh);
                 }
             } else {
@@ -371,9 +389,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
             // that used it last
             if (leader) {
                 bool free_ok = true;
-                if (cn >= RING)
-                    for (int j = 0; j < a.nstate; ++j)
-                        wait_flag(&consumed[slot * MAXSTATE + j], want, tag(epoch, FAILED), seen[j], limit, free_ok);
+                if (cn >= NSLOT)
+                    for (int j = 0; j < nslab; ++j)
+                        wait_flag(&consumed[slot * MAXSLAB + j], want, tag(epoch, FAILED),
+                                  poll64(&consumed[slot * MAXSLAB + j]), limit, free_ok);
                 if (lane == 0) ts.go = free_ok ? 1u : 0u;
             }
             meetings += 1;
@@ -390,6 +409,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
                     gq_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
                     gk_o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
+                // the four tiles' totals of this lane's channels: one LDS read per
+                // channel block, all issued before the first is used
+                float dsrc[KT];
+#pragma unroll
+                for (int blk = 0; blk < KT; ++blk) dsrc[blk] = ts.D[r >> 2][16 * blk + 4 * gq + (r & 3)];
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int p = 0; p < KB; ++p) {
                     float qf[8], kf[8], ki[8], v2[8], v3[8];
@@ -398,7 +423,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
                         const int blk = 2 * p + hh;
                         const int ch = 16 * blk + 4 * gq;
                         f32x4 Dt[NT];
-                        row_gather16(ts.D[r >> 2][ch + (r & 3)], Dt);
+                        row_gather16(dsrc[blk], Dt);
                         f32x4 before = {1.f, 1.f, 1.f, 1.f}, dma = Dt[M], w2 = before, w3 = before;
 #pragma unroll
                         for (int t = 0; t < M; ++t) before = t ? before * Dt[t] : Dt[t];
@@ -522,25 +547,20 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
         }
         if (!ok && leader && lane == 0) {
             // a wait expired: the state side stops waiting and writes NaN
-            for (int sl = 0; sl < RING; ++sl) post64(&ready[sl], tag(epoch, FAILED));
+            for (int sl = 0; sl < NSLOT; ++sl) post64(&ready[sl], tag(epoch, FAILED));
         }
         return;
     }
 
-    // ========================================================== state workgroup
-    const int jst = role - 1;
-    const int w = wave;
-    const int col0 = SCOLS * jst + 16 * w;        // first value column of this wave
-    const bool active = col0 < dv;                // uniform
-    typedef StateSmem<DK> SS;
-    SS &ss = sm.state;
+    // ========================================================== state waves
+    const int w = wave - NPROD;
+    const int col0 = SLAB * slab + 16 * w;        // first value column of this wave
+    const int tid = (int)threadIdx.x - 64 * NPROD; // thread index among the state waves
     const size_t s_base = (size_t)bh * DK * dv + col0 + r;
     const size_t Hdv = (size_t)H * dv;
     const uint32_t lane_v = (uint32_t)(4 * gq * H * dv + r);   // rows 4gq + i, column r
     OT *o = static_cast<OT *>(a.o);
-
-    if (threadIdx.x == 0) ss.failed = 0u;
-    lds_barrier();
+    constexpr int NCOPYS = (SLOT_U4 + 64 * NSTW - 1) / (64 * NSTW);
 
     f32x4 S[KT];           // rows 16kt + 4gq + i, column r
     uint16_t vin[NT][4];   // V rows 16mm + 4gq + i, column r, of the chunk being computed
@@ -576,178 +596,229 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
     };
     // copy of chunk c's slot into stage c & 1, this thread's share
     auto copy_slot = [&](int c) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(slots + c % RING);
-        const unsigned base = (unsigned)(size_t)&ss.stage[c & 1];
+        const uint4 *src = reinterpret_cast<const uint4 *>(slots + c % NSLOT);
+        const unsigned base = (unsigned)(size_t)&sm.stage[c & 1];
 #pragma unroll
-        for (int u2 = 0; u2 < NCOPY; ++u2) {
-            const int idx = u2 * NTHREADS + (int)threadIdx.x;
-            const unsigned dst = __builtin_amdgcn_readfirstlane(base + (unsigned)(u2 * NTHREADS + 64 * wave) * 16u);
+        for (int u2 = 0; u2 < NCOPYS; ++u2) {
+            const int idx = u2 * 64 * NSTW + tid;
+            const unsigned dst = __builtin_amdgcn_readfirstlane(base + (unsigned)(u2 * 64 * NSTW + 64 * w) * 16u);
             if (idx < SLOT_U4) lds_dma16(src + idx, dst);
         }
     };
-    // this wave's verdict on chunk c's slot: ready, or the wait expired or the
-    // prep side failed
+    // this wave's verdict on chunk c's slot: ready, the prep side has not
+    // failed, and (first chunk of each preparing workgroup) that workgroup
+    // runs on this XCD
     auto slot_ok = [&](int c, uint64_t first) -> bool {
         bool ok = true;
         const uint64_t seen =
-            wait_flag(&ready[c % RING], tag(epoch, (uint32_t)(c + 1)), tag(epoch, FAILED), first, limit, ok);
+            wait_flag(&ready[c % NSLOT], tag(epoch, (uint32_t)(c + 1)), tag(epoch, FAILED), first, limit, ok);
+        if (c < nslab && poll64(&info[c]) != tag(epoch, xcc_id())) ok = false;
         return ok && (uint32_t)seen != FAILED;
+    };
+    unsigned smeet = 0;   // state-wave meetings so far
+    auto state_meet = [&]() {
+        smeet += 1;
+        if (!lds_meet(&sm.state_arrivals, NSTW * smeet, lane, limit) && lane == 0) sm.failed = 1u;
     };
 
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            S[kt][i] = (active && a.S0) ? a.S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
+            S[kt][i] = a.S0 ? a.S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
 
     bool failed = false;
-    uint64_t pend = 0;   // polled value of the next chunk's ready flag
+    uint64_t pend = 0;   // polled value of the next chunk's ready flag (per lane, made uniform at use)
     if (nchunks > 0) {
-        bool okc = slot_ok(0, poll64(&ready[0]));
-        // every workgroup of the head must sit on the XCD whose L2 carries the ring
-        if (okc && poll64(info) != tag(epoch, xcc_id())) okc = false;
+        const bool okc = slot_ok(0, poll64(&ready[0]));
         if (okc) copy_slot(0);
-        else if (lane == 0) ss.failed = 1u;
-        if (active) load_v(0, vin);
-        if (nchunks > 1) pend = poll64(&ready[1 % RING]);
+        else if (lane == 0) sm.failed = 1u;
+        load_v(0, vin);
+        if (nchunks > 1) pend = poll64_raw(&ready[1 % NSLOT]);
     }
     wait_vm();
-    lds_barrier();
-    failed = ss.failed != 0u;
+    state_meet();
+    failed = __builtin_amdgcn_readfirstlane(sm.failed) != 0u;
     if (nchunks > 0 && w == 0 && lane == 0)
-        post64(&consumed[0 * MAXSTATE + jst], tag(epoch, failed ? FAILED : 1u));
+        post64(&consumed[0 * MAXSLAB + slab], tag(epoch, failed ? FAILED : 1u));
 
-    for (int c = 0; c < nchunks; ++c) {
+    // One chunk of the recurrence.  vcur holds this chunk's V; the next
+    // chunk's V goes into vnext.  LDS operands are
+    // read ahead of the products that use them: the state-independent tiles
+    // first, each row tile's scaled queries and keys while the previous row
+    // tile's products run, K-bar during the output products.  Scheduling fences
+    // keep the compiler from sinking the reads back next to their uses.
+    auto chunk_step = [&](int c, uint16_t (&vcur)[NT][4], uint16_t (&vnext)[NT][4]) __attribute__((always_inline)) {
+        wait_vm();   // already true at run time (see the prep loop); for the compiler's wait tracking
         if (c + 1 < nchunks) {
             if (!failed) {
-                const bool okc = slot_ok(c + 1, pend);
+                const bool okc = slot_ok(c + 1, uniform64(pend));
                 if (okc) copy_slot(c + 1);
-                else if (lane == 0) ss.failed = 1u;
-                if (c + 2 < nchunks) pend = poll64(&ready[(c + 2) % RING]);
+                else if (lane == 0) sm.failed = 1u;
             }
-            if (active) load_v(c + 1, vnx);
+            load_v(c + 1, vnext);
+            if (!failed && c + 2 < nchunks) pend = poll64_raw(&ready[(c + 2) % NSLOT]);
         }
-        if (active) {
-            const SL &st = ss.stage[c & 1];
-            if (failed) {
-                // this chunk's stage was not filled: the state turns NaN, and with it
-                // every output from here on and the final state
+        const SL &st = sm.stage[c & 1];
+        if (failed) {
+            // this chunk's stage was not filled: the state turns NaN, and with it
+            // every output from here on and the final state
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) S[kt] = f32x4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
+            for (int kt = 0; kt < KT; ++kt) S[kt] = f32x4{1.f, 1.f, 1.f, 1.f} * __builtin_nanf("");
+        }
+        const int tro = tile_tr_offset(lane);
+
+        // ---- operands that do not depend on the state
+        f16x4 lt[NSTRICT], inv[NT];
+#pragma unroll
+        for (int i = 0; i < NSTRICT; ++i) lt[i] = h16::tr4(&st.LT[i][tro]);
+#pragma unroll
+        for (int mm = 0; mm < NT; ++mm) inv[mm] = h16::tr4(&st.InvT[mm][tro]);
+        f32x4 bts[NT];
+        row_gather16(st.beta[TILE * (r >> 2) + 4 * gq + (r & 3)], bts);
+        // scaled queries and keys of row tile mm: k-items channels 32j + 4gq + i and 32j + 16 + 4gq + i
+        f16x8 aq[2][KB], ak[2][KB];
+        auto load_rows = [&](int mm, f16x8 (&q8)[KB], f16x8 (&k8)[KB]) {
+            const int row = (TILE * mm + r) * LDK;
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int ch = row + 32 * j + 4 * gq;
+                q8[j] = h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]);
+                k8[j] = h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]);
             }
+        };
+        load_rows(0, aq[0], ak[0]);
 
-            // state slab as fp16 B operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
-            f16x8 Sh[KB];
+        // state slab as fp16 B operands
+        f16x8 Sh[KB];
 #pragma unroll
-            for (int j = 0; j < KB; ++j) Sh[j] = h16::pack8(S[2 * j], S[2 * j + 1]);
+        for (int j = 0; j < KB; ++j) Sh[j] = h16::pack8(S[2 * j], S[2 * j + 1]);
 
-            // (Gamma.Q) S and X = V - (Gamma.K) S, scaled by beta
-            f32x4 accQ[NT], Y[NT], bts[NT];
-            row_gather16(st.beta[TILE * (r >> 2) + 4 * gq + (r & 3)], bts);
+        // ---- (Gamma.Q) S, computed transposed (the state slab as A operand,
+        // the scaled queries as B): lane (g, r) then holds output columns
+        // 4g..4g+3 of token r, four consecutive floats for one wide store;
+        // and Y = beta (V - (Gamma.K) S) in the state's own layout
+        f32x4 accQ[NT], Y[NT];
 #pragma unroll
-            for (int mm = 0; mm < NT; ++mm) {
-                f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
-                const int row = (TILE * mm + r) * LDK;
+        for (int mm = 0; mm < NT; ++mm) {
+            if (mm + 1 < NT) load_rows(mm + 1, aq[(mm + 1) & 1], ak[(mm + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < KB; ++j) {
-                    const int ch = row + 32 * j + 4 * gq;
-                    aQ = h16::mma32(h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]), Sh[j], aQ);
-                    aK = h16::mma32(h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]), Sh[j], aK);
-                }
-                accQ[mm] = aQ;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Y[mm][i] = bts[mm][i] * (to_f32(vin[mm][i]) - aK[i]);
+            for (int j = 0; j < KB; ++j) {
+                aQ = h16::mma32(Sh[j], aq[mm & 1][j], aQ);
+                aK = h16::mma32(ak[mm & 1][j], Sh[j], aK);
             }
+            accQ[mm] = aQ;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Y[mm][i] = bts[mm][i] * (to_f32(vcur[mm][i]) - aK[i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 
-            // U = (I + L)^-1 Diag(beta) X, one tile at a time
-            const int tro = tile_tr_offset(lane);
-            f16x4 Uh[NT], Ul[NT];
-            f32x4 U[NT];
+        // ---- A_qk tiles, read while the solve runs
+        f16x4 aqk[NLOWER];
 #pragma unroll
-            for (int mm = 0; mm < NT; ++mm) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int n = 0; n < mm; ++n)
-                    acc = h16::mma16(h16::tr4(&st.LT[strict_index(mm, n)][tro]), Uh[n], acc);
-                f16x4 rh, rl;
-                h16::split4(Y[mm] - acc, rh, rl);
-                const f16x4 aa = h16::tr4(&st.InvT[mm][tro]);
-                f32x4 uu = h16::mma16(aa, rh, f32x4{0.f, 0.f, 0.f, 0.f});
-                uu = h16::mma16(aa, rl, uu);
-                U[mm] = uu;
-                h16::split4(uu, Uh[mm], Ul[mm]);
-            }
+        for (int i = 0; i < NLOWER; ++i) aqk[i] = h16::tr4(&st.AqkT[i][tro]);
 
-            // O = (Gamma.Q) S + A_qk U, stored straight from the accumulators
-            const bool full = (c + 1) * C <= T;
-            const auto orr = rsrc(o_head + (size_t)c * C * Hdv);
-            auto store_o = [&](int row, float x) {
-                if constexpr (OBF)
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(x), orr, lane_v * 2u, (uint32_t)row * o_stride, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), orr, lane_v * 4u, (uint32_t)row * o_stride, 0);
-            };
+        // ---- U = (I + L)^-1 Diag(beta) X, one tile at a time
+        f16x4 Uh[NT], Ul[NT];
 #pragma unroll
-            for (int mm = 0; mm < NT; ++mm) {
-                f32x4 acc = accQ[mm];
+        for (int mm = 0; mm < NT; ++mm) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int n = 0; n <= mm; ++n) {
-                    const f16x4 aa = h16::tr4(&st.AqkT[lower_index(mm, n)][tro]);
-                    acc = h16::mma16(aa, Uh[n], acc);
-                    acc = h16::mma16(aa, Ul[n], acc);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = c * C + TILE * mm + 4 * gq + i;
-                    if (o && (full || t < T))
-                        store_o(TILE * mm + i, acc[i]);
-                }
-            }
+            for (int n = 0; n < mm; ++n) acc = h16::mma16(lt[strict_index(mm, n)], Uh[n], acc);
+            f16x4 rh, rl;
+            h16::split4(Y[mm] - acc, rh, rl);
+            f32x4 uu = h16::mma16(inv[mm], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+            uu = h16::mma16(inv[mm], rl, uu);
+            h16::split4(uu, Uh[mm], Ul[mm]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 
-            // S <- Diag(Gamma_C) S + K-bar^T U; K-bar^T read transposed from its token rows
-            // U's two fp16 terms as 8-item B operands (k-items: tokens of tiles 2j2 and 2j2 + 1)
-            f16x8 Ubh[2], Ubl[2];
+        // ---- K-bar^T operands of the first four state row tiles, read during the output products
+        const int tk = h16::tr_offset(lane, LDKB);
+        auto load_kb = [&](int kt, f16x8 (&k8)[2]) {
 #pragma unroll
             for (int j2 = 0; j2 < 2; ++j2) {
-                Ubh[j2] = __builtin_shufflevector(Uh[2 * j2], Uh[2 * j2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-                Ubl[j2] = __builtin_shufflevector(Ul[2 * j2], Ul[2 * j2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                const _Float16 *base = &st.Kb[(32 * j2) * LDKB + 16 * kt + tk];
+                k8[j2] = __builtin_shufflevector(h16::tr4(base), h16::tr4(base + 16 * LDKB), 0, 1, 2, 3, 4, 5, 6, 7);
             }
-            const int tk = h16::tr_offset(lane, LDKB);
-            static_assert(KT % 4 == 0, "row tiles of the state come in fours");
-            f32x4 gam[4];
+        };
+        f16x8 kb[KT][2];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                if (kt % 4 == 0) row_gather16(st.GamC[16 * (kt + (r >> 2)) + 4 * gq + (r & 3)], gam);
-                f32x4 acc = S[kt] * gam[kt % 4];
+        for (int kt = 0; kt < KT / 2; ++kt) load_kb(kt, kb[kt]);
+        f32x4 gam[KT / 4][4];
+        static_assert(KT % 4 == 0, "row tiles of the state come in fours");
 #pragma unroll
-                for (int j2 = 0; j2 < 2; ++j2) {
-                    const _Float16 *base = &st.Kb[(32 * j2) * LDKB + 16 * kt + tk];
-                    const f16x4 a0 = h16::tr4(base);
-                    const f16x4 a1 = h16::tr4(base + 16 * LDKB);
-                    const f16x8 aa = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    acc = h16::mma32(aa, Ubh[j2], acc);
-                    acc = h16::mma32(aa, Ubl[j2], acc);
-                }
-                S[kt] = acc;
+        for (int q4 = 0; q4 < KT / 4; ++q4) row_gather16(st.GamC[16 * (4 * q4 + (r >> 2)) + 4 * gq + (r & 3)], gam[q4]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O^T = ((Gamma.Q) S)^T + U^T A_qk^T (U as the A operand, the A_qk
+        // tiles as B): lane (g, r) holds four consecutive columns of token r,
+        // one wide store per row tile
+        const auto orr = rsrc(o_head + (size_t)c * C * Hdv);
+        const uint32_t o_lane = (uint32_t)r * o_stride + (uint32_t)(4 * gq) * (uint32_t)sizeof(OT);
+#pragma unroll
+        for (int mm = 0; mm < NT; ++mm) {
+            f32x4 acc = accQ[mm];
+#pragma unroll
+            for (int n = 0; n <= mm; ++n) {
+                acc = h16::mma16(Uh[n], aqk[lower_index(mm, n)], acc);
+                acc = h16::mma16(Ul[n], aqk[lower_index(mm, n)], acc);
+            }
+            if (o && c * C + TILE * mm + r < T) {
+                if constexpr (OBF)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{(uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16),
+                              (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16)},
+                        orr, o_lane, (uint32_t)(TILE * mm) * o_stride, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), orr, o_lane,
+                                                           (uint32_t)(TILE * mm) * o_stride, 0);
             }
         }
+#pragma unroll
+        for (int kt = KT / 2; kt < KT; ++kt) load_kb(kt, kb[kt]);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // the next chunk's slot is in LDS (every wave waited for its share)
+        // ---- S <- Diag(Gamma_C) S + K-bar^T U, U's two fp16 terms as 8-item B operands
+        // (k-items: the tokens of tiles 2 j2 and 2 j2 + 1)
+        f16x8 Ubh[2], Ubl[2];
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+            Ubh[j2] = __builtin_shufflevector(Uh[2 * j2], Uh[2 * j2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            Ubl[j2] = __builtin_shufflevector(Ul[2 * j2], Ul[2 * j2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+            f32x4 acc = S[kt] * gam[kt / 4][kt % 4];
+#pragma unroll
+            for (int j2 = 0; j2 < 2; ++j2) {
+                acc = h16::mma32(kb[kt][j2], Ubh[j2], acc);
+                acc = h16::mma32(kb[kt][j2], Ubl[j2], acc);
+            }
+            S[kt] = acc;
+        }
+
+        // the next chunk's slot is in LDS (every state wave waited for its share)
         wait_vm();
-        lds_barrier();
-        failed = ss.failed != 0u;
+        state_meet();
+        failed = __builtin_amdgcn_readfirstlane(sm.failed) != 0u;
         if (c + 1 < nchunks && w == 0 && lane == 0)
-            post64(&consumed[((c + 1) % RING) * MAXSTATE + jst], tag(epoch, failed ? FAILED : (uint32_t)(c + 2)));
+            post64(&consumed[((c + 1) % NSLOT) * MAXSLAB + slab], tag(epoch, failed ? FAILED : (uint32_t)(c + 2)));
+    };
+    for (int c = 0; c < nchunks; ++c) {
+        chunk_step(c, vin, vnx);
 #pragma unroll
         for (int mm = 0; mm < NT; ++mm)
 #pragma unroll
             for (int i = 0; i < 4; ++i) vin[mm][i] = vnx[mm][i];
     }
     if (failed && w == 0 && lane == 0) {
-        // release the prep side from every slot wait
-        for (int sl = 0; sl < RING; ++sl) post64(&consumed[sl * MAXSTATE + jst], tag(epoch, FAILED));
+        // release every prep team from its slot waits
+        for (int sl = 0; sl < NSLOT; ++sl) post64(&consumed[sl * MAXSLAB + slab], tag(epoch, FAILED));
     }
-    if (active && a.S_final) {
+    if (a.S_final) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -776,17 +847,16 @@ uint32_t next_epoch() {
     return e;
 }
 
-int nstate_for(int dv) { return (dv + SCOLS - 1) / SCOLS; }
+int nslab_for(int dv) { return dv / SLAB; }
 
 template <int DK>
 size_t slot_bytes() { return sizeof(Slot<DK>); }
 
 // Heads per launch: every workgroup of a launch must be resident at once (one
-// workgroup per CU at this LDS size), and a head's 1 + nstate workgroups are
-// spread as 8 heads per (1 + nstate) x 8 block indices.
-int group_heads(int resident, int nstate) {
-    const int P = 1 + nstate;
-    const int per8 = resident / (8 * P);
+// workgroup per CU at this LDS size), and a head's nslab workgroups are
+// spread as 8 heads per nslab x 8 block indices.
+int group_heads(int resident, int nslab) {
+    const int per8 = resident / (8 * nslab);
     return min(PS_MAX_GROUP, 8 * per8);
 }
 
@@ -817,26 +887,26 @@ hipError_t launch(const ChunkFwdArgs &ca, void *ws, size_t ws_bytes, hipStream_t
 {
     used = false;
     const void *kern = kernel_ptr<DK, GBF, OBF, GL>();
-    const int nstate = nstate_for(ca.dv);
+    const int nslab = nslab_for(ca.dv);
     const int BH = ca.B * ca.H;
-    const int G = min(group_heads(resident_workgroups(kern), nstate), BH);
+    const int G = min(group_heads(resident_workgroups(kern), nslab), BH);
     if (G <= 0) return hipSuccess;   // not resident together: the caller takes the other kernel
     const size_t slot_off = ((size_t)G * FLAG_BYTES + 255) & ~(size_t)255;
-    const size_t need = slot_off + (size_t)G * RING * sizeof(Slot<DK>);
+    const size_t need = slot_off + (size_t)G * NSLOT * sizeof(Slot<DK>);
     if (!ws || ws_bytes < need) return hipSuccess;
     used = true;
     PsArgs a;
     a.q = (const uint16_t *)ca.q; a.k = (const uint16_t *)ca.k; a.v = (const uint16_t *)ca.v;
     a.g = ca.g; a.beta = ca.beta; a.S0 = ca.S0; a.o = ca.o; a.S_final = ca.S_final; a.A_log = ca.A_log;
     a.ws = (unsigned char *)ws; a.slot_off = slot_off;
-    a.B = ca.B; a.T = ca.T; a.H = ca.H; a.dv = ca.dv; a.nstate = nstate;
+    a.B = ca.B; a.T = ca.T; a.H = ca.H; a.dv = ca.dv; a.nslab = nslab;
     a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
     (void)hipGetLastError();
     for (int h0 = 0; h0 < BH; h0 += G) {
         a.h_begin = h0;
         a.G = min(G, BH - h0);
         a.epoch = next_epoch();
-        const unsigned grid = (unsigned)(8 * ((a.G + 7) / 8) * (1 + nstate));
+        const unsigned grid = (unsigned)(8 * ((a.G + 7) / 8) * nslab);
         void *args[] = {&a};
         const hipError_t e = hipLaunchCooperativeKernel(kern, dim3(grid), dim3(NTHREADS), args, 0, stream);
         if (e != hipSuccess) return e;
@@ -856,16 +926,18 @@ hipError_t dispatch(const ChunkFwdArgs &a, void *ws, size_t n, hipStream_t s, bo
 
 size_t chunk_ps_workspace_bytes(int B, int H, int dk, int dv)
 {
-    if (dk != 128 || dv <= 0 || dv % 64 != 0 || dv > 512 || B <= 0 || H <= 0) return 0;
+    if (dk != 128 || dv < 2 * SLAB || dv % SLAB != 0 || dv > SLAB * MAXSLAB || B <= 0 || H <= 0) return 0;
     const int G = min(PS_MAX_GROUP, B * H);
     const size_t slot_off = ((size_t)G * FLAG_BYTES + 255) & ~(size_t)255;
-    return slot_off + (size_t)G * RING * sizeof(Slot<128>);
+    return slot_off + (size_t)G * NSLOT * sizeof(Slot<128>);
 }
 
 hipError_t launch_chunk_fwd_ps(const ChunkFwdArgs &a, void *ws, size_t ws_bytes, hipStream_t stream, bool &used)
 {
     used = false;
-    if (!a.qkv_bf16 || a.dk != 128 || a.lengths || a.dv % 64 != 0 || a.dv > 512) return hipSuccess;
+    // one slab per head shares nothing: the ring would only add its copies
+    if (!a.qkv_bf16 || a.dk != 128 || a.lengths || a.dv < 2 * SLAB || a.dv % SLAB != 0 || a.dv > SLAB * MAXSLAB)
+        return hipSuccess;
     // buffer offsets inside one chunk (64 rows of H * dv values) stay 32-bit
     if ((uint64_t)C * a.H * a.dv * 4 + (uint64_t)a.H * a.dv * 4 >= ((uint64_t)1 << 31)) return hipSuccess;
     return a.A_log ? dispatch<128, true>(a, ws, ws_bytes, stream, used) : dispatch<128, false>(a, ws, ws_bytes, stream, used);

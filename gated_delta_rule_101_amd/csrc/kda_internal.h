@@ -75,8 +75,8 @@ struct ChunkBwdArgs {
 };
 
 hipError_t launch_chunk_fwd(const ChunkFwdArgs &a, hipStream_t stream);        // any dtypes
-// Prep/state workgroup pairs through a ring in the workspace (bfloat16 q, k, v,
-// dk = 128, dv a multiple of 64 up to 512, no per-sequence lengths).  `used` is
+// Prep/state workgroups through a ring in the workspace (bfloat16 q, k, v,
+// dk = 128, dv a multiple of 64 from 128 to 512, no per-sequence lengths).  `used` is
 // false when the call is not taken (shape, or a workspace that is missing or
 // too small): the caller then launches the other kernels.
 constexpr int PS_MAX_GROUP = 128;   // heads per launch, at most

@@ -155,6 +155,23 @@ def _workspace(lib, workspace, B, T, H, dk, dv, device):
     return workspace
 
 
+def _ring_pays(q: torch.Tensor, B: int, H: int, dk: int, dv: int) -> bool:
+    """Whether the workspace (ring) kernel is the faster choice for this call:
+    its workgroups share each head's state-independent chunk work, which pays
+    while the grid (B H dv/64 workgroups) fills at most half the device
+    (include/kda.h states the measured ratios)."""
+    if q.dtype != torch.bfloat16 or dk != 128 or dv < 128 or dv % 64 or dv > 512 or not q.is_cuda:
+        return False
+    cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+    return 2 * B * H * (dv // 64) <= cus
+
+
+def _use_ring(ring: Optional[bool], workspace, q, B, H, dk, dv) -> bool:
+    if ring is not None:
+        return ring
+    return workspace is not None or _ring_pays(q, B, H, dk, dv)
+
+
 def _nbytes(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
@@ -163,7 +180,7 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
                   output_final_state: bool = True, o: Optional[torch.Tensor] = None,
                   S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                  ring: bool = True, workspace: Optional[torch.Tensor] = None,
+                  ring: Optional[bool] = None, workspace: Optional[torch.Tensor] = None,
                   stream: Optional[torch.cuda.Stream] = None
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA forward.  Shapes as in include/kda.h:
@@ -172,7 +189,9 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     unless out_dtype (or a passed `o`) says bfloat16.  `S_final` may be passed
     (and may be S0 itself for an in-place continuation).  With ring=True the
     call goes through kda_chunk_fwd_ws with `workspace` (device bytes; allocated
-    here when not given), ring=False calls kda_chunk_fwd."""
+    here when not given), ring=False calls kda_chunk_fwd; ring=None (default)
+    takes the workspace path when a workspace is passed or the ring kernel is
+    the faster one for the shape."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -188,6 +207,7 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         raise ValueError("o must be [B,T,H,dv]")
     if S_final is None and output_final_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    ring = _use_ring(ring, workspace, q, B, H, dk, dv)
     ws = _workspace(lib, workspace, B, T, H, dk, dv, q.device) if ring else None
     dev = _check_dev(q, k, v, g, beta, S0, o, S_final, ws)
     if ring:
@@ -251,7 +271,7 @@ def kda_chunk_fwd_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: tor
                        A_log: torch.Tensor, beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
                        output_final_state: bool = True, o: Optional[torch.Tensor] = None,
                        S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                       ring: bool = True, workspace: Optional[torch.Tensor] = None,
+                       ring: Optional[bool] = None, workspace: Optional[torch.Tensor] = None,
                        stream: Optional[torch.cuda.Stream] = None
                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """kda_chunk_fwd with the log-decay formed in the kernel from gate logits:
@@ -268,6 +288,7 @@ def kda_chunk_fwd_gate(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: tor
         raise ValueError("o must be [B,T,H,dv]")
     if S_final is None and output_final_state:
         S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    ring = _use_ring(ring, workspace, q, B, H, dk, dv)
     ws = _workspace(lib, workspace, B, T, H, dk, dv, q.device) if ring else None
     dev = _check_dev(q, k, v, z, A_log, beta, S0, o, S_final, ws)
     if ring:

@@ -169,13 +169,18 @@ kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
 /*
  * kda_chunk_fwd_ws, kda_chunk_fwd_gate_ws -- kda_chunk_fwd and
  * kda_chunk_fwd_gate with a caller-owned workspace.  The workspace lets
- * bfloat16 q, k, v with dk = 128 (dv a multiple of 64 up to 512) take the
- * prep/state kernel: per head, one workgroup computes the state-independent
- * part of every chunk of the chunkwise form ("Kimi K3 - Lesson 3 of 14 -
- * Sequence axis", the chunkwise diagram: decays, 1/Gamma-rescaled operands,
- * intra-chunk Gram tiles, the diagonal inverses) exactly once and hands it,
- * through a three-slot ring held in the workspace, to the workgroups that
- * carry the state.  Other inputs run the kernels of kda_chunk_fwd.
+ * bfloat16 q, k, v with dk = 128 (dv a multiple of 64 from 128 to 512) take
+ * the ring kernel: a head's dv columns are split over dv / 64 workgroups,
+ * which take turns computing the state-independent part of the chunks of the
+ * chunkwise form ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the chunkwise
+ * diagram: decays, 1/Gamma-rescaled operands, intra-chunk Gram tiles, the
+ * diagonal inverses), so each chunk's part is computed once per head instead
+ * of once per workgroup, and hand it to one another through a four-slot ring
+ * per head held in the workspace.  Other inputs run the kernels of
+ * kda_chunk_fwd.  The ring pays when the grid (B H dv / 64 workgroups) fills
+ * at most half the device, and more the larger dv is (about 0.88x the time
+ * of kda_chunk_fwd at dv = 128, 0.75x at dv = 256, 0.66x at dv = 512, T =
+ * 4096); a full-device grid at dv = 128 runs faster without it (1.1x).
  *
  *   workspace        device memory of at least kda_chunk_fwd_workspace_bytes(B,
  *                    T, H, dk, dv) bytes, 16-byte aligned, owned by the caller;

@@ -245,6 +245,7 @@ def test_workspace_forward_validation(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(B, 0, H, d, d) == 0     # nothing to run
     assert lib.kda_chunk_fwd_workspace_bytes(B, T, H, 64, 64) == 0   # dk = 64: no workspace used
     assert lib.kda_chunk_fwd_workspace_bytes(B, T, H, d, 96) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(B, T, H, d, 64) == 0    # one slab per head: nothing to share
     # more heads than one launch holds: the ring is sized for one launch
     assert lib.kda_chunk_fwd_workspace_bytes(4, T, 64, d, d) == lib.kda_chunk_fwd_workspace_bytes(4, T, 32, d, d)
     names = ("q", "k", "v", "g", "beta", "S0", "o", "Sf", "ws")
