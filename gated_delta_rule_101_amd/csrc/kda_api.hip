@@ -229,6 +229,31 @@ kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v, con
     return run_chunk(a, stream);
 }
 
+kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+                                   const void *beta, const float *S0, void *o, float *S_final,
+                                   int B, int T, int H, int dk, int dv,
+                                   kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                   void *stream)
+{
+    const kda_status_t st = check_chunk(q, k, v, g, beta, S0, o, S_final, nullptr, nullptr, B, T, H, dk, dv,
+                                        qkv_dtype, gate_dtype, out_dtype, true, true);
+    if (st != KDA_OK) return st;
+    if (B == 0 || H == 0) return KDA_OK;
+    kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S0, o, S_final, B, T, H, dk, dv,
+                                     qkv_dtype, gate_dtype, out_dtype);
+    const size_t need = T > 0 && qkv_dtype == KDA_BF16 ? kda::chunk_ps_workspace_bytes(B, H, dk, dv) : 0;
+    if (need > 0) {
+        // the ring kernel applies: its ring goes into the library's own scratch
+        if (need > kda::noalloc_scratch_bytes()) return KDA_ERR_SCRATCH;
+        void *ws = nullptr;
+        if (kda::noalloc_scratch((hipStream_t)stream, &ws) != hipSuccess) return KDA_ERR_LAUNCH;
+        bool used = false;
+        const hipError_t e = kda::launch_chunk_fwd_ps(a, ws, kda::noalloc_scratch_bytes(), (hipStream_t)stream, used);
+        if (used) return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+    return run_chunk(a, stream);
+}
+
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv)
 {
     if (T <= 0) return 0;
@@ -430,6 +455,7 @@ const char *kda_status_string(kda_status_t status)
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: null, misaligned or overlapping pointer, bad size or dtype";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk/dv combination not provided";
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
+    case KDA_ERR_SCRATCH: return "KDA_ERR_SCRATCH: the input needs more scratch than kda_chunk_fwd_noalloc holds";
     }
     return "KDA_ERR_UNKNOWN";
 }

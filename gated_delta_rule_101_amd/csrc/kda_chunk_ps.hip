@@ -45,6 +45,7 @@
 #include <atomic>
 #include <chrono>
 #include <cstddef>
+#include <mutex>
 
 #include "kda_chunk_tiles.h"
 #include "kda_device.h"
@@ -922,7 +923,46 @@ hipError_t dispatch(const ChunkFwdArgs &a, void *ws, size_t n, hipStream_t s, bo
     return a.out_bf16 ? launch<DK, false, true, GL>(a, ws, n, s, used) : launch<DK, false, false, GL>(a, ws, n, s, used);
 }
 
+// The ring of the no-allocation entry point: file-scope device memory, one
+// copy per device, held until the process ends.  Host code reaches it only
+// through the per-device address that hipGetSymbolAddress returns (the
+// array's name on the host is a stand-in, not a device address).
+constexpr size_t NOALLOC_BYTES =
+    (((size_t)NOALLOC_HEADS * FLAG_BYTES + 255) & ~(size_t)255) + (size_t)NOALLOC_HEADS * NSLOT * sizeof(Slot<128>);
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
 }  // namespace
+
+size_t noalloc_scratch_bytes() { return NOALLOC_BYTES; }
+
+hipError_t noalloc_scratch(hipStream_t stream, void **out)
+{
+    *out = nullptr;
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (stream && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // looked up once per device, with that device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t chunk_ps_workspace_bytes(int B, int H, int dk, int dv)
 {

@@ -83,6 +83,11 @@ constexpr int PS_MAX_GROUP = 128;   // heads per launch, at most
 hipError_t launch_chunk_fwd_ps(const ChunkFwdArgs &a, void *workspace, size_t workspace_bytes,
                                hipStream_t stream, bool &used);
 size_t chunk_ps_workspace_bytes(int B, int H, int dk, int dv);   // 0: the pair kernel does not apply
+// The ring kernel's workspace inside the library (no allocation): a device
+// array sized for NOALLOC_HEADS heads, its address on the stream's device.
+constexpr int NOALLOC_HEADS = 64;
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t stream, void **out);
 // Bound on every spin wait of the chunk kernels (sleeps between polls); the
 // previous value is returned.  A wait that runs out marks the call failed.
 unsigned set_spin_limit(unsigned limit);

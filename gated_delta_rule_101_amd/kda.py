@@ -26,10 +26,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_SCRATCH = 0, 1, 2, 3, 4
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_chunk_fwd_ws", "kda_chunk_fwd_gate_ws",
+           "kda_chunk_fwd_noalloc",
            "kda_chunk_fwd_workspace_bytes", "kda_debug_set_spin_limit", "kda_verify_step", "kda_commit_step",
            "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_status_string", "kda_abi_version")
@@ -61,6 +62,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_gate.restype = i
     sz = ctypes.c_size_t
     lib.kda_chunk_fwd_ws.argtypes = [vp] * 9 + [sz] + [i] * 8 + [vp]
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp] * 8 + [i] * 8 + [vp]
+    lib.kda_chunk_fwd_noalloc.restype = i
     lib.kda_chunk_fwd_ws.restype = i
     lib.kda_chunk_fwd_gate_ws.argtypes = [vp] * 10 + [sz] + [i] * 8 + [vp]
     lib.kda_chunk_fwd_gate_ws.restype = i
@@ -221,6 +224,27 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                                _dtype_code(o), _stream_handle(stream, dev))
         _raise(st, "kda_chunk_fwd")
     return o, S_final
+
+
+def kda_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, S0: Optional[torch.Tensor], o: torch.Tensor,
+                          S_final: Optional[torch.Tensor], stream: Optional[torch.cuda.Stream] = None) -> None:
+    """kda_chunk_fwd_noalloc: the workspace forward with the library's own fixed
+    scratch as the ring; o and S_final are the caller's (shapes as
+    kda_chunk_fwd).  Raises KdaError (status KDA_ERR_SCRATCH) for inputs beyond
+    the scratch."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch between q, k, v, g, beta")
+    if o.shape != (B, T, H, dv) or (S_final is not None and S_final.shape != (B, H, dk, dv)):
+        raise ValueError("o must be [B,T,H,dv], S_final [B,H,dk,dv]")
+    dev = _check_dev(q, k, v, g, beta, S0, o, S_final)
+    st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                   _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(g),
+                                   _dtype_code(o), _stream_handle(stream, dev))
+    _raise(st, "kda_chunk_fwd_noalloc")
 
 
 def kda_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

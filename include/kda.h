@@ -84,11 +84,12 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,  /* NULL / misaligned / overlapping pointer, negative size, bad dtype */
     KDA_ERR_UNSUPPORTED = 2,  /* valid but not provided: dk or dv outside the supported set */
-    KDA_ERR_LAUNCH = 3        /* the HIP runtime rejected the kernel launch */
+    KDA_ERR_LAUNCH = 3,       /* the HIP runtime rejected the kernel launch */
+    KDA_ERR_SCRATCH = 4       /* kda_chunk_fwd_noalloc: input beyond its fixed scratch */
 } kda_status_t;
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 /*
  * kda_chunk_fwd -- chunkwise forward over T tokens for B sequences x H heads.
@@ -212,6 +213,30 @@ kda_status_t kda_chunk_fwd_gate_ws(const void *q, const void *k, const void *v,
                                    const float *S0, void *o, float *S_final,
                                    void *workspace, size_t workspace_bytes,
                                    int B, int T, int H, int dk, int dv,
+                                   kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                                   kda_dtype_t out_dtype, void *stream);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd_ws for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the ring lives in a device array inside the library
+ * instead of a caller's workspace.  The call allocates nothing and calls no
+ * allocating routine.
+ *
+ * Arguments, preconditions, results and errors as kda_chunk_fwd_ws without
+ * the workspace.  The array holds the ring of 64 heads (about 15.8 MiB per
+ * device, kept until the process ends): where the ring kernel applies
+ * (bfloat16 q, k, v, dk = 128, dv a multiple of 64 from 128 to 512) and B * H
+ * exceeds 64, the call returns KDA_ERR_SCRATCH and enqueues nothing; other
+ * inputs run the kernels of kda_chunk_fwd, which use no scratch.  Every call
+ * on one device shares that device's array: calls that overlap in time on one
+ * device (two streams, two threads) race and give undefined results; calls
+ * ordered on one stream do not.  The array's contents carry over from call to
+ * call and need no clearing (each launch tags its flags with a fresh epoch).
+ */
+kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                   const void *g, const void *beta, const float *S0,
+                                   void *o, float *S_final, int B, int T, int H, int dk, int dv,
                                    kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
                                    kda_dtype_t out_dtype, void *stream);
 

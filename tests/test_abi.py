@@ -44,8 +44,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     from gated_delta_rule_101_amd import kda
-    assert lib.kda_abi_version() == 5
-    for st in (kda.KDA_OK, kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_LAUNCH):
+    assert lib.kda_abi_version() == 6
+    for st in (kda.KDA_OK, kda.KDA_ERR_INVALID_ARG, kda.KDA_ERR_UNSUPPORTED, kda.KDA_ERR_LAUNCH,
+               kda.KDA_ERR_SCRATCH):
         assert lib.kda_status_string(st).decode().startswith("KDA_")
     assert lib.kda_status_string(77).decode() == "KDA_ERR_UNKNOWN"
 
@@ -269,6 +270,15 @@ def test_workspace_forward_validation(lib):
         kw.get("ws", base["ws"]), kw.get("size", need), B, T, H, d, d, 1, 1, 0, None)
     assert gate(A=None) == INV
     assert gate(size=1) == INV
+    # kda_chunk_fwd_noalloc: the forward's checks, and inputs beyond its fixed scratch
+    # (the ring of 64 heads) refused before anything is enqueued
+    SCR = kda.KDA_ERR_SCRATCH
+    na = lambda B=B, H=H, dv=d, qd=1, q=base["q"]: lib.kda_chunk_fwd_noalloc(  # noqa: E731
+        q, base["k"], base["v"], base["g"], base["beta"], None, base["o"], None, B, T, H, d, dv, qd, 1, 0, None)
+    assert na(q=None) == INV
+    assert na(B=0) == OK
+    assert na(B=5, H=13) == SCR                          # 65 heads with the ring
+    assert na(B=4, H=16, dv=96) == UNS
     # the spin-bound hook returns the previous bound
     old = lib.kda_debug_set_spin_limit(123)
     assert lib.kda_debug_set_spin_limit(old) == 123
