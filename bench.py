@@ -12,12 +12,16 @@ tokens, commit 8 of them) is reported under "speculative", the output
 epilogue (alone over the training-shape reads, and fused into decode) under
 "epilogue", the chunkwise backward under "backward", and two secondary
 forward workloads (one head group B1 H8 T4096, a latency figure; the long
-sequence B1 H96 T131072) under "forward_secondary".  Each carries a
+sequence B1 H96 T131072) under "forward_secondary", and the forward and decode with the log-decay formed
+in the kernel from gate logits under "gate_prologue".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
 by HIP events on the launch stream, and `traffic`: the HBM bytes per launch
 that the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in
 profiles/traffic.json, or null when the kernel's source has changed since
 (for the backward, one launch is one call: the sum over its five kernels).
+"peaks" holds what plain kernels reach on the same device (a streaming copy,
+a loop of independent bf16 matrix-core products); every roofline also states
+its fraction of that achievable peak.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -56,6 +60,29 @@ def fwd_bytes(B, T, H, dk, dv, s_qkv, s_g, s_o, s0: bool, sfinal: bool) -> int:
     return B * T * H * per_tok + (int(s0) + int(sfinal)) * 4 * B * H * dk * dv
 
 
+def fwd_executed_flops(B, T, H, dk, dv, C=CHUNK, tile=16) -> int:
+    """Matrix-core FLOP the bf16 forward kernels execute, counted per 16x16
+    tile product as issued (2 x 16 x 16 x K per instruction), including the
+    zero halves of triangular tiles, the second terms of two-term operands and
+    the state-independent work each dv/64 slab workgroup repeats:
+      per chunk and slab (value columns 64): (Gamma.Q) S and (Gamma.K) S,
+        2 x (C/16) x (dk/32) 16x16x32 products per 16 columns; the blocked
+        solve, 6 strict tiles + 4 inverses x 2 terms, 16x16x16; the outputs,
+        10 lower tiles x 2 terms, 16x16x16; the state update, (dk/16) x 2 x 2
+        16x16x32;
+      per chunk and slab, the prep: the in-tile cumsum, (C/16) x (dk/16)
+        16x16x16; the diagonal Gram tiles, (C/16) x (dk/32) x 4 16x16x32; the
+        6 off-diagonal tiles, 6 x (dk/32) x 2 16x16x32."""
+    nt, kb, kt = C // tile, dk // 32, dk // 16
+    m32, m16 = 2 * 16 * 16 * 32, 2 * 16 * 16 * 16
+    cols = dv // 16
+    state = cols * ((2 * nt * kb + kt * 2 * 2) * m32 + (6 + 4 * 2 + 10 * 2) * m16)
+    nslab = max(1, dv // 64)
+    prep = nslab * ((nt * kb * 4 + 6 * kb * 2) * m32 + nt * kt * m16)
+    chunks = B * H * ((T + C - 1) // C)
+    return chunks * (state + prep)
+
+
 def fwd_flops(B, T, H, dk, dv, C=CHUNK) -> int:
     """Algorithmic FLOP of the chunkwise form per token-head: three C x d x d
     products (Gamma.Q S, Gamma.K S, K-bar^T U) = 6 dk dv; the four C x C x d
@@ -81,7 +108,10 @@ def gated_decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) -> int:
     return decode_bytes(B, H, dk, dv, s_qkv, s_g, s_o) + B * H * dv * s_qkv + 4 * dv
 
 
-def bwd_flops(B, T, H, dk, dv, C=CHUNK) -> int:
+BWD_CHUNK = 32   # the backward kernels' chunk length
+
+
+def bwd_flops(B, T, H, dk, dv, C=BWD_CHUNK) -> int:
     """Algorithmic FLOP of the chunkwise backward per token-head: eight
     C x d x d products with the state or its gradient (recomputed W S and
     K-bar^T U; K-bar dS', (Gamma.Q)^T dO, W^T dU; dO S^T, dU S^T, U dS'^T)
@@ -111,6 +141,8 @@ CHUNK_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk_pipe.hip", "gated_delt
                  "gated_delta_rule_101_amd/build_lib.py"]
 DECODE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_decode.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
                   "gated_delta_rule_101_amd/build_lib.py"]
+RING_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_chunk_ps.hip", "gated_delta_rule_101_amd/csrc/kda_chunk_tiles.h",
+                "gated_delta_rule_101_amd/csrc/kda_device.h", "gated_delta_rule_101_amd/build_lib.py"]
 BWD_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_bwd.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
                "gated_delta_rule_101_amd/build_lib.py"]
 VERIFY_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_verify.hip", "gated_delta_rule_101_amd/csrc/kda_device.h",
@@ -122,6 +154,7 @@ EPILOGUE_SOURCES = ["gated_delta_rule_101_amd/csrc/kda_epilogue.hip", "gated_del
 # template argument), the output epilogue is the stand-alone one
 SINGLE_KERNELS = (
     ("kda_chunk_fwd", ("kda_chunk_pipe_kernel",), CHUNK_SOURCES),
+    ("kda_chunk_fwd_ws", ("kda_chunk_ps_kernel",), RING_SOURCES),
     ("kda_decode_step", ("kda_decode_kernel",), DECODE_SOURCES),
     ("kda_verify_step", ("kda_verify_tile_kernel<", "false>("), VERIFY_SOURCES),
     ("kda_commit_step", ("kda_verify_tile_kernel<", "true>("), VERIFY_SOURCES),
@@ -147,9 +180,10 @@ def stored_traffic(kernel: str, sources) -> "dict | None":
 
 # ------------------------------------------------------------------- timing
 
-def time_launches(fn, steps, warmup, stream):
+def time_launches(fn, steps, warmup, stream, per_launch=False):
     """Wall time of `steps` back-to-back calls and the mean kernel duration
-    from HIP events recorded around each launch on `stream`."""
+    from HIP events recorded around each launch on `stream` (and, with
+    per_launch, the list of the launches' durations in seconds)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -162,8 +196,19 @@ def time_launches(fn, steps, warmup, stream):
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ker = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
-    return wall, ker
+    each = [a.elapsed_time(b) * 1e-3 for a, b in ev]
+    ker = sum(each) / steps
+    return (wall, ker, each) if per_launch else (wall, ker)
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+# achievable peaks measured by bench_peaks (None until measured)
+ACHIEVABLE = {"hbm_GBs": None, "bf16_TFLOPs": None}
 
 
 def roofline(algo_bytes_per_launch, kernel_s, traffic_rec):
@@ -171,8 +216,69 @@ def roofline(algo_bytes_per_launch, kernel_s, traffic_rec):
     traffic = None
     if traffic_rec:
         traffic = traffic_rec["hbm_bytes_per_launch"]
-    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    out = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+    if ACHIEVABLE["hbm_GBs"]:
+        out["achievable_peak"] = ACHIEVABLE["hbm_GBs"]
+        out["frac_of_achievable"] = round(achieved / ACHIEVABLE["hbm_GBs"], 4)
+    return out
+
+
+def bench_peaks(reps=10):
+    """What plain kernels reach here: a 1 GiB streaming device copy (bytes read
+    plus bytes written per second) and a loop of independent bf16 16x16x32
+    matrix-core products on every CU (FLOP per second)."""
+    import ctypes
+    import torch
+    from gated_delta_rule_101_amd.build_lib import PROBE_LIBRARY
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.kda_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.kda_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def copy():
+        assert lib.kda_probe_copy(src.data_ptr(), dst.data_ptr(), n, sh) == 0
+
+    _, ker, each = time_launches(copy, reps, 3, stream, per_launch=True)
+    probe_gbs = 2 * n / min(each) / 1e9
+    _, ker, each = time_launches(lambda: dst.copy_(src), reps, 3, stream, per_launch=True)
+    runtime_gbs = 2 * n / min(each) / 1e9
+    lib.kda_probe_update.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p]
+
+    def update():
+        assert lib.kda_probe_update(src.data_ptr(), n, 0, sh) == 0
+
+    _, ker, each = time_launches(update, reps, 3, stream, per_launch=True)
+    update_gbs = 2 * n / min(each) / 1e9
+    copy_gbs = max(probe_gbs, runtime_gbs, update_gbs)
+    del src, dst
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 4 * cus, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    rates = {}
+    for big, shape, flop_per in ((0, "16x16x32", 8 * 16384), (1, "32x32x16", 4 * 32768)):
+        def mfma():
+            assert lib.kda_probe_mfma(out.data_ptr(), blocks, iters, big, sh) == 0
+
+        _, ker_m, each_m = time_launches(mfma, reps, 3, stream, per_launch=True)
+        rates[shape] = blocks * 4 * iters * flop_per / min(each_m) / 1e12
+    tfs = max(rates.values())
+    ACHIEVABLE["hbm_GBs"] = round(copy_gbs, 1)
+    ACHIEVABLE["bf16_TFLOPs"] = round(tfs, 1)
+    log(f"[bench] peaks: device copy {copy_gbs:.0f} GB/s, bf16 MFMA loop {tfs:.0f} TFLOP/s")
+    return {"hbm_copy": {"GB/s": round(copy_gbs, 1), "frac_of_published": round(copy_gbs / HBM_PEAK_GBS, 4),
+                         "by_kernel_GB/s": {"probe_copy": round(probe_gbs, 1), "torch_copy": round(runtime_gbs, 1),
+                                            "probe_in_place": round(update_gbs, 1)},
+                         "sample": f"1 GiB moved each way: a copy (the probe kernel, torch's copy_) and an "
+                                   f"in-place read-modify-write; the fastest, read + write bytes, best of {reps}"},
+            "mfma_bf16": {"TFLOP/s": round(tfs, 1), "frac_of_published": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4),
+                          "by_shape_TFLOP/s": {k: round(v, 1) for k, v in rates.items()},
+                          "sample": f"{blocks} workgroups x 4 waves x {iters} rounds of independent bf16 products "
+                                    f"(8 of 16x16x32 or 4 of 32x32x16), the faster shape, best of {reps}"}}
 
 
 # --------------------------------------------------------------- workloads
@@ -191,28 +297,48 @@ def bench_fwd(kda, steps, warmup):
         kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], None, o=o, S_final=Sf)
 
     log(f"[bench] chunk_fwd: {warmup} warmup + {steps} timed launches")
-    wall, ker = time_launches(step, steps, warmup, stream)
+    wall, ker, each = time_launches(step, steps, warmup, stream, per_launch=True)
     nbytes = fwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 4, s0=False, sfinal=True)
+    nbytes_bf16_o = fwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 2, s0=False, sfinal=True)
     flops = fwd_flops(w.B, w.T, w.H, w.dk, w.dv)
+    executed = fwd_executed_flops(w.B, w.T, w.H, w.dk, w.dv)
     ms = wall / steps * 1e3
     tok_s = w.B * w.T / (wall / steps)
-    log(f"[bench] chunk_fwd {ms:.3f} ms/step (kernel {ker * 1e3:.3f} ms), {tok_s:.3e} tokens/s")
+    log(f"[bench] chunk_fwd {ms:.3f} ms/step (kernel mean {ker * 1e3:.3f}, median {median(each) * 1e3:.3f}, "
+        f"min {min(each) * 1e3:.3f} ms), {tok_s:.3e} tokens/s")
     rf = roofline(nbytes, ker, stored_traffic("kda_chunk_fwd", CHUNK_SOURCES))
-    tflops = flops / (wall / steps) / 1e12
+    # the same kernel time against the byte count with a bfloat16 o (the
+    # survey's count; the kernel writes float32 o here)
+    rf["frac_bf16_o_count"] = round(nbytes_bf16_o / ker / 1e9 / HBM_PEAK_GBS, 4)
+    rf["bytes_bf16_o_count"] = nbytes_bf16_o
+    tflops = flops / ker / 1e12
+    ex_tflops = executed / ker / 1e12
     extra = {
-        "tflops": round(tflops, 2),
+        "tflops": round(flops / (wall / steps) / 1e12, 2),
         "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "executed_mfma_flop_per_step": executed,
+        "executed_mfma_tflops": round(ex_tflops, 2),
+        "executed_mfma_frac": round(ex_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "algorithmic_flop_per_step": flops,
         "algorithmic_bytes_per_step": nbytes,
+        "kernel": "kda_chunk_pipe_kernel (no workspace: the ring kernel is slower on a full-device grid)",
         "kernel_ms": round(ker * 1e3, 4),
+        "kernel_ms_median": round(median(each) * 1e3, 4),
+        "kernel_ms_min": round(min(each) * 1e3, 4),
+        "timed_launches": steps,
     }
+    if ACHIEVABLE["bf16_TFLOPs"]:
+        extra["executed_mfma_frac_of_achievable"] = round(ex_tflops / ACHIEVABLE["bf16_TFLOPs"], 4)
     return w, d, ms, tok_s, rf, extra
 
 
 def bench_fwd_secondary(kda, w, steps, warmup):
     """Secondary forward workloads, timed like the headline one: the single
     head group (B1 H8 T4096: eight sequential carries, a latency figure) and
-    the long single sequence (B1 H96 T131072: 2048 chunks per carry)."""
+    the long single sequence (B1 H96 T131072: 2048 chunks per carry).  Both
+    forward kernels are timed: the pipelined one (kda_chunk_fwd) and the ring
+    one (kda_chunk_fwd_ws, its workspace allocated before timing); the figures
+    at the top of the record are the faster one's."""
     import torch
     from kda_workloads import gen_torch
     log(f"[bench] generating {w.name} on the device")
@@ -220,22 +346,89 @@ def bench_fwd_secondary(kda, w, steps, warmup):
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-
-    def step():
-        kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o=o, S_final=Sf)
-
-    wall, ker = time_launches(step, steps, warmup, stream)
+    need = kda.kda_chunk_fwd_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     s_q, s_g = (2 if w.qkv == "bf16" else 4), (2 if w.gate == "bf16" else 4)
     nbytes = fwd_bytes(w.B, w.T, w.H, w.dk, w.dv, s_q, s_g, 4, s0=d["S0"] is not None, sfinal=True)
     flops = fwd_flops(w.B, w.T, w.H, w.dk, w.dv)
-    ms = wall / steps * 1e3
-    log(f"[bench] {w.name} {ms:.3f} ms/step (kernel {ker * 1e3:.3f} ms)")
-    out = {"workload": w.name, "ms": round(ms, 4), "kernel_ms": round(ker * 1e3, 4),
-           "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
-           "tflops": round(flops / (wall / steps) / 1e12, 2),
-           "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}
-    del d, o, Sf
+    runs = {}
+    for name, ring in (("pipelined", False), ("ring", True)):
+        if ring and ws is None:
+            continue
+
+        def step():
+            kda.kda_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o=o, S_final=Sf,
+                              ring=ring, workspace=ws if ring else None)
+
+        wall, ker, each = time_launches(step, steps, warmup, stream, per_launch=True)
+        ms = wall / steps * 1e3
+        log(f"[bench] {w.name} {name}: {ms:.3f} ms/step (kernel mean {ker * 1e3:.3f}, min {min(each) * 1e3:.3f} ms)")
+        runs[name] = {"ms": round(ms, 4), "kernel_ms": round(ker * 1e3, 4),
+                      "kernel_ms_median": round(median(each) * 1e3, 4), "kernel_ms_min": round(min(each) * 1e3, 4),
+                      "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+                      "tflops": round(flops / (wall / steps) / 1e12, 2),
+                      "roofline": roofline(nbytes, ker, stored_traffic("kda_chunk_fwd_ws", RING_SOURCES)
+                                           if ring and w.name == "kda_fwd_B1_H8_T4096_d128_bf16" else None)}
+    best = min(runs, key=lambda k: runs[k]["ms"])
+    out = {"workload": w.name, "faster_kernel": best, **runs[best], "algorithmic_bytes": nbytes,
+           "kernels": runs}
+    del d, o, Sf, ws
     torch.cuda.empty_cache()
+    return out
+
+
+def bench_gate_prologue(kda, steps=10, decode_reps=1):
+    """The gate prologue: the log-decay formed inside the kernels from gate
+    logits z and per-head scales A_log, g = -5 sigmoid(exp(A_log) z).  The
+    chunked forward on the training shape (bf16 z; it reads z where the plain
+    forward reads g) and the decode step on the decode workload."""
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.TRAIN_BF16
+    d = gen_torch.fwd_inputs(w)
+    z = d["g"].float().mul_(-1.0).to(d["g"].dtype)   # logits of the same shape and dtype as g
+    del d["g"]
+    A_log = torch.linspace(-1.0, 1.0, w.H, device="cuda")
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        kda.kda_chunk_fwd_gate(d["q"], d["k"], d["v"], z, A_log, d["beta"], None, o=o, S_final=Sf, ring=False)
+
+    wall, ker, each = time_launches(fwd, steps, 2, stream, per_launch=True)
+    nbytes = fwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 4, s0=False, sfinal=True) + 4 * w.H
+    ms = wall / steps * 1e3
+    log(f"[bench] chunk_fwd_gate {ms:.3f} ms/step (kernel mean {ker * 1e3:.3f} ms)")
+    out = {"chunk_fwd_gate": {"workload": w.name + "_gate_logits", "ms": round(ms, 4), "kernel_ms": round(ker * 1e3, 4),
+                              "kernel_ms_min": round(min(each) * 1e3, 4),
+                              "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+                              "algorithmic_bytes": nbytes, "roofline": roofline(nbytes, ker, None)}}
+    del d, z, o, Sf
+    torch.cuda.empty_cache()
+
+    dw = configs.DECODE_BF16
+    S = gen_torch.decode_initial_state(dw)
+    xs = [gen_torch.decode_step_inputs(dw, s) for s in range(dw.steps)]
+    zs = [x["g"].float().mul(-1.0).to(x["g"].dtype) for x in xs]
+    A_d = torch.linspace(-1.0, 1.0, dw.H, device="cuda")
+    od = torch.empty((dw.B, dw.H, dw.dv), dtype=torch.float32, device="cuda")
+    it = {"i": 0}
+
+    def one():
+        i = it["i"] % dw.steps
+        it["i"] += 1
+        x = xs[i]
+        kda.kda_decode_step_gate(x["q"], x["k"], x["v"], zs[i], A_d, x["beta"], S, o=od)
+
+    n = dw.steps * decode_reps
+    wall, ker = time_launches(one, n, dw.steps // 4, stream)
+    per_step = decode_bytes(dw.B, dw.H, dw.dk, dw.dv, 2, 4, 4) + 4 * dw.H
+    gbs = per_step * n / wall / 1e9
+    log(f"[bench] decode_step_gate {wall / n * 1e3:.3f} ms/step (kernel {ker * 1e3:.3f} ms), {gbs:.1f} GB/s")
+    out["decode_step_gate"] = {"workload": dw.name + "_gate_logits", "ms_per_step": round(wall / n * 1e3, 4),
+                               "GB/s": round(gbs, 1), "algorithmic_bytes_per_step": per_step,
+                               "roofline": roofline(per_step, ker, None)}
     return out
 
 
@@ -378,7 +571,7 @@ def bench_backward(kda, reps=3):
         torch.cuda.synchronize()
         return None
     wall, ker = time_launches(fn, reps, 1, stream)
-    flops = bwd_flops(w.B, w.T, w.H, w.dk, w.dv)
+    flops = bwd_flops(w.B, w.T, w.H, w.dk, w.dv)   # at the kernels' 32-token chunks
     nbytes = bwd_bytes(w.B, w.T, w.H, w.dk, w.dv, 2, 2, 4)
     tfs = flops / ker / 1e12
     log(f"[bench] backward {wall / reps * 1e3:.3f} ms (kernels {ker * 1e3:.3f} ms), {tfs:.1f} TFLOP/s, "
@@ -425,7 +618,14 @@ def cpu_baseline(w, d, batch=32):
     dt1 = time.perf_counter() - t0
     flop_head_tok = 7 * w.dk * w.dv   # fade, the two state-vector products and the rank-one update
     log(f"[bench] cpu baseline, one thread: {w.T} tokens of one head in {dt1:.2f} s")
+    try:
+        affinity = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = None
     return {"value": round(tok_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host": {"nproc": os.cpu_count(), "affinity_cpus": len(affinity) if affinity is not None else None,
+                     "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+                     "oracle_threads": threads},
             "sample": f"all {n_all} heads x {w.T} tokens of {w.name} (the full step), float64 "
                       f"token recurrence, {batch} heads per call, {dt:.2f} s wall",
             "gflops_f64": round(w.B * w.T * w.H * flop_head_tok / dt / 1e9, 2),
@@ -442,7 +642,8 @@ COPY_BYTES = 1 << 30   # the calibration copy moves 1 GiB each way
 def profile_pass(kda, reps=3):
     """A short run for `rocprofv3 --pmc`: a plain device copy of known size
     (calibrates the byte counters), then the chunked forward and the decode
-    step of the benchmark workloads, `reps` launches each, verify and commit
+    step of the benchmark workloads, `reps` launches each, the ring forward
+    on the head-group workload (`reps` launches), verify and commit
     of the speculative workload and the output epilogue (three launches
     each), and one backward call (its five kernels) on the training shape."""
     import torch
@@ -456,6 +657,15 @@ def profile_pass(kda, reps=3):
     w, d, *_ = bench_fwd(kda, reps, 1)
     del d
     torch.cuda.empty_cache()
+    # the ring kernel on the workload where it is the faster one (one head group)
+    hw = configs.HEADGROUP_BF16
+    hd = gen_torch.fwd_inputs(hw)
+    ws = torch.empty(kda.kda_chunk_fwd_workspace_bytes(hw.B, hw.T, hw.H, hw.dk, hw.dv), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(reps):
+        kda.kda_chunk_fwd(hd["q"], hd["k"], hd["v"], hd["g"], hd["beta"], hd["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    del hd, ws
     bench_decode(kda, 1)
     bench_speculative(kda, 1)
     bench_epilogue(kda, reps=1, fused=False)   # the fused decode would mix into the decode record
@@ -530,7 +740,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -562,6 +772,7 @@ def main():
         print(json.dumps(bench_backward(kda, reps=2)), flush=True)
         return
 
+    peaks = bench_peaks()
     w, d, ms, tok_s, rf, extra = bench_fwd(kda, args.steps, args.warmup)
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -573,6 +784,7 @@ def main():
                    "state": "f32"},
         **extra,
         "roofline": rf,
+        "peaks": peaks,
     }
     if not args.no_decode:
         from kda_workloads import configs
@@ -582,6 +794,7 @@ def main():
         out["speculative"] = bench_speculative(kda, 10)
         out["epilogue"] = bench_epilogue(kda)
         out["backward"] = bench_backward(kda)
+        out["gate_prologue"] = bench_gate_prologue(kda)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d)
     print(json.dumps(out), flush=True)

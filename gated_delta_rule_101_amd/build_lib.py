@@ -19,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libkda.so")
+PROBE_LIBRARY = os.path.join(HERE, "libkda_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -80,6 +81,14 @@ def build_library(verbose: bool = False) -> str:
     os.replace(tmp, LIBRARY)
     if verbose:
         print(f"built {LIBRARY}", file=sys.stderr)
+    # the benchmark's achievable-peak probes: a library of their own
+    probe_src = os.path.join(HERE, "probe", "peaks.hip")
+    if os.path.exists(probe_src):
+        tmp = PROBE_LIBRARY + f".tmp{os.getpid()}"
+        _run([cc, *HIPCC_FLAGS, "-shared", "-o", tmp, probe_src])
+        os.replace(tmp, PROBE_LIBRARY)
+        if verbose:
+            print(f"built {PROBE_LIBRARY}", file=sys.stderr)
     return LIBRARY
 
 

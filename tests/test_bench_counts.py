@@ -43,9 +43,24 @@ def test_epilogue_counts():
         bench.decode_bytes(256, 96, 128, 128, 2, 4, 4) + 256 * 96 * 128 * 2 + 4 * 128
 
 
+def test_executed_forward_flops():
+    # one chunk of one head, dk = dv = 128 (two 64-column slabs, eight 16-column state waves).
+    # per state wave: (Gamma.Q) S and (Gamma.K) S, 4 row tiles x 4 k-blocks x 2; the state
+    # update, 8 row tiles x 2 token halves x 2 terms (16x16x32); the solve, 6 strict tiles
+    # + 4 inverses x 2 terms, and the outputs, 10 lower tiles x 2 terms (16x16x16)
+    m32, m16 = 2 * 16 * 16 * 32, 2 * 16 * 16 * 16
+    state = 8 * ((32 + 32) * m32 + (6 + 8 + 20) * m16)
+    # per slab: cumsum 4 tiles x 8 channel tiles (16x16x16), diagonal Gram 4 tiles x 4
+    # k-blocks x 4 products, off-diagonal 6 tiles x 4 k-blocks x 2 (16x16x32)
+    prep = 2 * ((4 * 4 * 4 + 6 * 4 * 2) * m32 + 4 * 8 * m16)
+    assert bench.fwd_executed_flops(1, 64, 1, 128, 128) == state + prep == 14811136
+    # a ragged last chunk still runs whole tiles
+    assert bench.fwd_executed_flops(1, 65, 1, 128, 128) == 2 * 14811136
+
+
 def test_backward_counts():
-    # per token-head at C = 64, d = 128: 16 d^2 + 9 C d + 5 C d + C^2
-    assert bench.bwd_flops(1, 1, 1, 128, 128) == 16 * 16384 + 14 * 64 * 128 + 4096 == 380928
+    # per token-head at the kernels' C = 32, d = 128: 16 d^2 + 9 C d + 5 C d + C^2
+    assert bench.bwd_flops(1, 1, 1, 128, 128) == 16 * 16384 + 14 * 32 * 128 + 1024 == 320512
     # bf16 q, k, v, g, beta and fp32 dO read; fp32 dq, dk, dg (d each), dv (d), dbeta written
     per = 2 * 384 + 2 * 129 + 4 * 128 + 4 * (3 * 128 + 128 + 1)
     assert bench.bwd_bytes(4, 16384, 32, 128, 128, 2, 2, 4) == 4 * 16384 * 32 * per
