@@ -746,6 +746,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short run for rocprofv3 --pmc: calibration copy, then each kernel a few times")
+    ap.add_argument("--profile-pass-fwd", action="store_true",
+                    help="short run for rocprofv3 --pmc: the headline forward only, three launches")
     ap.add_argument("--only-backward", action="store_true",
                     help="run only the backward leg (two calls) and print its JSON object")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -767,6 +769,9 @@ def main():
     kda.load_library()
     if args.profile_pass:
         profile_pass(kda)
+        return
+    if args.profile_pass_fwd:
+        bench_fwd(kda, 3, 1)
         return
     if args.only_backward:
         print(json.dumps(bench_backward(kda, reps=2)), flush=True)
