@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import shutil
 import subprocess
 import tempfile
 from typing import Optional, Tuple
@@ -50,6 +51,23 @@ def _c64(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
+G_MIN = -5.0
+
+
+def check_preconditions(q, k, v, g, beta, S=None) -> None:
+    """The method's input domain: every input finite, and every log-decay in
+    [g_min, 0] = [-5, 0] ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the g_min
+    paragraphs: the scaled-sigmoid mapping holds each channel's log-decay
+    between -5 and 0, which is what bounds the in-tile 1/Gamma rescale by e^80).
+    The recurrence itself is defined for any g; this is a tripwire for inputs
+    the GPU path does not accept.  Raises ValueError."""
+    for name, x in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("S", S)):
+        if x is not None and not np.all(np.isfinite(x)):
+            raise ValueError(f"oracle input {name} holds a non-finite value")
+    if g.size and (np.min(g) < G_MIN or np.max(g) > 0.0):
+        raise ValueError(f"oracle log-decay outside [{G_MIN}, 0]: [{np.min(g)}, {np.max(g)}]")
+
+
 class Oracle:
     """Handle on one built copy of the C oracle."""
 
@@ -71,9 +89,12 @@ class Oracle:
         return int(self.lib.kda_oracle_max_threads())
 
     def fwd(self, q, k, v, g, beta, S0=None, *, want_state: bool = True,
-            nthreads: int = 0) -> Tuple[np.ndarray, Optional[np.ndarray]]:
-        """Token-by-token forward.  Returns (o [B,T,H,dv], S_final [B,H,dk,dv] or None)."""
+            nthreads: int = 0, check: bool = True) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+        """Token-by-token forward.  Returns (o [B,T,H,dv], S_final [B,H,dk,dv] or None).
+        With `check`, inputs outside the method's domain raise (check_preconditions)."""
         q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+        if check:
+            check_preconditions(q, k, v, g, beta, S0)
         B, T, H, dk = q.shape
         dv = v.shape[-1]
         assert k.shape == q.shape and g.shape == q.shape
@@ -90,9 +111,12 @@ class Oracle:
             raise RuntimeError("kda_oracle_fwd failed")
         return o, Sf
 
-    def decode_step(self, q, k, v, g, beta, S, *, nthreads: int = 0) -> np.ndarray:
-        """One token for every (b, h): S [B,H,dk,dv] float64 updated IN PLACE; returns o [B,H,dv]."""
+    def decode_step(self, q, k, v, g, beta, S, *, nthreads: int = 0, check: bool = True) -> np.ndarray:
+        """One token for every (b, h): S [B,H,dk,dv] float64 updated IN PLACE; returns o [B,H,dv].
+        With `check`, inputs outside the method's domain raise (check_preconditions)."""
         q, k, v, g, beta = (_c64(x) for x in (q, k, v, g, beta))
+        if check:
+            check_preconditions(q, k, v, g, beta, S)
         assert isinstance(S, np.ndarray) and S.dtype == np.float64 and S.flags.c_contiguous
         B, H, dk = q.shape
         dv = v.shape[-1]
@@ -176,8 +200,11 @@ def build_variant(source_text: str) -> Oracle:
     on the CPU to show that the pins catch them.
     """
     d = tempfile.mkdtemp(prefix="kda_oracle_variant_")
-    src = os.path.join(d, "variant.c")
-    with open(src, "w") as f:
-        f.write(source_text)
-    lib = compile_oracle(src, os.path.join(d, "libvariant.so"))
-    return Oracle(lib)
+    try:
+        src = os.path.join(d, "variant.c")
+        with open(src, "w") as f:
+            f.write(source_text)
+        # once loaded, the library stays mapped after its file is removed
+        return Oracle(compile_oracle(src, os.path.join(d, "libvariant.so")))
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
