@@ -456,6 +456,7 @@ const char *kda_status_string(kda_status_t status)
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: dk/dv combination not provided";
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected the kernel launch";
     case KDA_ERR_SCRATCH: return "KDA_ERR_SCRATCH: the input needs more scratch than kda_chunk_fwd_noalloc holds";
+    default: break;
     }
     return "KDA_ERR_UNKNOWN";
 }

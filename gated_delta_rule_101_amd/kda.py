@@ -23,7 +23,8 @@ from typing import Optional, Tuple
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(HERE, "libkda.so")
+# KDA_LIBRARY selects another build of the library (a sanitizer build, say)
+LIBRARY = os.environ.get("KDA_LIBRARY") or os.path.join(HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_SCRATCH = 0, 1, 2, 3, 4

@@ -75,9 +75,14 @@
 extern "C" {
 #endif
 
+/* Both enums span the whole int range (the two range members), so any int a
+ * caller passes is a value of the type: out-of-set values are rejected by
+ * the checks, not undefined behaviour. */
 typedef enum {
     KDA_F32 = 0,   /* IEEE float32 */
-    KDA_BF16 = 1   /* bfloat16 (round-to-nearest-even when produced) */
+    KDA_BF16 = 1,  /* bfloat16 (round-to-nearest-even when produced) */
+    KDA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    KDA_DTYPE_RANGE_MAX_ = 2147483647
 } kda_dtype_t;
 
 typedef enum {
@@ -85,7 +90,9 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1,  /* NULL / misaligned / overlapping pointer, negative size, bad dtype */
     KDA_ERR_UNSUPPORTED = 2,  /* valid but not provided: dk or dv outside the supported set */
     KDA_ERR_LAUNCH = 3,       /* the HIP runtime rejected the kernel launch */
-    KDA_ERR_SCRATCH = 4       /* kda_chunk_fwd_noalloc: input beyond its fixed scratch */
+    KDA_ERR_SCRATCH = 4,      /* kda_chunk_fwd_noalloc: input beyond its fixed scratch */
+    KDA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    KDA_STATUS_RANGE_MAX_ = 2147483647
 } kda_status_t;
 
 /* ABI version of this header; bumped on any incompatible change. */
@@ -374,7 +381,7 @@ kda_status_t kda_chunk_bwd(const void *q, const void *k, const void *v, const vo
                            void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
-const char *kda_status_string(kda_status_t status);
+const char *kda_status_string(kda_status_t status);   /* codes outside the set: "KDA_ERR_UNKNOWN" */
 
 /* KDA_ABI_VERSION of the built library. */
 int kda_abi_version(void);

@@ -135,7 +135,9 @@ _DEFAULT: Optional[Oracle] = None
 def default() -> Oracle:
     global _DEFAULT
     if _DEFAULT is None:
-        _DEFAULT = Oracle()
+        # KDA_ORACLE_LIBRARY: another build of the oracle (the sanitizer build of its tests)
+        alt = os.environ.get("KDA_ORACLE_LIBRARY")
+        _DEFAULT = Oracle(alt) if alt else Oracle()
     return _DEFAULT
 
 
