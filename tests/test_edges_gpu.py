@@ -81,10 +81,11 @@ RINGS = [True, False]
 
 @pytest.mark.parametrize("ring", RINGS, ids=["ring", "pipelined"])
 def test_large_values_within_bound(kda, orc, ring):
-    """v scaled by 2^11 (exact in bf16): |o| and |S| reach the thousands."""
+    """v scaled by 2^13 (exact in bf16): |o| and |S| reach the thousands (the
+    largest values stay inside the fp16 range of the operands)."""
     w = T_.scaled(B=1, H=2, T=64 * 6 + 9, name="edge_large_v")
     x = gen.fwd_inputs(w, seed=21)
-    x = _with(x, "v", x["v"].values * np.float32(2048.0))
+    x = _with(x, "v", x["v"].values * np.float32(8192.0))
     say(f"[large v] ring={ring} {w.name}")
     o, S = _run_fwd(kda, x, ring)
     o_ref, S_ref = _oracle_fwd(orc, x)
