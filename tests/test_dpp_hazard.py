@@ -1,9 +1,10 @@
-"""The inverse in the bf16 chunk kernel fuses a DPP row broadcast into v_fmac
+"""The inverse in the bf16 chunk kernels fuses a DPP row broadcast into v_fmac
 through inline assembly, which the compiler's hazard recognizer does not see
 into.  gfx950 needs two wait states between a vector-ALU write of a VGPR and a
-DPP read of it; this test compiles the kernel source to gfx950 assembly (no
-GPU needed) and checks that no broadcast source is written by a vector-ALU
-instruction within the two preceding instructions."""
+DPP read of it; this test compiles each kernel source to gfx950 assembly (no
+GPU needed) with the flags the build uses for that file, and checks that no
+broadcast source is written by a vector-ALU instruction within the two
+preceding instructions."""
 
 import os
 import re
@@ -13,7 +14,8 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "gated_delta_rule_101_amd", "csrc", "kda_chunk_pipe.hip")
+# both bf16 chunk kernels run the inverse with the fused broadcast
+SOURCES = [os.path.join(ROOT, "gated_delta_rule_101_amd", "csrc", f) for f in ("kda_chunk_pipe.hip", "kda_chunk_ps.hip")]
 
 
 def _vregs(tok):
@@ -51,14 +53,19 @@ def dpp_hazards(asm_text):
     return checked, bad
 
 
-def test_dpp_broadcast_sources_have_their_wait_states(tmp_path):
+@pytest.mark.parametrize("src", SOURCES, ids=[os.path.basename(x) for x in SOURCES])
+def test_dpp_broadcast_sources_have_their_wait_states(tmp_path, src):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    from gated_delta_rule_101_amd.build_lib import HIPCC_FLAGS
-    flags = [f for f in HIPCC_FLAGS if f != "-fPIC"]
+    from gated_delta_rule_101_amd.build_lib import HIPCC_FLAGS, SOURCE_FLAGS
+    # the flags the shipped object is built with (optimisation level and scheduler included)
+    flags = [f for f in [*HIPCC_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), [])] if f != "-fPIC"]
+    if any(f.startswith("-O") for f in SOURCE_FLAGS.get(os.path.basename(src), [])):
+        flags = [f for f in flags if not f.startswith("-O")] + \
+                [f for f in SOURCE_FLAGS[os.path.basename(src)] if f.startswith("-O")]
     out = tmp_path / "k.o"
-    subprocess.run([hipcc, *flags, "--save-temps", "-c", SRC, "-o", str(out)], cwd=tmp_path,
+    subprocess.run([hipcc, *flags, "--save-temps", "-c", src, "-o", str(out)], cwd=tmp_path,
                    check=True, capture_output=True)
     asm = [f for f in os.listdir(tmp_path) if f.endswith(".s") and "gfx950" in f]
     assert asm, os.listdir(tmp_path)

@@ -60,6 +60,10 @@ SPEC_CASES = [
     # up to 16 drafts with dk = 64 (the matrix-core tile, two 32-channel pairs)
     configs.HEADGROUP_BF16.scaled(B=3, H=2, T=12, dk=64, dv=64, name="spec_bf16_K12_dk64_dv64"),
     configs.TINY_F32.scaled(B=3, H=2, T=9, dk=64, dv=128, s0_sd=0.3, name="spec_f32_K9_dk64_dv128"),
+    # bf16 with dv > 128: verify and commit take the pipelined chunk kernel (commit with
+    # per-sequence lengths = the accepted counts, so its identity-token path runs)
+    configs.HEADGROUP_BF16.scaled(B=3, H=2, T=9, dv=192, name="spec_bf16_K9_dv192"),
+    configs.HEADGROUP_BF16.scaled(B=3, H=2, T=16, dv=256, name="spec_bf16_K16_dv256"),
 ]
 
 
