@@ -114,6 +114,10 @@ struct alignas(16) PipeSmem {
     // that the 16 lanes of a quarter-wave reading 16 bytes of rows 0..15 hit
     // distinct banks
     alignas(16) float LdT[NT][TILE][TILE + 4];
+    // bfloat16 gates of the next chunk for tiles 1..3 ([tile - 1][token][channel]),
+    // loaded straight into LDS so that no registers hold them through the
+    // staging pass (tile 0's producer, the lightest, keeps them in registers)
+    alignas(16) uint16_t gnext[NT - 1][TILE * DK];
     unsigned arrivals;                          // producer meeting counter
     unsigned failed;                            // some producer wait expired (read after the loop)
 };
@@ -241,11 +245,35 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             lds_barrier();
             return;
         }
-        load_g(0, r, gq);
-        load_qk(0, r, gq);
-        lds_barrier();
+        // bfloat16 gates (not logits) of tiles 1..3 come through sm.gnext:
+        // DK / 32 LDS-direct loads of 1 KB per chunk (a token row is DK / 8
+        // lanes of 16 bytes), issued from inline assembly so the compiler does
+        // not make every later LDS read wait for them; the loop top waits for
+        // them by count (only the 2 KT q and k loads are younger)
+        constexpr bool GDMA = GBF && !GL;
+        constexpr int GROW_LANES = DK / 8;          // lanes per token row
+        constexpr int GROWS = 64 / GROW_LANES;      // token rows per load
+        static_assert(TILE % GROWS == 0, "whole loads per tile");
+        auto dma_g = [&](int c, int tm) {
+            const unsigned base = (unsigned)(size_t)&sm.gnext[tm - 1][0];
+#pragma unroll
+            for (int j = 0; j < TILE / GROWS; ++j) {
+                const GT *src = g + token_row(c, GROWS * j + lane / GROW_LANES) * DK + 8 * (lane % GROW_LANES);
+                const unsigned dst = __builtin_amdgcn_readfirstlane(base + 1024u * j);
+                asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(dst) : "memory");
+            }
+        };
         unsigned meetings = 0;   // producer meetings so far (uniform)
         bool all_met = true;     // every meeting completed within its bound
+        // One loop instance per tile: the tile's work, and which of its values
+        // stay live through the loop, are fixed at compile time.
+        auto tile_loop = [&](auto tile) __attribute__((always_inline)) {
+        constexpr int M = decltype(tile)::value;
+        constexpr bool GLDS = GDMA && M >= 1;   // this tile's gates come through LDS
+        if constexpr (GLDS) dma_g(0, M);
+        else load_g(0, r, gq);
+        load_qk(0, r, gq);   // after the gates: the loop top's count relies on the order
+        lds_barrier();
         for (int cn = 0; cn < nchunks; ++cn) {
             {
                 Stage &st = sm.stage[cn & 1];
@@ -260,7 +288,29 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 // ---------------------------------------------- decays within tile m
                 // b = inclusive cumsum of g over the tile's 16 tokens, per channel
                 float f[KT][4];   // f = e^b in [e^-80, 1] (1/f, up to e^80, is recomputed where used)
-                if constexpr (GBF && !GL) {
+                if constexpr (GLDS) {
+                    // the gates' LDS-direct loads are complete once at most the 2 KT
+                    // q and k loads issued after them are outstanding
+                    static_assert(2 * KT < 64, "vmcnt field");
+                    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * KT) & 15) | (((2 * KT) >> 4) << 14));
+                    i16x4 tri;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tri[i] = (4 * gq + i <= r) ? (short)0x3F80 : (short)0;   // bf16 1.0
+                    const int tro = h16::tr_offset(lane, DK);
+                    const _Float16 *gsrc = reinterpret_cast<const _Float16 *>(&sm.gnext[M - 1][0]);
+#pragma unroll
+                    for (int blk = 0; blk < KT; ++blk) {
+                        // channels as rows, tokens 4 gq + i as k-items; tokens past the
+                        // end are identity tokens (g = 0)
+                        i16x4 gt = __builtin_bit_cast(i16x4, h16::tr4(gsrc + 16 * blk + tro));
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (cn * C + TILE * M + 4 * gq + i >= len) gt[i] = 0;
+                        const f32x4 bsum = BF::mma16(gt, tri, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) f[blk][i] = fast_exp2(bsum[i] * LOG2E);
+                    }
+                } else if constexpr (GBF && !GL) {
                     // as a matrix-core product: b^T = g^T Tri, Tri(s, t) = [s <= t].
                     // g goes through this tile's rows of the Qt staging area (rewritten
                     // below) as KT stored 16x16 tiles, read back transposed: channels
@@ -304,7 +354,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         *reinterpret_cast<f32x4 *>(&sm.D[m][16 * blk + 4 * gq]) =
                             f32x4{f[blk][0], f[blk][1], f[blk][2], f[blk][3]};
                 }
-                load_g(cnext, r, gq);
+                if constexpr (!GLDS) load_g(cnext, r, gq);
                 lds_wave_sync();
 
                 // diagonal Gram tile, block (m, m): f-scaled rows against 1/f-scaled
@@ -322,7 +372,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     gk_d = BF::mma32(akh, bih, gk_d);
                 };
 
-                if (m < NT - 1) {
+                if constexpr (M < NT - 1) {
                     // keys decayed to the end of tile m: B operands of the later tiles' Gram blocks
 #pragma unroll
                     for (int blk = 0; blk < KT; ++blk) {
@@ -356,6 +406,9 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         diagonal(qf, kf, ki);
                     }
                 }
+                // the next chunk's gates (tiles 1..3): after every use of this chunk's
+                // gates and of the q, k loaded before them
+                if constexpr (GLDS) dma_g(cnext, M);
                 meetings += 1;
                 all_met = producer_meet(&sm.arrivals, NPROD * meetings, lane, spin_limit) && all_met;
 
@@ -469,13 +522,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     }
                     lds_wave_sync();
                 };
-                static_assert(NT == 4, "one block_row instance per tile");
-                switch (m) {
-                case 0: block_row(TileIndex<0>{}); break;
-                case 1: block_row(TileIndex<1>{}); break;
-                case 2: block_row(TileIndex<2>{}); break;
-                default: block_row(TileIndex<3>{}); break;
-                }
+                block_row(TileIndex<M>{});
                 // ------------------------------------------ (I + L_mm)^-1, lane column r
                 {
                     // column r of L_mm, and X = e_r; `one` is opaque so the 16 selects
@@ -502,6 +549,14 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 }
             }
             lds_barrier();
+        }
+        };
+        static_assert(NT == 4, "one loop instance per tile");
+        switch (m) {
+        case 0: tile_loop(TileIndex<0>{}); break;
+        case 1: tile_loop(TileIndex<1>{}); break;
+        case 2: tile_loop(TileIndex<2>{}); break;
+        default: tile_loop(TileIndex<3>{}); break;
         }
         if (!all_met && lane == 0) sm.failed = 1u;
         lds_barrier();   // the consumers' last chunk

@@ -273,6 +273,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
 
         unsigned meetings = 0;
         bool ok = true;
+        // One loop instance per tile: the tile's work, and which of its values
+        // stay live through the loop, are fixed at compile time.
+        auto tile_loop = [&](auto tile) __attribute__((always_inline)) {
+        constexpr int M = decltype(tile)::value;
         // this workgroup prepares chunks slab, slab + nslab, ...
         if (slab < nchunks) {
             load_g(slab);
@@ -354,7 +358,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
                 gk_d = BF::mma32(akh, bih, gk_d);
             };
 
-            if (m < NT - 1) {
+            if constexpr (M < NT - 1) {
 #pragma unroll
                 for (int blk = 0; blk < KT; ++blk) {
                     const int ch = 16 * blk + 4 * gq;
@@ -508,13 +512,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
                 }
                 lds_wave_sync();
             };
-            static_assert(NT == 4, "one block_row instance per tile");
-            switch (m) {
-            case 0: block_row(TileIndex<0>{}); break;
-            case 1: block_row(TileIndex<1>{}); break;
-            case 2: block_row(TileIndex<2>{}); break;
-            default: block_row(TileIndex<3>{}); break;
-            }
+            block_row(TileIndex<M>{});
             if (m == 0) st->beta[lane] = bcur;
 
             // ------------------------------------------ (I + L_mm)^-1, lane column r
@@ -545,6 +543,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) kda_chunk_ps_kernel(PsArgs a)
             meetings += 1;
             ok = lds_meet(&ts.arrivals, NPROD * meetings, lane, limit);
             if (ok && leader && lane == 0) post64(&ready[slot], tag(epoch, (uint32_t)(cn + 1)));
+        }
+        };
+        static_assert(NT == 4, "one loop instance per tile");
+        switch (m) {
+        case 0: tile_loop(TileIndex<0>{}); break;
+        case 1: tile_loop(TileIndex<1>{}); break;
+        case 2: tile_loop(TileIndex<2>{}); break;
+        default: tile_loop(TileIndex<3>{}); break;
         }
         if (!ok && leader && lane == 0) {
             // a wait expired: the state side stops waiting and writes NaN
