@@ -53,6 +53,9 @@
 namespace kda {
 namespace {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int C = 64;             // tokens per chunk
 constexpr int TILE = 16;          // tokens per tile
 constexpr int NT = C / TILE;      // tiles per chunk
@@ -567,25 +570,37 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         const size_t Hdv = (size_t)H * dv;
         const uint32_t lane_v = (uint32_t)(4 * gq * H * dv + r);   // rows 4gq + i, column r
 
-        f32x4 S[KT];          // rows 16kt + 4gq + i, column r
-        uint16_t vin[NT][4];  // V rows 16mm + 4gq + i, column r
+        f32x4 S[KT];           // rows 16kt + 4gq + i, column r
+        uint16_t vin[NT][4];   // V rows 16mm + 4gq + i, column r, of the chunk being computed
+        uint16_t vnx[NT][4];   // the same for the next chunk
+        // V and o of this consumer's columns are addressed through buffer
+        // resources based at the chunk's first row: the row's byte offset inside
+        // the chunk is a scalar (soffset), the lane's column and row group a fixed
+        // voffset, so no vector instruction computes an address (the launcher
+        // keeps these offsets below 2^31).
+        const uint16_t *v_head = v + ((size_t)b * T * H + h) * dv + col0;
+        OT *o_head = o ? o + ((size_t)b * T * H + h) * dv + col0 : nullptr;
+        const uint32_t v_stride = (uint32_t)Hdv * 2u, o_stride = (uint32_t)Hdv * (uint32_t)sizeof(OT);
+        auto rsrc = [](const void *base) {
+            return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+        };
         // V of chunk c.  A token past the end reads the last token instead (its
-        // beta is zero, so its value never enters U); a full chunk needs no
-        // clamping and addresses every row from one uniform base.
-        auto load_v = [&](int c) {
+        // beta is zero, so its value never enters U).
+        auto load_v = [&](int c, uint16_t (&dst)[NT][4]) {
+            const auto vr = rsrc(v_head + (size_t)c * C * Hdv);
             if ((c + 1) * C <= T) {
-                const uint16_t *vb = v + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0 + lane_v;
 #pragma unroll
                 for (int mm = 0; mm < NT; ++mm)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) vin[mm][i] = vb[(size_t)(TILE * mm + i) * Hdv];
+                    for (int i = 0; i < 4; ++i)
+                        dst[mm][i] = __builtin_amdgcn_raw_buffer_load_b16(vr, lane_v * 2u, (uint32_t)(TILE * mm + i) * v_stride, 0);
             } else {
 #pragma unroll
                 for (int mm = 0; mm < NT; ++mm)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int t = min(c * C + TILE * mm + 4 * gq + i, T - 1);
-                        vin[mm][i] = v[(((size_t)b * T + t) * H + h) * dv + col0 + r];
+                        const int t = min(TILE * mm + 4 * gq + i, T - 1 - c * C);
+                        dst[mm][i] = __builtin_amdgcn_raw_buffer_load_b16(vr, (uint32_t)t * v_stride + 2u * r, 0u, 0);
                     }
             }
         };
@@ -607,105 +622,168 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 S[kt][i] = S0 ? S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
-        if (nchunks > 0) load_v(0);
+        if (nchunks > 0) load_v(0, vin);
         lds_barrier();
-        for (int c = -1; c < nchunks; ++c) {
-            if (c >= 0) {
-                const Stage &st = sm.stage[c & 1];
 
+        // One chunk of the recurrence.  The next chunk's V is requested first;
+        // LDS operands are read ahead of the products that use them: the
+        // state-independent tiles first, each row tile's scaled queries and
+        // keys while the previous row tile's products run, K-bar during the
+        // output products.  Scheduling fences keep the compiler from sinking
+        // the reads back next to their uses.
+        auto chunk_step = [&](int c) __attribute__((always_inline)) {
+            // this chunk's V (requested a chunk ago) and the previous chunk's
+            // output stores are complete; the compiler's wait tracking learns it here
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            if (c + 1 < nchunks) load_v(c + 1, vnx);
+            const Stage &st = sm.stage[c & 1];
+            const int tro = tile_tr_offset(lane);
 
-                // state slab as fp16 B operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
-                f16x8 Sh[KB];
+            // ---- operands that do not depend on the state
+            f16x4 lt[NSTRICT], inv[NT];
 #pragma unroll
-                for (int j = 0; j < KB; ++j) Sh[j] = h16::pack8(S[2 * j], S[2 * j + 1]);
-
-                // (Gamma.Q) S and X = V - (Gamma.K) S, scaled by beta
-                f32x4 accQ[NT], Y[NT], bts[NT];
-                row_gather16(sm.betas[c % 3][TILE * (r >> 2) + 4 * gq + (r & 3)], bts);
+            for (int i = 0; i < NSTRICT; ++i) lt[i] = h16::tr4(&st.LT[i][tro]);
 #pragma unroll
-                for (int mm = 0; mm < NT; ++mm) {
-                    f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
-                    const int row = (TILE * mm + r) * LDK;
+            for (int mm = 0; mm < NT; ++mm) inv[mm] = h16::tr4(&st.InvT[mm][tro]);
+            f32x4 bts[NT];
+            row_gather16(sm.betas[c % 3][TILE * (r >> 2) + 4 * gq + (r & 3)], bts);
+            // scaled queries and keys of row tile mm: k-items channels 32j + 4gq + i and 32j + 16 + 4gq + i
+            f16x8 aq[2][KB], ak[2][KB];
+            auto load_rows = [&](int mm, f16x8 (&q8)[KB], f16x8 (&k8)[KB]) {
+                const int row = (TILE * mm + r) * LDK;
 #pragma unroll
-                    for (int j = 0; j < KB; ++j) {
-                        const int ch = row + 32 * j + 4 * gq;
-                        aQ = h16::mma32(h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]), Sh[j], aQ);
-                        aK = h16::mma32(h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]), Sh[j], aK);
-                    }
-                    accQ[mm] = aQ;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Y[mm][i] = bts[mm][i] * (to_f32(vin[mm][i]) - aK[i]);
+                for (int j = 0; j < KB; ++j) {
+                    const int ch = row + 32 * j + 4 * gq;
+                    q8[j] = h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]);
+                    k8[j] = h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]);
                 }
-                if (w == 0 && c + 2 < nchunks) sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
+            };
+            load_rows(0, aq[0], ak[0]);
 
-                // U = (I + L)^-1 Diag(beta) X, one tile at a time
-                const int tro = tile_tr_offset(lane);
-                f16x4 Uh[NT], Ul[NT];
-                f32x4 U[NT];
+            // state slab as fp16 operands: k-items = channels 32j + 4gq + i and 32j + 16 + 4gq + i
+            f16x8 Sh[KB];
 #pragma unroll
-                for (int mm = 0; mm < NT; ++mm) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < KB; ++j) Sh[j] = h16::pack8(S[2 * j], S[2 * j + 1]);
+
+            // ---- (Gamma.Q) S, computed transposed (the state slab as A operand,
+            // the scaled queries as B): lane (g, r) then holds output columns
+            // 4g..4g+3 of token r, four consecutive values for one wide store;
+            // and Y = beta (V - (Gamma.K) S) in the state's own layout
+            f32x4 accQ[NT], Y[NT];
 #pragma unroll
-                    for (int n = 0; n < mm; ++n)
-                        acc = h16::mma16(h16::tr4(&st.LT[strict_index(mm, n)][tro]), Uh[n], acc);
-                    f16x4 rh, rl;
-                    h16::split4(Y[mm] - acc, rh, rl);
-                    const f16x4 a = h16::tr4(&st.InvT[mm][tro]);
-                    f32x4 u = h16::mma16(a, rh, f32x4{0.f, 0.f, 0.f, 0.f});
-                    u = h16::mma16(a, rl, u);
-                    U[mm] = u;
-                    h16::split4(u, Uh[mm], Ul[mm]);
+            for (int mm = 0; mm < NT; ++mm) {
+                if (mm + 1 < NT) load_rows(mm + 1, aq[(mm + 1) & 1], ak[(mm + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < KB; ++j) {
+                    aQ = h16::mma32(Sh[j], aq[mm & 1][j], aQ);
+                    aK = h16::mma32(ak[mm & 1][j], Sh[j], aK);
                 }
+                accQ[mm] = aQ;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Y[mm][i] = bts[mm][i] * (to_f32(vin[mm][i]) - aK[i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (w == 0 && c + 2 < nchunks) sm.betas[(c + 2) % 3][lane] = to_f32(bnext);
 
-                // O = (Gamma.Q) S + A_qk U, stored straight from the accumulators
-                OT *ob = o + (((size_t)b * T + (size_t)c * C) * H + h) * dv + col0 + lane_v;
-                const bool full = (c + 1) * C <= T;   // uniform: every row of the chunk is real
+            // ---- A_qk tiles, read while the solve runs
+            f16x4 aqk[NLOWER];
+#pragma unroll
+            for (int i = 0; i < NLOWER; ++i) aqk[i] = h16::tr4(&st.AqkT[i][tro]);
+
+            // ---- U = (I + L)^-1 Diag(beta) X, one tile at a time
+            f16x4 Uh[NT], Ul[NT];
+#pragma unroll
+            for (int mm = 0; mm < NT; ++mm) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int n = 0; n < mm; ++n) acc = h16::mma16(lt[strict_index(mm, n)], Uh[n], acc);
+                f16x4 rh, rl;
+                h16::split4(Y[mm] - acc, rh, rl);
+                f32x4 uu = h16::mma16(inv[mm], rh, f32x4{0.f, 0.f, 0.f, 0.f});
+                uu = h16::mma16(inv[mm], rl, uu);
+                h16::split4(uu, Uh[mm], Ul[mm]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- K-bar^T operands of the first half of the state row tiles, read during the output products
+            const int tk = h16::tr_offset(lane, LDKB);
+            auto load_kb = [&](int kt, f16x8 (&k8)[2]) {
+#pragma unroll
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    const _Float16 *base = &st.Kb[(32 * j2) * LDKB + 16 * kt + tk];
+                    k8[j2] = __builtin_shufflevector(h16::tr4(base), h16::tr4(base + 16 * LDKB), 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+            };
+            f16x8 kb[KT][2];
+#pragma unroll
+            for (int kt = 0; kt < KT / 2; ++kt) load_kb(kt, kb[kt]);
+            // total decay of the chunk for rows 16kt + 4gq + (0..3), four row
+            // tiles per LDS read (one value per lane, shared across the row)
+            static_assert(KT % 4 == 0, "row tiles of the state come in fours");
+            f32x4 gam[KT / 4][4];
+#pragma unroll
+            for (int q4 = 0; q4 < KT / 4; ++q4) row_gather16(st.GamC[16 * (4 * q4 + (r >> 2)) + 4 * gq + (r & 3)], gam[q4]);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- O^T = ((Gamma.Q) S)^T + U^T A_qk^T (U as the A operand, the A_qk
+            // tiles as B): lane (g, r) holds four consecutive columns of token r,
+            // one wide store per row tile
+            if (o) {
+                const auto orr = rsrc(o_head + (size_t)c * C * Hdv);
+                const uint32_t o_lane = (uint32_t)r * o_stride + (uint32_t)(4 * gq) * (uint32_t)sizeof(OT);
 #pragma unroll
                 for (int mm = 0; mm < NT; ++mm) {
                     f32x4 acc = accQ[mm];
 #pragma unroll
                     for (int n = 0; n <= mm; ++n) {
-                        const f16x4 a = h16::tr4(&st.AqkT[lower_index(mm, n)][tro]);
-                        acc = h16::mma16(a, Uh[n], acc);
-                        acc = h16::mma16(a, Ul[n], acc);
+                        acc = h16::mma16(Uh[n], aqk[lower_index(mm, n)], acc);
+                        acc = h16::mma16(Ul[n], aqk[lower_index(mm, n)], acc);
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = c * C + TILE * mm + 4 * gq + i;
-                        if (o && (full || t < T)) ob[(size_t)(TILE * mm + i) * Hdv] = from_f32<OT>(acc[i]);
+                    if (c * C + TILE * mm + r < T) {
+                        if constexpr (OBF)
+                            __builtin_amdgcn_raw_buffer_store_b64(
+                                u32x2{(uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16),
+                                      (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16)},
+                                orr, o_lane, (uint32_t)(TILE * mm) * o_stride, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), orr, o_lane,
+                                                                   (uint32_t)(TILE * mm) * o_stride, 0);
                     }
                 }
+            }
+#pragma unroll
+            for (int kt = KT / 2; kt < KT; ++kt) load_kb(kt, kb[kt]);
+            __builtin_amdgcn_sched_barrier(0);
 
-                // S <- Diag(Gamma_C) S + K-bar^T U; K-bar^T read transposed from its token rows
-                f16x8 Ubh[2], Ubl[2];
-                h16::split8(U[0], U[1], Ubh[0], Ubl[0]);
-                h16::split8(U[2], U[3], Ubh[1], Ubl[1]);
-                const int tk = h16::tr_offset(lane, LDKB);
-                // total decay of the chunk for rows 16kt + 4gq + (0..3), four row
-                // tiles per LDS read (one value per lane, shared across the row)
-                static_assert(KT % 4 == 0, "row tiles of the state come in fours");
-                f32x4 gam[4];
+            // ---- S <- Diag(Gamma_C) S + K-bar^T U, U's two fp16 terms as 8-item B operands
+            // (k-items: the tokens of tiles 2 j2 and 2 j2 + 1)
+            f16x8 Ubh[2], Ubl[2];
 #pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    if (kt % 4 == 0) row_gather16(st.GamC[16 * (kt + (r >> 2)) + 4 * gq + (r & 3)], gam);
-                    f32x4 acc = S[kt] * gam[kt % 4];
+            for (int j2 = 0; j2 < 2; ++j2) {
+                Ubh[j2] = __builtin_shufflevector(Uh[2 * j2], Uh[2 * j2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                Ubl[j2] = __builtin_shufflevector(Ul[2 * j2], Ul[2 * j2 + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            }
 #pragma unroll
-                    for (int j2 = 0; j2 < 2; ++j2) {
-                        const _Float16 *base = &st.Kb[(32 * j2) * LDKB + 16 * kt + tk];
-                        const f16x4 a0 = h16::tr4(base);
-                        const f16x4 a1 = h16::tr4(base + 16 * LDKB);
-                        const f16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc = h16::mma32(a, Ubh[j2], acc);
-                        acc = h16::mma32(a, Ubl[j2], acc);
-                    }
-                    S[kt] = acc;
+            for (int kt = 0; kt < KT; ++kt) {
+                f32x4 acc = S[kt] * gam[kt / 4][kt % 4];
+#pragma unroll
+                for (int j2 = 0; j2 < 2; ++j2) {
+                    acc = h16::mma32(kb[kt][j2], Ubh[j2], acc);
+                    acc = h16::mma32(kb[kt][j2], Ubl[j2], acc);
                 }
-
-                // Next loads go out only now, after this chunk's output stores:
-                // vector-memory loads and stores complete out of order, so a wait
-                // for a load issued before a store is a wait for the store as well.
-                if (c + 1 < nchunks) load_v(c + 1);
-                if (w == 0 && c + 3 < nchunks) bnext = load_beta(c + 3);
+                S[kt] = acc;
+            }
+            if (w == 0 && c + 3 < nchunks) bnext = load_beta(c + 3);
+        };
+        for (int c = -1; c < nchunks; ++c) {
+            if (c >= 0) {
+                chunk_step(c);
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vin[mm][i] = vnx[mm][i];
             }
             lds_barrier();
         }
@@ -763,6 +841,8 @@ hipError_t dispatch(const ChunkFwdArgs &a, hipStream_t s)
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream)
 {
     (void)hipGetLastError();   // report only this launch's own failure
+    // the consumers' buffer offsets inside one chunk (64 rows of H * dv values) stay 32-bit
+    if ((uint64_t)C * a.H * a.dv * 4 + (uint64_t)a.H * a.dv * 4 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
     if (a.dk == 64) return dispatch<64>(a, stream);
     return dispatch<128>(a, stream);
 }
