@@ -230,12 +230,24 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
             for (int blk = 0; blk < KT; ++blk) in.g[blk].load(gb + 16 * blk);
         };
+        // q and k come through buffer loads based at the chunk's first token row
+        // (the launcher keeps a chunk's byte span below 2^31).  A plain load
+        // from these read-only arrays is ordered with nothing else in its basic
+        // block, and the compiler issued the next chunk's after the inverse
+        // below, a whole phase late; a buffer load stays ahead of the LDS
+        // writes that follow it.
         auto load_qk = [&](int c, int r, int gq) {
-            const size_t off = token_row(c, r) * DK + 4 * gq;
+            const size_t row0 = (((size_t)b * T + (size_t)c * C) * H + h) * DK;
+            const auto qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(q + row0), (short)0, (int)0xFFFFFFFF, 0x00020000);
+            const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(k + row0), (short)0, (int)0xFFFFFFFF, 0x00020000);
+            const int t = min(TILE * m + r, T - 1 - c * C);   // as token_row
+            const uint32_t off = (uint32_t)t * (uint32_t)(H * DK * 2) + 8u * (uint32_t)gq;
 #pragma unroll
             for (int blk = 0; blk < KT; ++blk) {
-                in.q[blk].load(q + off + 16 * blk);
-                in.k[blk].load(k + off + 16 * blk);
+                const u32x2 qv = __builtin_amdgcn_raw_buffer_load_b64(qr, off + 32u * blk, 0, 0);
+                const u32x2 kv = __builtin_amdgcn_raw_buffer_load_b64(kr, off + 32u * blk, 0, 0);
+                in.q[blk].a = make_uint2(qv.x, qv.y);
+                in.k[blk].a = make_uint2(kv.x, kv.y);
             }
         };
 
@@ -526,6 +538,9 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     lds_wave_sync();
                 };
                 block_row(TileIndex<M>{});
+                // the machine scheduler may not move the next chunk's q, k loads
+                // (issued in the block row) down past the inverse either
+                __builtin_amdgcn_sched_barrier(0);
                 // ------------------------------------------ (I + L_mm)^-1, lane column r
                 {
                     // column r of L_mm, and X = e_r; `one` is opaque so the 16 selects
@@ -841,8 +856,10 @@ hipError_t dispatch(const ChunkFwdArgs &a, hipStream_t s)
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream)
 {
     (void)hipGetLastError();   // report only this launch's own failure
-    // the consumers' buffer offsets inside one chunk (64 rows of H * dv values) stay 32-bit
+    // buffer offsets inside one chunk (64 rows of H * dv values for V and o, of
+    // H * dk for q and k) stay 32-bit
     if ((uint64_t)C * a.H * a.dv * 4 + (uint64_t)a.H * a.dv * 4 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
+    if ((uint64_t)C * a.H * a.dk * 2 + (uint64_t)a.H * a.dk * 2 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
     if (a.dk == 64) return dispatch<64>(a, stream);
     return dispatch<128>(a, stream);
 }
