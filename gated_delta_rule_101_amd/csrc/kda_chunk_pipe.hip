@@ -106,10 +106,9 @@ struct alignas(16) PipeSmem {
     Stage stage[2];
     // Producer scratch.
     alignas(16) _Float16 Kh[NT - 1][TILE * LDK];   // keys of tiles 0..2 decayed to their tile end
-    // total decay of each tile; rows 64 bytes longer than DK floats so that
-    // the four rows a lane row gathers from (same channel) fall in distinct banks
-    static constexpr int LDD = DK + 16;
-    alignas(16) float D[NT][LDD];
+    // total decay of each tile (read four channels at a time, one address per
+    // lane group)
+    alignas(16) float D[NT][DK];
     // beta of chunks c, c + 1, c + 2 (slot = chunk mod 3): written by a consumer
     // two iterations ahead, read by the producers one iteration ahead.
     alignas(16) float betas[3][C];
@@ -308,19 +307,18 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                     // q and k loads issued after them are outstanding
                     static_assert(2 * KT < 64, "vmcnt field");
                     __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * KT) & 15) | (((2 * KT) >> 4) << 14));
+                    // Tri(s, t) = [s <= t], with the rows of tokens past the end zeroed:
+                    // identity tokens (g = 0) drop out of every sum
                     i16x4 tri;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) tri[i] = (4 * gq + i <= r) ? (short)0x3F80 : (short)0;   // bf16 1.0
+                    for (int i = 0; i < 4; ++i)
+                        tri[i] = (4 * gq + i <= r && cn * C + TILE * M + 4 * gq + i < len) ? (short)0x3F80 : (short)0;   // bf16 1.0
                     const int tro = h16::tr_offset(lane, DK);
                     const _Float16 *gsrc = reinterpret_cast<const _Float16 *>(&sm.gnext[M - 1][0]);
 #pragma unroll
                     for (int blk = 0; blk < KT; ++blk) {
-                        // channels as rows, tokens 4 gq + i as k-items; tokens past the
-                        // end are identity tokens (g = 0)
-                        i16x4 gt = __builtin_bit_cast(i16x4, h16::tr4(gsrc + 16 * blk + tro));
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (cn * C + TILE * M + 4 * gq + i >= len) gt[i] = 0;
+                        // channels as rows, tokens 4 gq + i as k-items
+                        const i16x4 gt = __builtin_bit_cast(i16x4, h16::tr4(gsrc + 16 * blk + tro));
                         const f32x4 bsum = BF::mma16(gt, tri, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
                         for (int i = 0; i < 4; ++i) f[blk][i] = fast_exp2(bsum[i] * LOG2E);
@@ -446,10 +444,11 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         for (int hh = 0; hh < 2; ++hh) {
                             const int blk = 2 * p + hh;
                             const int ch = 16 * blk + 4 * gq;
-                            // the four tiles' totals of these 4 channels: one LDS
-                            // read per lane, shared across the lane's row
+                            // the four tiles' totals of these 4 channels (each read is
+                            // one address per lane group, broadcast to its 16 lanes)
                             f32x4 Dt[NT];
-                            row_gather16(sm.D[r >> 2][ch + (r & 3)], Dt);
+#pragma unroll
+                            for (int t = 0; t < NT; ++t) Dt[t] = *reinterpret_cast<const f32x4 *>(&sm.D[t][ch]);
                             // whole-tile decay before tile M, from its start to the chunk
                             // end, and across the tiles strictly between M and M - 2, M - 3
                             f32x4 before = {1.f, 1.f, 1.f, 1.f}, dma = Dt[M], w2 = before, w3 = before;

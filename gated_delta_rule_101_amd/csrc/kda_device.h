@@ -148,7 +148,10 @@ template <> struct Prec<true> {
     // together): hi = RNE(x); the residual x - hi is exact in float32.
     static constexpr bool SPLIT = true;
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    // The residual is never fused with the product that made x (contraction off):
+    // the split then does not depend on where the compiler inlines it.
     static __device__ __forceinline__ void split2(float a, float b, bf16x2 &hi, bf16x2 &lo) {
+#pragma clang fp contract(off)
         hi = bf16x2{(__bf16)a, (__bf16)b};
         const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
         const float ra = a - __uint_as_float(hb << 16);
