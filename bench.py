@@ -273,8 +273,9 @@ def bench_peaks(reps=10):
     return {"hbm_copy": {"GB/s": round(copy_gbs, 1), "frac_of_published": round(copy_gbs / HBM_PEAK_GBS, 4),
                          "by_kernel_GB/s": {"probe_copy": round(probe_gbs, 1), "torch_copy": round(runtime_gbs, 1),
                                             "probe_in_place": round(update_gbs, 1)},
-                         "sample": f"1 GiB moved each way: a copy (the probe kernel, torch's copy_) and an "
-                                   f"in-place read-modify-write; the fastest, read + write bytes, best of {reps}"},
+                         "sample": f"1 GiB moved each way: a streaming copy (the probe kernel: 16 KB per "
+                                   f"workgroup, non-temporal loads and stores), torch's copy_, and the same probe "
+                                   f"read-modify-writing in place; the fastest, read + write bytes, best of {reps}"},
             "mfma_bf16": {"TFLOP/s": round(tfs, 1), "frac_of_published": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4),
                           "by_shape_TFLOP/s": {k: round(v, 1) for k, v in rates.items()},
                           "sample": f"{blocks} workgroups x 4 waves x {iters} rounds of independent bf16 products "

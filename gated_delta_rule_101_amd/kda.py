@@ -162,9 +162,10 @@ def _workspace(lib, workspace, B, T, H, dk, dv, device):
 def _ring_pays(q: torch.Tensor, B: int, H: int, dk: int, dv: int) -> bool:
     """Whether the workspace (ring) kernel is the faster choice for this call:
     its workgroups share each head's state-independent chunk work, which pays
-    while the grid (B H dv/64 workgroups) fills at most half the device
+    for dv of 256 and more while the grid (B H dv/64 workgroups) fills at most
+    half the device; at dv = 128 the two kernels measure the same
     (include/kda.h states the measured ratios)."""
-    if q.dtype != torch.bfloat16 or dk != 128 or dv < 128 or dv % 64 or dv > 512 or not q.is_cuda:
+    if q.dtype != torch.bfloat16 or dk != 128 or dv < 256 or dv % 64 or dv > 512 or not q.is_cuda:
         return False
     cus = torch.cuda.get_device_properties(q.device).multi_processor_count
     return 2 * B * H * (dv // 64) <= cus

@@ -1,5 +1,5 @@
 // Achievable-peak probes for the benchmark (not part of the KDA library):
-// a streaming device copy (the HBM bandwidth a plain kernel reaches) and a
+// streaming device copies (the HBM bandwidth a plain kernel reaches) and a
 // loop of independent bf16 16x16x32 matrix-core products (the MFMA issue rate
 // a plain kernel reaches).  Built into libkda_probe.so; bench.py calls them
 // through ctypes and reports the KDA kernels' fractions against both these
@@ -15,39 +15,37 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// dst[i] = src[i] over n 16-byte units (n a multiple of 4), grid-stride;
-// each thread keeps four loads in flight, each instruction covering
-// consecutive units across the wave.
-__global__ void __launch_bounds__(256) probe_copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
-                                                         size_t n)
+// Streaming kernels: workgroup w moves the 1024 consecutive 16-byte units
+// starting at unit 1024 w (16 KB), each thread four units 256 apart (every
+// instruction covers 4 KB of consecutive bytes across the workgroup), with
+// non-temporal loads and stores.  Of the forms tried on MI355X (spans of 16
+// KB to 1 MB per workgroup, 4 or 8 units in flight, 256 or 512 threads,
+// cached or non-temporal), this one moved the most bytes per second.
+constexpr int SPAN = 1024;   // units per workgroup
+constexpr int UNITS = 4;     // units per thread
+
+// dst[i] = src[i]
+__global__ void __launch_bounds__(256) probe_copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst)
 {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += 4 * stride) {
-        u32x4 x[4];
+    const size_t base = (size_t)blockIdx.x * SPAN + threadIdx.x;
+    u32x4 x[UNITS];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * stride < n) x[u] = src[i + u * stride];
+    for (int u = 0; u < UNITS; ++u) x[u] = __builtin_nontemporal_load(&src[base + 256 * u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * stride < n) dst[i + u * stride] = x[u];
-    }
+    for (int u = 0; u < UNITS; ++u) __builtin_nontemporal_store(x[u], &dst[base + 256 * u]);
 }
 
-// buf[i] ^= mask over n 16-byte units in place (read and write the same
-// lines, as a state update does), four units in flight per thread.
-__global__ void __launch_bounds__(256) probe_update_kernel(u32x4 *__restrict__ buf, size_t n, uint32_t mask)
+// buf[i] ^= mask in place (read and write the same lines, as a state update does)
+__global__ void __launch_bounds__(256) probe_update_kernel(u32x4 *__restrict__ buf, uint32_t mask)
 {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += 4 * stride) {
-        u32x4 x[4];
+    const size_t base = (size_t)blockIdx.x * SPAN + threadIdx.x;
+    u32x4 x[UNITS];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * stride < n) x[u] = buf[i + u * stride];
+    for (int u = 0; u < UNITS; ++u) x[u] = __builtin_nontemporal_load(&buf[base + 256 * u]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (i + u * stride < n) buf[i + u * stride] = x[u] ^ mask;
-    }
+    for (int u = 0; u < UNITS; ++u) __builtin_nontemporal_store(x[u] ^ mask, &buf[base + 256 * u]);
 }
+static_assert(SPAN == UNITS * 256, "one pass per workgroup");
 
 // Each wave runs `iters` rounds of NACC independent bf16 matrix-core products
 // (16x16x32: 2 * 16 * 16 * 32 FLOP each; 32x32x16: 2 * 32 * 32 * 16) and
@@ -84,21 +82,24 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(float *__restrict__ out
 
 extern "C" {
 
-// Copy `bytes` (a multiple of 64; both pointers 16-byte aligned) on `stream`.
+// Copy `bytes` (a multiple of 16384, at most 2^44; both pointers 16-byte
+// aligned) on `stream`.
 int kda_probe_copy(const void *src, void *dst, size_t bytes, void *stream)
 {
-    if (!src || !dst || bytes % 64 || ((uintptr_t)src | (uintptr_t)dst) & 15) return 1;
-    hipLaunchKernelGGL(probe_copy_kernel, dim3(16384), dim3(256), 0, (hipStream_t)stream,
-                       (const u32x4 *)src, (u32x4 *)dst, bytes / 16);
+    const size_t span = (size_t)SPAN * 16;
+    if (!src || !dst || bytes == 0 || bytes % span || bytes / span > 0x7FFFFFFFu || ((uintptr_t)src | (uintptr_t)dst) & 15) return 1;
+    hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)(bytes / span)), dim3(256), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, (u32x4 *)dst);
     return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 
-// buf ^= mask in place over `bytes` (a multiple of 64, 16-byte aligned).
+// buf ^= mask in place over `bytes` (as for the copy).
 int kda_probe_update(void *buf, size_t bytes, unsigned mask, void *stream)
 {
-    if (!buf || bytes % 64 || (uintptr_t)buf & 15) return 1;
-    hipLaunchKernelGGL(probe_update_kernel, dim3(16384), dim3(256), 0, (hipStream_t)stream, (u32x4 *)buf,
-                       bytes / 16, (uint32_t)mask);
+    const size_t span = (size_t)SPAN * 16;
+    if (!buf || bytes == 0 || bytes % span || bytes / span > 0x7FFFFFFFu || (uintptr_t)buf & 15) return 1;
+    hipLaunchKernelGGL(probe_update_kernel, dim3((unsigned)(bytes / span)), dim3(256), 0, (hipStream_t)stream,
+                       (u32x4 *)buf, (uint32_t)mask);
     return hipGetLastError() == hipSuccess ? 0 : 3;
 }
 

@@ -185,10 +185,11 @@ kda_status_t kda_chunk_fwd_gate(const void *q, const void *k, const void *v,
  * diagonal inverses), so each chunk's part is computed once per head instead
  * of once per workgroup, and hand it to one another through a four-slot ring
  * per head held in the workspace.  Other inputs run the kernels of
- * kda_chunk_fwd.  The ring pays when the grid (B H dv / 64 workgroups) fills
- * at most half the device, and more the larger dv is (about 0.88x the time
- * of kda_chunk_fwd at dv = 128, 0.75x at dv = 256, 0.66x at dv = 512, T =
- * 4096); a full-device grid at dv = 128 runs faster without it (1.1x).
+ * kda_chunk_fwd.  The ring pays for dv of 256 and more when the grid (B H dv
+ * / 64 workgroups) fills at most half the device (at B = 1, H = 8, T = 4096:
+ * 1.0x the time of kda_chunk_fwd at dv = 128, 0.84x at dv = 256, 0.79x at
+ * dv = 512); a full-device grid runs faster without it (1.28x at B = 1, H =
+ * 96, T = 131072, dv = 128).
  *
  *   workspace        device memory of at least kda_chunk_fwd_workspace_bytes(B,
  *                    T, H, dk, dv) bytes, 16-byte aligned, owned by the caller;
