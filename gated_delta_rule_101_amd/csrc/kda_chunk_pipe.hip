@@ -235,20 +235,22 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         // block, and the compiler issued the next chunk's after the inverse
         // below, a whole phase late; a buffer load stays ahead of the LDS
         // writes that follow it.
-        auto load_qk = [&](int c, int r, int gq) {
+        // channel blocks blk0 .. blk1 - 1 of this lane's row
+        auto load_qk_blocks = [&](int c, int r, int gq, int blk0, int blk1) {
             const size_t row0 = (((size_t)b * T + (size_t)c * C) * H + h) * DK;
             const auto qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(q + row0), (short)0, (int)0xFFFFFFFF, 0x00020000);
             const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(k + row0), (short)0, (int)0xFFFFFFFF, 0x00020000);
             const int t = min(TILE * m + r, T - 1 - c * C);   // as token_row
             const uint32_t off = (uint32_t)t * (uint32_t)(H * DK * 2) + 8u * (uint32_t)gq;
 #pragma unroll
-            for (int blk = 0; blk < KT; ++blk) {
+            for (int blk = blk0; blk < blk1; ++blk) {
                 const u32x2 qv = __builtin_amdgcn_raw_buffer_load_b64(qr, off + 32u * blk, 0, 0);
                 const u32x2 kv = __builtin_amdgcn_raw_buffer_load_b64(kr, off + 32u * blk, 0, 0);
                 in.q[blk].a = make_uint2(qv.x, qv.y);
                 in.k[blk].a = make_uint2(kv.x, kv.y);
             }
         };
+        auto load_qk = [&](int c, int r, int gq) { load_qk_blocks(c, r, gq, 0, KT); };
 
         if (threadIdx.x == 0) {
             sm.arrivals = 0;
@@ -507,10 +509,10 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             gq_o[2] = h16::mma32(h16::pack8(a), bk, gq_o[2]);
                             gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
                         }
+                        // this block pair's q and k are consumed: fetch the next chunk's
+                        load_qk_blocks(cnext, r, gq, 2 * p, 2 * p + 2);
                     }
 
-                    // q and k of chunk cn are consumed: fetch the next chunk's
-                    load_qk(cnext, r, gq);
                     lds_wave_sync();
 
                     // ------------------------------------------ Gram results of block row M
