@@ -121,6 +121,7 @@ struct alignas(16) PipeSmem {
     // staging pass (tile 0's producer, the lightest, keeps them in registers)
     alignas(16) uint16_t gnext[NT - 1][TILE * DK];
     unsigned arrivals;                          // producer meeting counter
+    unsigned inv_posted;                        // diagonal inverses stored so far (all producers)
     unsigned failed;                            // some producer wait expired (read after the loop)
 };
 
@@ -254,6 +255,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 
         if (threadIdx.x == 0) {
             sm.arrivals = 0;
+            sm.inv_posted = 0;
             sm.failed = 0;
         }
         if (nchunks == 0) {
@@ -289,7 +291,43 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         if constexpr (GLDS) dma_g(0, M);
         else load_g(0, r, gq);
         load_qk(0, r, gq);   // after the gates: the loop top's count relies on the order
+        // this tile's L block starts as zero (the first, unused inverse is then I)
+        for (int i = lane; i < TILE * (TILE + 4); i += 64) (&sm.LdT[M][0][0])[i] = 0.f;
         lds_barrier();
+        // (I + L_mm)^-1 of chunk c, lane column r, stored transposed into the
+        // chunk's stage and counted in inv_posted.  It runs at the top of the
+        // next iteration (the L block stays in LdT until that iteration's block
+        // row), beside the next chunk's cumsum rather than after this chunk's
+        // block row; the consumers wait for the count before their solve.  At c
+        // = -1 it inverts the zeroed LdT into stage 1, which chunk 1 rewrites
+        // before any consumer reads it.
+        auto invert_chunk = [&](int c) __attribute__((always_inline)) {
+            int r = lane & 15, gq = lane >> 4;
+            asm volatile("" : "+v"(r), "+v"(gq));
+            // column r of L_mm, and X = e_r; `one` is opaque so the 16 selects
+            // are not hoisted out of the chunk loop
+            float Lc[TILE];
+#pragma unroll
+            for (int i4 = 0; i4 < TILE / 4; ++i4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.LdT[M][r][4 * i4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
+            }
+            float one = 1.f;
+            asm volatile("" : "+v"(one));
+            float X[TILE];
+#pragma unroll
+            for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
+            unit_lower_inverse_steps<0>(X, Lc);
+            // lane group gq stores rows 4gq..4gq+3 of column r (row r of the transpose)
+            f32x4 part;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
+            *reinterpret_cast<f16x4 *>(&sm.stage[c & 1].InvT[M][tile_at(r, gq)]) = h16::pack4(part);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            if (lane == 0) __hip_atomic_fetch_add(&sm.inv_posted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        };
         for (int cn = 0; cn < nchunks; ++cn) {
             {
                 Stage &st = sm.stage[cn & 1];
@@ -363,6 +401,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         }
                     }
                 }
+                invert_chunk(cn - 1);
                 if (r == TILE - 1) {
 #pragma unroll
                     for (int blk = 0; blk < KT; ++blk)
@@ -542,33 +581,10 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 // the machine scheduler may not move the next chunk's q, k loads
                 // (issued in the block row) down past the inverse either
                 __builtin_amdgcn_sched_barrier(0);
-                // ------------------------------------------ (I + L_mm)^-1, lane column r
-                {
-                    // column r of L_mm, and X = e_r; `one` is opaque so the 16 selects
-                    // are not hoisted out of the chunk loop
-                    float Lc[TILE];
-#pragma unroll
-                    for (int i4 = 0; i4 < TILE / 4; ++i4) {
-                        const f32x4 x = *reinterpret_cast<const f32x4 *>(&sm.LdT[m][r][4 * i4]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) Lc[4 * i4 + i] = x[i];
-                    }
-                    float one = 1.f;
-                    asm volatile("" : "+v"(one));
-                    float X[TILE];
-#pragma unroll
-                    for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
-                    unit_lower_inverse_steps<0>(X, Lc);
-                    // lane group gq stores rows 4gq..4gq+3 of column r (row r of the transpose)
-                    f32x4 part;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
-                    *reinterpret_cast<f16x4 *>(&st.InvT[m][tile_at(r, gq)]) = h16::pack4(part);
-                }
             }
             lds_barrier();
         }
+        invert_chunk(nchunks - 1);
         };
         static_assert(NT == 4, "one loop instance per tile");
         switch (m) {
@@ -656,11 +672,9 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             const int tro = tile_tr_offset(lane);
 
             // ---- operands that do not depend on the state
-            f16x4 lt[NSTRICT], inv[NT];
+            f16x4 lt[NSTRICT];
 #pragma unroll
             for (int i = 0; i < NSTRICT; ++i) lt[i] = h16::tr4(&st.LT[i][tro]);
-#pragma unroll
-            for (int mm = 0; mm < NT; ++mm) inv[mm] = h16::tr4(&st.InvT[mm][tro]);
             f32x4 bts[NT];
             row_gather16(sm.betas[c % 3][TILE * (r >> 2) + 4 * gq + (r & 3)], bts);
             // scaled queries and keys of row tile mm: k-items channels 32j + 4gq + i and 32j + 16 + 4gq + i
@@ -708,6 +722,24 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
             for (int i = 0; i < NLOWER; ++i) aqk[i] = h16::tr4(&st.AqkT[i][tro]);
 
+            // ---- the diagonal inverses of this chunk: the producers store them at
+            // the start of this period (four per chunk, counted from the first
+            // period on); a bounded wait, failing loudly like theirs
+            {
+                bool ok = false;
+                const unsigned want = 4u * (unsigned)(c + 2);
+                for (unsigned it = 0; it <= spin_limit; ++it) {
+                    const unsigned seen = __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(&sm.inv_posted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+                    if (seen >= want) { ok = true; break; }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+                if (!ok && lane == 0) sm.failed = 1u;
+            }
+            f16x4 inv[NT];
+#pragma unroll
+            for (int mm = 0; mm < NT; ++mm) inv[mm] = h16::tr4(&st.InvT[mm][tro]);
             // ---- U = (I + L)^-1 Diag(beta) X, one tile at a time
             f16x4 Uh[NT], Ul[NT];
 #pragma unroll
