@@ -31,13 +31,15 @@
 //           pairs f-scaled rows with 1/f-scaled keys in two-term bfloat16
 //           (the 1/f keys exceed fp16 range); a tile n = m - d pairs the
 //           f-scaled rows times the whole tiles strictly between (D_{m-1},
-//           D_{m-1} D_{m-2}) with K-hat_n, in fp16.  Finally (I + L_mm)^-1 by
-//           column-oriented forward substitution in fp32.
+//           D_{m-1} D_{m-2}) with K-hat_n, in fp16.
+//   inverse (I + L_mm)^-1 by column-oriented forward substitution in fp32,
+//           done at the top of the next chunk's iteration, beside its cumsum,
+//           and counted for the consumers.
 // Consumer wave 4 + w, value columns 16w..16w+15 of the slab, state slab
 // S (dk x 16, fp32) in registers:
 //   X = V - (Gamma.K) S,  U = (I + L)^-1 Diag(beta) X (blocked forward
-//   substitution over the four tiles), O = (Gamma.Q) S + A_qk U,
-//   S <- Diag(Gamma_C) S + K-bar^T U.
+//   substitution over the four tiles, once the chunk's four inverses are
+//   counted), O = (Gamma.Q) S + A_qk U, S <- Diag(Gamma_C) S + K-bar^T U.
 //
 // Operand precision: fp16 single operands for (Gamma.Q) S, (Gamma.K) S, the
 // off-diagonal Gram tiles and L U; fp16 two-term U (and right-hand sides of
