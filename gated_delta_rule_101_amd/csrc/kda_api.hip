@@ -283,6 +283,49 @@ kda_status_t kda_chunk_fwd_gate_ws(const void *q, const void *k, const void *v, 
                     qkv_dtype, gate_dtype, out_dtype, stream);
 }
 
+size_t kda_chunk_fwd_seqpar_workspace_bytes(int B, int T, int H, int dk, int dv, int segments)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || segments < 1 || segments > KDA_SEQPAR_MAX_SEGMENTS || T % segments) return 0;
+    if ((dk != 64 && dk != 128) || dv % 64 || dv <= 0 || dv > 512) return 0;
+    return kda::chunk_seqpar_workspace_bytes(B, H, dk, dv, segments);
+}
+
+kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, const float *S0, void *o, float *S_final,
+                                  void *workspace, size_t workspace_bytes,
+                                  int B, int T, int H, int dk, int dv, int segments,
+                                  kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                  void *stream)
+{
+    const kda_status_t st = check_chunk(q, k, v, g, beta, S0, o, S_final, nullptr, nullptr, B, T, H, dk, dv,
+                                        qkv_dtype, gate_dtype, out_dtype, true, true);
+    if (st != KDA_OK) return st;
+    if (segments < 1 || segments > KDA_SEQPAR_MAX_SEGMENTS || (T > 0 && T % segments)) return KDA_ERR_INVALID_ARG;
+    if (qkv_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)B * segments * H * (dv / 64 + dk / 64) >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0) return KDA_OK;
+    kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S0, o, S_final, B, T, H, dk, dv,
+                                     qkv_dtype, gate_dtype, out_dtype);
+    if (T == 0) return run_chunk(a, stream);
+    const size_t need = kda::chunk_seqpar_workspace_bytes(B, H, dk, dv, segments);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
+    {
+        const size_t tok = (size_t)B * T * H;
+        const size_t sq = dsize(qkv_dtype), sg = dsize(gate_dtype), so = dsize(out_dtype);
+        const size_t state_bytes = (size_t)B * H * dk * dv * sizeof(float);
+        const Span sp_w = span(workspace, workspace_bytes);
+        const Span others[] = {span(q, tok * dk * sq), span(k, tok * dk * sq), span(v, tok * dv * sq),
+                               span(g, tok * dk * sg), span(beta, tok * sg), span(o, tok * dv * so),
+                               span(S0, S0 ? state_bytes : 0), span(S_final, S_final ? state_bytes : 0)};
+        for (const Span &x : others)
+            if (overlap(sp_w, x)) return KDA_ERR_INVALID_ARG;
+    }
+    // the final state is written by the combine step, which reads S0 first:
+    // S_final may alias S0 as in kda_chunk_fwd
+    return kda::launch_chunk_fwd_seqpar(a, segments, workspace, (hipStream_t)stream) == hipSuccess ? KDA_OK
+                                                                                          : KDA_ERR_LAUNCH;
+}
+
 unsigned kda_debug_set_spin_limit(unsigned limit) { return kda::set_spin_limit(limit); }
 
 kda_status_t kda_verify_step(const void *q, const void *k, const void *v, const void *g,

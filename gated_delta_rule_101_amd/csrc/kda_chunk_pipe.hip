@@ -163,14 +163,19 @@ __device__ __forceinline__ bool producer_meet(unsigned *arrivals, unsigned targe
     return ok;
 }
 
-template <int DK, bool GBF, bool OBF, bool GL>
+// TR: slabs from nslab_v on are transition slabs.  Their dk "value" columns
+// start from the identity with zero values and end as the columns of the
+// chunk sequence's linear map on the state, M with S_out = M S_in + N (N the
+// value slabs' final state from a zero start), written to M_out [b h][dk][dk];
+// they write no output.
+template <int DK, bool GBF, bool OBF, bool GL, bool TR = false>
 __global__ void __launch_bounds__(NTHREADS, 1)
 kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                       const uint16_t *__restrict__ v, const typename Store<GBF>::type *__restrict__ g,
                       const typename Store<GBF>::type *__restrict__ beta, const float *S0,
                       typename Store<OBF>::type *__restrict__ o, float *S_final,
                       const int *__restrict__ lengths, const float *__restrict__ A_log,
-                      int B, int T, int H, int dv, int nslab, unsigned spin_limit)
+                      int B, int T, int H, int dv, int nslab, int nslab_v, float *M_out, unsigned spin_limit)
 {
     typedef typename Store<GBF>::type GT;
     typedef typename Store<OBF>::type OT;
@@ -599,8 +604,11 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         lds_barrier();   // the consumers' last chunk
     } else {
         const int w = wave - NPROD;                 // column group
-        const int col0 = slab * WV + 16 * w;        // first value column of this consumer
-        const size_t s_base = (size_t)bh * DK * dv + col0 + r;
+        const bool trans = TR && slab >= nslab_v;   // a transition slab (uniform)
+        const int col0 = (trans ? slab - nslab_v : slab) * WV + 16 * w;   // first column of this consumer
+        const int lds = trans ? DK : dv;            // row stride of this slab's state matrix
+        float *const S_out = trans ? M_out : S_final;
+        const size_t s_base = (size_t)bh * DK * lds + col0 + r;
         const size_t Hdv = (size_t)H * dv;
         const uint32_t lane_v = (uint32_t)(4 * gq * H * dv + r);   // rows 4gq + i, column r
 
@@ -613,7 +621,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         // voffset, so no vector instruction computes an address (the launcher
         // keeps these offsets below 2^31).
         const uint16_t *v_head = v + ((size_t)b * T * H + h) * dv + col0;
-        OT *o_head = o ? o + ((size_t)b * T * H + h) * dv + col0 : nullptr;
+        OT *o_head = (o && !trans) ? o + ((size_t)b * T * H + h) * dv + col0 : nullptr;
         const uint32_t v_stride = (uint32_t)Hdv * 2u, o_stride = (uint32_t)Hdv * (uint32_t)sizeof(OT);
         auto rsrc = [](const void *base) {
             return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
@@ -621,6 +629,13 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         // V of chunk c.  A token past the end reads the last token instead (its
         // beta is zero, so its value never enters U).
         auto load_v = [&](int c, uint16_t (&dst)[NT][4]) {
+            if (trans) {   // zero values
+#pragma unroll
+                for (int mm = 0; mm < NT; ++mm)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[mm][i] = 0;
+                return;
+            }
             const auto vr = rsrc(v_head + (size_t)c * C * Hdv);
             if ((c + 1) * C <= T) {
 #pragma unroll
@@ -655,7 +670,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                S[kt][i] = S0 ? S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
+                S[kt][i] = trans ? (16 * kt + 4 * gq + i == col0 + r ? 1.f : 0.f)
+                                 : S0 ? S0[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] : 0.f;
         if (nchunks > 0) load_v(0, vin);
         lds_barrier();
 
@@ -780,7 +796,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             // ---- O^T = ((Gamma.Q) S)^T + U^T A_qk^T (U as the A operand, the A_qk
             // tiles as B): lane (g, r) holds four consecutive columns of token r,
             // one wide store per row tile
-            if (o) {
+            if (o_head) {
                 const auto orr = rsrc(o_head + (size_t)c * C * Hdv);
                 const uint32_t o_lane = (uint32_t)r * o_stride + (uint32_t)(4 * gq) * (uint32_t)sizeof(OT);
 #pragma unroll
@@ -844,18 +860,18 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             const float nan = __builtin_nanf("");
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) S[kt] = f32x4{nan, nan, nan, nan};
-            if (o)
+            if (o_head)
                 for (int t = 4 * gq; t < T; t += 16)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (t + i < T) o[(((size_t)b * T + t + i) * H + h) * dv + col0 + r] = from_f32<OT>(nan);
         }
-        if (S_final) {
+        if (S_out) {
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    S_final[s_base + (size_t)(16 * kt + 4 * gq + i) * dv] = S[kt][i];
+                    S_out[s_base + (size_t)(16 * kt + 4 * gq + i) * lds] = S[kt][i];
         }
     }
 }
@@ -869,7 +885,24 @@ hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
     const unsigned grid = (unsigned)(a.B * a.H * nslab);
     kda_chunk_pipe_kernel<DK, GBF, OBF, GL><<<grid, NTHREADS, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const GT *)a.g,
-        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.lengths, a.A_log, a.B, a.T, a.H, a.dv, nslab, spin_limit());
+        (const GT *)a.beta, a.S0, (OT *)a.o, a.S_final, a.lengths, a.A_log, a.B, a.T, a.H, a.dv, nslab, nslab,
+        nullptr, spin_limit());
+    return hipGetLastError();
+}
+
+// The value slabs' final states from a zero start (a.S_final) and the chunk
+// sequence's linear map (M_out), no outputs; bf16 gates or fp32 gates, no
+// logits, no per-sequence lengths.
+template <int DK, bool GBF>
+hipError_t launch_trans(const ChunkFwdArgs &a, float *M_out, hipStream_t stream)
+{
+    typedef typename Store<GBF>::type GT;
+    const int nslab_v = a.dv / WV, nslab = nslab_v + DK / WV;
+    const unsigned grid = (unsigned)(a.B * a.H * nslab);
+    kda_chunk_pipe_kernel<DK, GBF, false, false, true><<<grid, NTHREADS, 0, stream>>>(
+        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const GT *)a.g,
+        (const GT *)a.beta, nullptr, nullptr, a.S_final, nullptr, nullptr, a.B, a.T, a.H, a.dv, nslab, nslab_v,
+        M_out, spin_limit());
     return hipGetLastError();
 }
 
@@ -887,6 +920,16 @@ hipError_t dispatch(const ChunkFwdArgs &a, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_chunk_fwd_bf16_trans(const ChunkFwdArgs &a, float *M_out, hipStream_t stream)
+{
+    (void)hipGetLastError();
+    if ((uint64_t)C * a.H * a.dv * 4 + (uint64_t)a.H * a.dv * 4 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
+    if ((uint64_t)C * a.H * a.dk * 2 + (uint64_t)a.H * a.dk * 2 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
+    if (a.lengths || a.A_log || !M_out) return hipErrorInvalidValue;
+    if (a.dk == 64) return a.gate_bf16 ? launch_trans<64, true>(a, M_out, stream) : launch_trans<64, false>(a, M_out, stream);
+    return a.gate_bf16 ? launch_trans<128, true>(a, M_out, stream) : launch_trans<128, false>(a, M_out, stream);
+}
 
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream)
 {

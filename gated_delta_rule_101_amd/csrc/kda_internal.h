@@ -93,6 +93,15 @@ hipError_t noalloc_scratch(hipStream_t stream, void **out);
 unsigned set_spin_limit(unsigned limit);
 unsigned spin_limit();
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream);   // bfloat16 q, k, v
+// bfloat16 q, k, v, no per-sequence lengths, no logits: a.S_final <- the value
+// slabs' final states from a zero start (N), M_out [B H][dk][dk] <- the chunk
+// sequence's linear map on the state (S_out = M S_in + N); no outputs.
+hipError_t launch_chunk_fwd_bf16_trans(const ChunkFwdArgs &a, float *M_out, hipStream_t stream);
+// The forward as P segments of T / P tokens run side by side and joined
+// through their linear maps (bfloat16 q, k, v, T a multiple of P, no lengths,
+// no logits); the workspace holds N, M and the segments' starting states.
+size_t chunk_seqpar_workspace_bytes(int B, int H, int dk, int dv, int P);
+hipError_t launch_chunk_fwd_seqpar(const ChunkFwdArgs &a, int P, void *workspace, hipStream_t stream);
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_spec_step(const SpecArgs &a, hipStream_t stream);           // dk, dv in {64, 128}
 hipError_t launch_verify_tile(const SpecArgs &a, hipStream_t stream);         // K <= 16: verify, or commit if accepted is set

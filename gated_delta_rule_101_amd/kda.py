@@ -31,7 +31,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_SCRATC
 
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_chunk_fwd_ws", "kda_chunk_fwd_gate_ws",
-           "kda_chunk_fwd_noalloc",
+           "kda_chunk_fwd_noalloc", "kda_chunk_fwd_seqpar", "kda_chunk_fwd_seqpar_workspace_bytes",
            "kda_chunk_fwd_workspace_bytes", "kda_debug_set_spin_limit", "kda_verify_step", "kda_commit_step",
            "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_status_string", "kda_abi_version")
@@ -70,6 +70,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_gate_ws.restype = i
     lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 5
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_seqpar.argtypes = [vp] * 9 + [sz] + [i] * 9 + [vp]
+    lib.kda_chunk_fwd_seqpar.restype = i
+    lib.kda_chunk_fwd_seqpar_workspace_bytes.argtypes = [i] * 6
+    lib.kda_chunk_fwd_seqpar_workspace_bytes.restype = sz
     lib.kda_debug_set_spin_limit.argtypes = [ctypes.c_uint]
     lib.kda_debug_set_spin_limit.restype = ctypes.c_uint
     lib.kda_decode_step_gate.argtypes = [vp] * 8 + [i] * 7 + [vp]
@@ -225,6 +229,49 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                                _ptr(S_final), B, T, H, dk, dv, _dtype_code(q), _dtype_code(g),
                                _dtype_code(o), _stream_handle(stream, dev))
         _raise(st, "kda_chunk_fwd")
+    return o, S_final
+
+
+def kda_chunk_fwd_seqpar_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, segments: int) -> int:
+    """Device bytes kda_chunk_fwd_seqpar needs (0: the shape or segment count is invalid)."""
+    return int(load_library().kda_chunk_fwd_seqpar_workspace_bytes(B, T, H, dk, dv, segments))
+
+
+def kda_chunk_fwd_seqpar(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                         beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *, segments: int,
+                         output_final_state: bool = True, o: Optional[torch.Tensor] = None,
+                         S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         stream: Optional[torch.cuda.Stream] = None
+                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_seqpar: the forward as `segments` pieces of the sequence run
+    side by side and joined through their linear maps on the state (bfloat16
+    q, k, v; `segments` divides T).  Shapes, dtypes and results as
+    kda_chunk_fwd; `workspace` (device bytes) is allocated here when not given."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch between q, k, v, g, beta")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != g.dtype:
+        raise TypeError("q, k, v share one dtype; g and beta share one dtype")
+    if S0 is not None and (S0.shape != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("S0 must be float32 [B,H,dk,dv]")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, T, H, dv):
+        raise ValueError("o must be [B,T,H,dv]")
+    if S_final is None and output_final_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None and T > 0:
+        need = int(lib.kda_chunk_fwd_seqpar_workspace_bytes(B, T, H, dk, dv, int(segments)))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dev = _check_dev(q, k, v, g, beta, S0, o, S_final, workspace)
+    st = lib.kda_chunk_fwd_seqpar(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0), _ptr(o),
+                                  _ptr(S_final), _ptr(workspace), _nbytes(workspace), B, T, H, dk, dv,
+                                  int(segments), _dtype_code(q), _dtype_code(g), _dtype_code(o),
+                                  _stream_handle(stream, dev))
+    _raise(st, "kda_chunk_fwd_seqpar")
     return o, S_final
 
 

@@ -249,6 +249,44 @@ kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                                    kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_chunk_fwd_seqpar -- kda_chunk_fwd computed as `segments` pieces of the
+ * sequence side by side, for grids too small to fill the device (few
+ * sequences and heads, long T).  Between chunks the chunkwise form is a
+ * sequential recurrence ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the
+ * chunkwise diagram), but each chunk's step is affine in the state, so a run
+ * of chunks is too: S_out = M S_in + N.  The call runs every segment of
+ * T / segments tokens from a zero state, also carrying dk transition columns
+ * that start from the identity with zero values (giving N and M per segment),
+ * forms the segments' true starting states in order (S_{p+1} = M_p S_p + N_p
+ * in float32; the last one is S_final), and runs every segment again from its
+ * starting state to write o.  The sequential part is T / segments tokens long
+ * twice instead of T once, at (dv + dk) / dv times the first pass's columns.
+ * Results equal kda_chunk_fwd's up to rounding (the chunks start at every
+ * segment start, and the segments meet through the float32 products).
+ *
+ *   segments   1 .. KDA_SEQPAR_MAX_SEGMENTS, dividing T; it pays while
+ *              B * segments * H * (dv + dk) / 64 workgroups fit the device.
+ *   workspace  device memory of at least kda_chunk_fwd_seqpar_workspace_bytes
+ *              bytes, 16-byte aligned, owned by the caller, not overlapping any
+ *              other argument; no initialisation needed, contents undefined
+ *              afterwards.  Calls sharing one workspace must not overlap in time.
+ *
+ * Everything else (shapes, dtypes, S0 / S_final aliasing, preconditions,
+ * precision, errors) as kda_chunk_fwd, with these additions: q, k, v must be
+ * bfloat16 (KDA_ERR_UNSUPPORTED otherwise); segments outside the range or not
+ * dividing T, or a missing or short workspace, is KDA_ERR_INVALID_ARG.
+ */
+#define KDA_SEQPAR_MAX_SEGMENTS 64
+size_t kda_chunk_fwd_seqpar_workspace_bytes(int B, int T, int H, int dk, int dv, int segments);   /* 0: invalid shape */
+
+kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v,
+                                  const void *g, const void *beta, const float *S0,
+                                  void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                                  int B, int T, int H, int dk, int dv, int segments,
+                                  kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                                  kda_dtype_t out_dtype, void *stream);
+
+/*
  * kda_debug_set_spin_limit -- test hook: the bound (sleeps between polls) on
  * every wait inside the chunk kernels launched after the call, process-wide;
  * returns the previous bound (default 2^20).  A small bound makes the waits

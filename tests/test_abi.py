@@ -282,3 +282,26 @@ def test_workspace_forward_validation(lib):
     # the spin-bound hook returns the previous bound
     old = lib.kda_debug_set_spin_limit(123)
     assert lib.kda_debug_set_spin_limit(old) == 123
+
+
+def test_seqpar_workspace_bytes_and_validation(lib):
+    """Workspace size of the sequence-parallel forward (N, M and the segments'
+    starting states, float32), 0 for invalid shapes; argument errors before
+    any launch."""
+    f = lib.kda_chunk_fwd_seqpar_workspace_bytes
+    assert f(1, 4096, 8, 128, 128, 8) == 8 * 8 * (2 * 128 * 128 + 128 * 128) * 4
+    assert f(2, 300, 3, 64, 128, 3) == 2 * 3 * 3 * (2 * 64 * 128 + 64 * 64) * 4
+    for args in [(1, 4096, 8, 128, 128, 0), (1, 4096, 8, 128, 128, 65), (1, 4095, 8, 128, 128, 2),
+                 (1, 4096, 8, 96, 128, 2), (1, 4096, 8, 128, 96, 2), (0, 4096, 8, 128, 128, 2)]:
+        assert f(*args) == 0, args
+    from gated_delta_rule_101_amd import kda
+    INV = kda.KDA_ERR_INVALID_ARG
+    # distinct, aligned, never dereferenced: each call fails validation first
+    q, k, v, g, beta, o, ws = (ctypes.c_void_p((i + 1) << 36) for i in range(7))
+
+    def call(segments, T=256, nbytes=1 << 30, qkv=kda.KDA_BF16):
+        return lib.kda_chunk_fwd_seqpar(q, k, v, g, beta, None, o, None, ws, nbytes, 1, T, 2, 128, 128, segments,
+                                        qkv, kda.KDA_F32, kda.KDA_F32, None)
+    assert call(0) == INV and call(65) == INV and call(3) == INV          # range, not dividing T
+    assert call(4, qkv=kda.KDA_F32) == kda.KDA_ERR_UNSUPPORTED
+    assert call(4, nbytes=1024) == INV                                     # short workspace
