@@ -12,7 +12,8 @@ tokens, commit 8 of them) is reported under "speculative", the output
 epilogue (alone over the training-shape reads, and fused into decode) under
 "epilogue", the chunkwise backward under "backward", and two secondary
 forward workloads (one head group B1 H8 T4096, a latency figure; the long
-sequence B1 H96 T131072) under "forward_secondary", and the forward and decode with the log-decay formed
+sequence B1 H96 T131072; the first also sequence-parallel) under
+"forward_secondary", and the forward and decode with the log-decay formed
 in the kernel from gate logits under "gate_prologue".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
 by HIP events on the launch stream, and `traffic`: the HBM bytes per launch
@@ -338,8 +339,10 @@ def bench_fwd_secondary(kda, w, steps, warmup):
     head group (B1 H8 T4096: eight sequential carries, a latency figure) and
     the long single sequence (B1 H96 T131072: 2048 chunks per carry).  Both
     forward kernels are timed: the pipelined one (kda_chunk_fwd) and the ring
-    one (kda_chunk_fwd_ws, its workspace allocated before timing); the figures
-    at the top of the record are the faster one's."""
+    one (kda_chunk_fwd_ws, its workspace allocated before timing), and, where
+    the plain grid has at most 64 workgroups, the sequence-parallel forward
+    (kda_chunk_fwd_seqpar) at 4, 8 and 16 segments; the figures at the top of
+    the record are the fastest one's."""
     import torch
     from kda_workloads import gen_torch
     log(f"[bench] generating {w.name} on the device")
@@ -370,6 +373,31 @@ def bench_fwd_secondary(kda, w, steps, warmup):
                       "tflops": round(flops / (wall / steps) / 1e12, 2),
                       "roofline": roofline(nbytes, ker, stored_traffic("kda_chunk_fwd_ws", RING_SOURCES)
                                            if ring and w.name == "kda_fwd_B1_H8_T4096_d128_bf16" else None)}
+    # sequence-parallel forward where the plain grid leaves most CUs idle
+    # (the three launches of one call timed together)
+    if w.B * w.H * (w.dv // 64) <= 64:
+        for P in (4, 8, 16):
+            if w.T % P:
+                continue
+            wsp = torch.empty(kda.kda_chunk_fwd_seqpar_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, P),
+                              dtype=torch.uint8, device="cuda")
+
+            def step():
+                kda.kda_chunk_fwd_seqpar(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], o=o, S_final=Sf,
+                                         segments=P, workspace=wsp)
+
+            wall, ker, each = time_launches(step, steps, warmup, stream, per_launch=True)
+            ms = wall / steps * 1e3
+            log(f"[bench] {w.name} sequence-parallel P={P}: {ms:.3f} ms/step (kernels mean {ker * 1e3:.3f}, "
+                f"min {min(each) * 1e3:.3f} ms)")
+            runs[f"sequence_parallel_P{P}"] = {
+                "ms": round(ms, 4), "kernel_ms": round(ker * 1e3, 4),
+                "kernel_ms_median": round(median(each) * 1e3, 4), "kernel_ms_min": round(min(each) * 1e3, 4),
+                "tokens_per_s": round(w.B * w.T / (wall / steps), 1),
+                "tflops": round(flops / (wall / steps) / 1e12, 2),
+                "workspace_bytes": int(wsp.numel()),
+                "roofline": roofline(nbytes, ker, None)}
+            del wsp
     best = min(runs, key=lambda k: runs[k]["ms"])
     out = {"workload": w.name, "faster_kernel": best, **runs[best], "algorithmic_bytes": nbytes,
            "kernels": runs}
@@ -675,6 +703,22 @@ def profile_pass(kda, reps=3):
     bench_backward(kda, reps=0)
 
 
+def profile_pass_seqpar(kda, P=8, reps=3):
+    """The one-head-group forward (B1 H8 T4096) through kda_chunk_fwd_seqpar
+    in P segments: one warm-up call, then `reps` calls (each three launches:
+    transition and value slabs, combine, re-run)."""
+    import torch
+    from kda_workloads import configs, gen_torch
+    w = configs.HEADGROUP_BF16
+    d = gen_torch.fwd_inputs(w)
+    ws = torch.empty(kda.kda_chunk_fwd_seqpar_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, P), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(1 + reps):
+        kda.kda_chunk_fwd_seqpar(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], segments=P, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[profile-pass-seqpar] {w.name}, {P} segments, {1 + reps} calls done")
+
+
 def _counter_rows(directory, counter):
     import csv
     import glob
@@ -749,6 +793,9 @@ def main():
                     help="short run for rocprofv3 --pmc: calibration copy, then each kernel a few times")
     ap.add_argument("--profile-pass-fwd", action="store_true",
                     help="short run for rocprofv3 --pmc: the headline forward only, three launches")
+    ap.add_argument("--profile-pass-seqpar", action="store_true",
+                    help="short run for rocprofv3: the one-head-group forward, sequence-parallel in 8 segments, "
+                         "three calls after one warm-up")
     ap.add_argument("--only-backward", action="store_true",
                     help="run only the backward leg (two calls) and print its JSON object")
     ap.add_argument("--counters-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -773,6 +820,9 @@ def main():
         return
     if args.profile_pass_fwd:
         bench_fwd(kda, 3, 1)
+        return
+    if args.profile_pass_seqpar:
+        profile_pass_seqpar(kda)
         return
     if args.only_backward:
         print(json.dumps(bench_backward(kda, reps=2)), flush=True)
