@@ -44,6 +44,9 @@ CASES = [
     (H8.scaled(H=1, T=128, name="two_tokens_per_segment"), 64),
     (H8.scaled(H=2, T=333, gate="bf16", name="bf16_gates_S0_T333"), 3),
     (H8.scaled(H=2, T=300, name="one_segment"), 1),
+    # B H dv / 8 >= 256: the combine's 8-column workgroups (4 below that)
+    (T.scaled(B=2, H=16, T=192, dk=64, dv=64, name="cw8_d64_B2_H16_T192"), 3),
+    (H8.scaled(H=16, T=256, name="cw8_d128_H16_T256"), 4),
 ]
 
 
