@@ -400,7 +400,8 @@ def bench_fwd_secondary(kda, w, steps, warmup):
             del wsp
     best = min(runs, key=lambda k: runs[k]["ms"])
     out = {"workload": w.name, "faster_kernel": best, **runs[best], "algorithmic_bytes": nbytes,
-           "kernels": runs}
+           "kernels": runs,
+           "library_segment_choice": kda.kda_chunk_fwd_seqpar_segments(w.B, w.T, w.H, w.dk, w.dv)}
     del d, o, Sf, ws
     torch.cuda.empty_cache()
     return out

@@ -290,6 +290,37 @@ size_t kda_chunk_fwd_seqpar_workspace_bytes(int B, int T, int H, int dk, int dv,
     return kda::chunk_seqpar_workspace_bytes(B, H, dk, dv, segments);
 }
 
+int kda_chunk_fwd_seqpar_segments(int B, int T, int H, int dk, int dv, int cus)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || (dk != 64 && dk != 128) || dv % 64 || dv <= 0 || dv > 512) return 1;
+    if (cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return 1;
+    }
+    // Estimated call time in microseconds, from kernel traces on MI355X: a
+    // pass of the pipelined kernel over n chunks of 64 tokens takes about
+    // (n + 1) x 5 us per round of workgroups (one workgroup per CU; the extra
+    // period is the producers' head start) plus 3 us; the combine about
+    // 4 + 2.75 P us; the three launches of the sequence-parallel call about
+    // 10 us more than one.
+    const auto chunks = [](int t) { return (int64_t)(t + 63) / 64; };
+    const auto pass = [cus](int64_t workgroups, int64_t n) {
+        return (double)((workgroups + cus - 1) / cus) * (double)(n + 1) * 5.0 + 3.0;
+    };
+    const int64_t heads = (int64_t)B * H;
+    double best = pass(heads * (dv / 64), chunks(T));
+    int pick = 1;
+    for (int P = 2; P <= KDA_SEQPAR_MAX_SEGMENTS && P <= T; ++P) {
+        if (T % P) continue;
+        const int64_t n = chunks(T / P);
+        const double est = pass(heads * P * (dv / 64 + dk / 64), n) + 4.0 + 2.75 * P + pass(heads * P * (dv / 64), n) + 10.0;
+        if (est < best) { best = est; pick = P; }
+    }
+    return pick;
+}
+
 kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, const void *g,
                                   const void *beta, const float *S0, void *o, float *S_final,
                                   void *workspace, size_t workspace_bytes,

@@ -32,6 +32,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_SCRATC
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_chunk_fwd_ws", "kda_chunk_fwd_gate_ws",
            "kda_chunk_fwd_noalloc", "kda_chunk_fwd_seqpar", "kda_chunk_fwd_seqpar_workspace_bytes",
+           "kda_chunk_fwd_seqpar_segments",
            "kda_chunk_fwd_workspace_bytes", "kda_debug_set_spin_limit", "kda_verify_step", "kda_commit_step",
            "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_status_string", "kda_abi_version")
@@ -74,6 +75,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_seqpar.restype = i
     lib.kda_chunk_fwd_seqpar_workspace_bytes.argtypes = [i] * 6
     lib.kda_chunk_fwd_seqpar_workspace_bytes.restype = sz
+    lib.kda_chunk_fwd_seqpar_segments.argtypes = [i] * 6
+    lib.kda_chunk_fwd_seqpar_segments.restype = i
     lib.kda_debug_set_spin_limit.argtypes = [ctypes.c_uint]
     lib.kda_debug_set_spin_limit.restype = ctypes.c_uint
     lib.kda_decode_step_gate.argtypes = [vp] * 8 + [i] * 7 + [vp]
@@ -237,8 +240,14 @@ def kda_chunk_fwd_seqpar_workspace_bytes(B: int, T: int, H: int, dk: int, dv: in
     return int(load_library().kda_chunk_fwd_seqpar_workspace_bytes(B, T, H, dk, dv, segments))
 
 
+def kda_chunk_fwd_seqpar_segments(B: int, T: int, H: int, dk: int, dv: int, cus: int = 0) -> int:
+    """Segment count for kda_chunk_fwd_seqpar (1: the plain forward is expected
+    faster); cus <= 0 takes the current device's compute-unit count."""
+    return int(load_library().kda_chunk_fwd_seqpar_segments(B, T, H, dk, dv, cus))
+
+
 def kda_chunk_fwd_seqpar(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                         beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *, segments: int,
+                         beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *, segments: Optional[int] = None,
                          output_final_state: bool = True, o: Optional[torch.Tensor] = None,
                          S_final: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                          workspace: Optional[torch.Tensor] = None,
@@ -246,11 +255,14 @@ def kda_chunk_fwd_seqpar(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """kda_chunk_fwd_seqpar: the forward as `segments` pieces of the sequence run
     side by side and joined through their linear maps on the state (bfloat16
-    q, k, v; `segments` divides T).  Shapes, dtypes and results as
+    q, k, v; `segments` divides T, and None takes
+    kda_chunk_fwd_seqpar_segments' choice).  Shapes, dtypes and results as
     kda_chunk_fwd; `workspace` (device bytes) is allocated here when not given."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    if segments is None:
+        segments = int(lib.kda_chunk_fwd_seqpar_segments(B, T, H, dk, dv, 0))
     if k.shape != q.shape or g.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
         raise ValueError("shape mismatch between q, k, v, g, beta")
     if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != g.dtype:

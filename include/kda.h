@@ -279,6 +279,19 @@ kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
 #define KDA_SEQPAR_MAX_SEGMENTS 64
 size_t kda_chunk_fwd_seqpar_workspace_bytes(int B, int T, int H, int dk, int dv, int segments);   /* 0: invalid shape */
 
+/*
+ * kda_chunk_fwd_seqpar_segments -- a segment count for kda_chunk_fwd_seqpar,
+ * or 1 where the plain kda_chunk_fwd is expected to be faster.  Host-only
+ * arithmetic on the shape: among the divisors of T up to
+ * KDA_SEQPAR_MAX_SEGMENTS, the one with the smallest estimated time (passes
+ * of B * segments * H * (dv + dk) / 64 and B * segments * H * dv / 64
+ * workgroups over `cus` compute units, and the combine), compared with the
+ * plain forward's, from per-chunk and per-segment costs measured on MI355X.
+ * cus <= 0 takes the current device's compute-unit count (1 is returned if
+ * that query fails).  Invalid shapes return 1.
+ */
+int kda_chunk_fwd_seqpar_segments(int B, int T, int H, int dk, int dv, int cus);
+
 kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v,
                                   const void *g, const void *beta, const float *S0,
                                   void *o, float *S_final, void *workspace, size_t workspace_bytes,

@@ -305,3 +305,23 @@ def test_seqpar_workspace_bytes_and_validation(lib):
     assert call(0) == INV and call(65) == INV and call(3) == INV          # range, not dividing T
     assert call(4, qkv=kda.KDA_F32) == kda.KDA_ERR_UNSUPPORTED
     assert call(4, nbytes=1024) == INV                                     # short workspace
+
+
+def test_seqpar_segment_choice(lib):
+    """kda_chunk_fwd_seqpar_segments (host arithmetic, with the compute-unit
+    count given) picks what measured fastest on MI355X for the one-head-group
+    shape (8 segments), two heads (16) and a longer head group (16, its first
+    pass in two rounds); shapes whose plain grid already fills the device, and
+    invalid shapes, take 1; the count always divides T."""
+    f = lib.kda_chunk_fwd_seqpar_segments
+    assert f(1, 4096, 8, 128, 128, 256) == 8            # 0.136 ms (16: 0.146, 4: 0.201, plain 0.329)
+    assert f(1, 4096, 2, 128, 128, 256) == 16           # 0.112 ms (8: 0.129, 32: 0.130)
+    assert f(1, 16384, 8, 128, 128, 256) == 16          # 0.328 ms (8: 0.368)
+    assert f(4, 16384, 32, 128, 128, 256) == 1          # training shape: 256 workgroups already
+    assert f(1, 131072, 96, 128, 128, 256) == 1         # long sequence: 2 segments would need 768
+    assert f(1, 64, 8, 128, 128, 256) == 1              # one chunk: nothing to gain
+    for args in [(0, 4096, 8, 128, 128, 256), (1, 4096, 8, 96, 128, 256), (1, 0, 8, 128, 128, 256)]:
+        assert f(*args) == 1, args
+    for T in (1000, 4096, 333, 8192, 130):
+        P = f(1, T, 2, 64, 64, 256)
+        assert 1 <= P <= 64 and T % P == 0, (T, P)

@@ -131,3 +131,17 @@ def test_seqpar_argument_errors(kda):
     with pytest.raises(kda.KdaError) as e:
         kda.kda_chunk_fwd_seqpar(*f, *args[3:], segments=4)
     assert e.value.status == kda.KDA_ERR_UNSUPPORTED
+
+
+def test_seqpar_segment_count_from_the_library(kda, orc):
+    """segments=None takes kda_chunk_fwd_seqpar_segments' choice (a divisor of T)."""
+    w = H8.scaled(H=2, T=2048, name="auto_segments")
+    P = kda.kda_chunk_fwd_seqpar_segments(w.B, w.T, w.H, w.dk, w.dv)
+    assert P > 1 and w.T % P == 0, P
+    x = gen.fwd_inputs(w)
+    d = {n: to_dev(x[n]) for n in x}
+    say(f"[seqpar auto] {w.name} segments={P}")
+    o, S = kda.kda_chunk_fwd_seqpar(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = orc.fwd(*[x[n].f64() for n in ("q", "k", "v", "g", "beta")], x["S0"].f64())
+    assert err_ratio(f64(o), o_ref) <= 2e-2 and err_ratio(f64(S), S_ref) <= 2e-2
