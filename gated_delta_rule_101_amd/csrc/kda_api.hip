@@ -303,7 +303,7 @@ int kda_chunk_fwd_seqpar_segments(int B, int T, int H, int dk, int dv, int cus)
     // pass of the pipelined kernel over n chunks of 64 tokens takes about
     // (n + 1) x 5 us per round of workgroups (one workgroup per CU; the extra
     // period is the producers' head start) plus 3 us; the combine about
-    // 4 + 2.75 P us; the three launches of the sequence-parallel call about
+    // 6 + 1.9 P us; the three launches of the sequence-parallel call about
     // 10 us more than one.
     const auto chunks = [](int t) { return (int64_t)(t + 63) / 64; };
     const auto pass = [cus](int64_t workgroups, int64_t n) {
@@ -315,7 +315,7 @@ int kda_chunk_fwd_seqpar_segments(int B, int T, int H, int dk, int dv, int cus)
     for (int P = 2; P <= KDA_SEQPAR_MAX_SEGMENTS && P <= T; ++P) {
         if (T % P) continue;
         const int64_t n = chunks(T / P);
-        const double est = pass(heads * P * (dv / 64 + dk / 64), n) + 4.0 + 2.75 * P + pass(heads * P * (dv / 64), n) + 10.0;
+        const double est = pass(heads * P * (dv / 64 + dk / 64), n) + 6.0 + 1.9 * P + pass(heads * P * (dv / 64), n) + 10.0;
         if (est < best) { best = est; pick = P; }
     }
     return pick;

@@ -23,111 +23,133 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-// One workgroup per (b, h, CW state columns): S <- S0 (or 0); for each
-// segment p, S_start[p] = S and S <- M_p S + N_p; S_final <- S.  fp32
-// throughout.  M_p sits in LDS (rows padded to 16-byte multiples).  A thread
-// takes one row of the product, all CW columns, over one of KS slices of the
-// inner index; lanes RW apart hold the slices of one row, so the 16 lanes of
-// an LDS read phase read 16 rows (no bank conflict), and the slices are added
-// with cross-lane shuffles.  N and M are loaded ahead into two register sets
-// used in turn, and M_{p+1} is written to the second LDS buffer once M_p's
-// product is done.
-template <int DK, int CW, int CT>
+constexpr int CT = 256;   // threads per combine workgroup
+constexpr int CW = 4;     // state columns per combine workgroup
+
+// One workgroup per (b, h, 4 state columns): S <- S0 (or 0); for each segment
+// p, S_start[p] = S and S <- M_p S + N_p; S_final <- S.  fp32 throughout.
+//
+// Thread (slice, rg) computes a 4 x 4 block of each product -- rows rg + R i
+// (R = DK / 4, i = 0..3), all four columns -- over one of KS slices of KL
+// inner indices (lane bits 0 .. log2 KS - 1 are the slice).  Its M_p entries
+// (4 rows x KL) come straight from global memory into registers, loaded two
+// segments ahead into two register sets used in turn; S sits in LDS, double-buffered so that one barrier per
+// segment separates the reads of S_p from the writes of S_{p+1}, with one
+// padding row per slice so that the slices' reads of one instruction fall in
+// distinct banks.  The slices are added by a reduce-scatter of cross-lane
+// shuffles, after which each lane holds 16 / KS of the block's sums.
+template <int DK>
 __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restrict__ M, const float *__restrict__ N,
                                                             const float *S0, float *__restrict__ S_start,
                                                             float *S_final, int H, int P, int dv)
 {
-    constexpr int LDM = DK + 4;
-    constexpr int KS = CT / DK;             // slices of the inner index
-    constexpr int RW = 64 / KS;             // rows per wave
-    constexpr int KL = DK / KS;             // inner length per slice
-    constexpr int MV = DK * DK / 4 / CT;    // 16-byte pieces of M per thread
-    static_assert(KS * DK == CT && RW * KS == 64 && CW % 4 == 0 && MV * 4 * CT == DK * DK, "thread layout");
-    __shared__ alignas(16) float sM[2][DK * LDM];
-    __shared__ alignas(16) float sS[DK][CW];
+    constexpr int R = DK / 4;                // row groups
+    constexpr int KS = CT / R;               // slices of the inner index
+    constexpr int KL = DK / KS;              // inner indices per slice
+    constexpr int LOGKS = KS == 8 ? 3 : 4;
+    constexpr int NOUT = 16 / KS;            // sums per lane after the reduce-scatter
+    constexpr int SROWS = DK + KS;           // S rows in LDS, one padding row per slice
+    static_assert(KS * R == CT && (1 << LOGKS) == KS && KL % 4 == 0 && NOUT >= 1 && DK * CW % CT == 0, "thread layout");
+    __shared__ alignas(16) float sS[2][SROWS][CW];
     const int ncg = dv / CW;
     const int bh = blockIdx.x / ncg, j0 = (blockIdx.x % ncg) * CW;
     const int b = bh / H, h = bh % H;
-    const int tid = threadIdx.x, lane = tid % 64;
-    const int row = (tid / 64) * RW + lane % RW, kq = lane / RW;
+    const int tid = threadIdx.x;
+    const int slice = tid % KS, rg = tid / KS;   // slice = the low bits of the lane
     auto seg = [&](int p) { return (size_t)(b * P + p) * H + h; };   // (sequence, head) of segment p
+    auto srow = [](int k) { return k + k / KL; };                     // LDS row of state row k
 
-    struct Set {
-        f32x4v m[MV];
-        float n[CW];
-    };
-    auto fetch = [&](int p, Set &x) {
-        if (p >= P) return;
-        const float *n = N + (seg(p) * DK + row) * dv + j0;
+    // this lane's sums after the reduce-scatter: block index o = 8 b0 + 4 b1 + 2 b2 (+ b3) (+ j),
+    // b the lane's slice bits: row rg + R (o / 4), column o % 4
+    int out_row[NOUT], out_col[NOUT];
 #pragma unroll
-        for (int j = 0; j < CW; ++j) x.n[j] = kq == 0 ? n[j] : 0.f;
-        const f32x4v *src = reinterpret_cast<const f32x4v *>(M + seg(p) * DK * DK);
+    for (int j = 0; j < NOUT; ++j) {
+        int o = 0;
 #pragma unroll
-        for (int u = 0; u < MV; ++u) x.m[u] = src[tid + CT * u];
-    };
-    auto put = [&](float *dst, const Set &x) {
+        for (int L = 0; L < LOGKS; ++L) o |= ((slice >> L) & 1) << (3 - L);
+        o |= j;
+        out_row[j] = rg + R * (o / 4);
+        out_col[j] = o % 4;
+    }
+
+    f32x4v mx[4][KL / 4], my[4][KL / 4];
+    float nx[NOUT], ny[NOUT];
+    // past the last segment a fetch reloads the last one (every call issues the
+    // same loads)
+    auto fetch = [&](int p, f32x4v (&m)[4][KL / 4], float (&n)[NOUT]) {
+        p = p < P ? p : P - 1;
+        const float *Mp = M + seg(p) * DK * DK;
 #pragma unroll
-        for (int u = 0; u < MV; ++u) {
-            const int e = 4 * (tid + CT * u);
-            *reinterpret_cast<f32x4v *>(&dst[(e / DK) * LDM + e % DK]) = x.m[u];
-        }
-    };
-    // segment p: `a` holds N_p and then receives segment p + 2; `nx` holds
-    // segment p + 1, which goes to LDS once M_p's product is done
-    auto step = [&](int p, Set &a, const Set &nx) {
-        const float *Mr = sM[p & 1] + row * LDM + kq * KL;
-        float acc[CW];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < CW; ++j) acc[j] = a.n[j];
-        fetch(p + 2, a);
-        for (int e = tid; e < DK * CW; e += CT) {
-            const int r = e / CW, j = e % CW;
-            S_start[(seg(p) * DK + r) * dv + j0 + j] = sS[r][j];
-        }
-#pragma unroll 2
-        for (int kk = 0; kk < KL; kk += 4) {
-            const f32x4v m4 = *reinterpret_cast<const f32x4v *>(&Mr[kk]);
+            for (int u = 0; u < KL / 4; ++u)
+                m[i][u] = *reinterpret_cast<const f32x4v *>(&Mp[(size_t)(rg + R * i) * DK + KL * slice + 4 * u]);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float *sr = sS[kq * KL + kk + u];
-#pragma unroll
-                for (int j = 0; j < CW; j += 4) {
-                    const f32x4v s4 = *reinterpret_cast<const f32x4v *>(&sr[j]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[j + i] = fmaf(m4[u], s4[i], acc[j + i]);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = RW; m < 64; m *= 2)
-#pragma unroll
-            for (int j = 0; j < CW; ++j) acc[j] += __shfl_xor(acc[j], m);
-        __syncthreads();   // every read of sS and of M_p is done
-        if (kq == 0)
-#pragma unroll
-            for (int j = 0; j < CW; j += 4)
-                *reinterpret_cast<f32x4v *>(&sS[row][j]) = f32x4v{acc[j], acc[j + 1], acc[j + 2], acc[j + 3]};
-        if (p + 1 < P) put(sM[(p + 1) & 1], nx);
-        __syncthreads();
+        for (int j = 0; j < NOUT; ++j) n[j] = N[(seg(p) * DK + out_row[j]) * dv + j0 + out_col[j]];
     };
 
     for (int e = tid; e < DK * CW; e += CT) {
         const int r = e / CW, j = e % CW;
-        sS[r][j] = S0 ? S0[((size_t)bh * DK + r) * dv + j0 + j] : 0.f;
+        sS[0][srow(r)][j] = S0 ? S0[((size_t)bh * DK + r) * dv + j0 + j] : 0.f;
     }
-    Set x, y;
-    fetch(0, x);
-    fetch(1, y);
-    put(sM[0], x);
+    fetch(0, mx, nx);
+    fetch(1, my, ny);
     __syncthreads();
+
+    // segment p: M_p and N_p in (m, n), which then receive segment p + 2
+    auto step = [&](int p, f32x4v (&m)[4][KL / 4], float (&n)[NOUT]) {
+        const int cur = p & 1;
+#pragma unroll
+        for (int u = 0; u < DK * CW / CT; ++u) {   // a fixed number of stores, as for the loads
+            const int e = tid + CT * u, r = e / CW, j = e % CW;
+            S_start[(seg(p) * DK + r) * dv + j0 + j] = sS[cur][srow(r)][j];
+        }
+        float acc[16];
+#pragma unroll
+        for (int o = 0; o < 16; ++o) acc[o] = 0.f;
+#pragma unroll
+        for (int u = 0; u < KL / 4; ++u) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const f32x4v s4 = *reinterpret_cast<const f32x4v *>(&sS[cur][srow(KL * slice + 4 * u + kk)][0]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[4 * i + c] = fmaf(m[i][u][kk], s4[c], acc[4 * i + c]);
+            }
+        }
+        float nn[NOUT];
+#pragma unroll
+        for (int j = 0; j < NOUT; ++j) nn[j] = n[j];
+        fetch(p + 2, m, n);
+        // reduce-scatter over the slice bits: at level L a lane keeps the half of
+        // its sums whose index bit 3 - L equals its slice bit L
+        int cnt = 16;
+#pragma unroll
+        for (int L = 0; L < LOGKS; ++L) {
+            const bool hi = (slice >> L) & 1;
+            cnt /= 2;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j >= cnt) break;
+                const float send = hi ? acc[j] : acc[j + cnt];
+                const float keep = hi ? acc[j + cnt] : acc[j];
+                acc[j] = keep + __shfl_xor(send, 1 << L);
+            }
+        }
+        float *nxt = &sS[cur ^ 1][0][0];
+#pragma unroll
+        for (int j = 0; j < NOUT; ++j) nxt[srow(out_row[j]) * CW + out_col[j]] = acc[j] + nn[j];
+        __syncthreads();
+    };
     for (int p = 0; p < P; p += 2) {
-        step(p, x, y);
-        if (p + 1 < P) step(p + 1, y, x);
+        step(p, mx, nx);
+        if (p + 1 < P) step(p + 1, my, ny);
     }
     if (S_final)
         for (int e = tid; e < DK * CW; e += CT) {
             const int r = e / CW, j = e % CW;
-            S_final[((size_t)bh * DK + r) * dv + j0 + j] = sS[r][j];
+            S_final[((size_t)bh * DK + r) * dv + j0 + j] = sS[P & 1][srow(r)][j];
         }
 }
 
@@ -135,14 +157,8 @@ template <int DK>
 void launch_combine(const float *M, const float *N, const float *S0, float *S_start, float *S_final, int B, int H,
                     int P, int dv, hipStream_t stream)
 {
-    // 4 columns per workgroup while 8 would leave CUs idle; each M_p is then
-    // read by twice as many workgroups (from L2)
-    const size_t wg8 = (size_t)B * H * (dv / 8);
-    if (wg8 >= 256)
-        seqpar_combine_kernel<DK, 8, 256><<<(unsigned)wg8, 256, 0, stream>>>(M, N, S0, S_start, S_final, H, P, dv);
-    else {
-        seqpar_combine_kernel<DK, 4, 256><<<(unsigned)(2 * wg8), 256, 0, stream>>>(M, N, S0, S_start, S_final, H, P, dv);
-    }
+    const unsigned grid = (unsigned)((size_t)B * H * (dv / CW));
+    seqpar_combine_kernel<DK><<<grid, CT, 0, stream>>>(M, N, S0, S_start, S_final, H, P, dv);
 }
 
 }  // namespace
@@ -156,7 +172,7 @@ size_t chunk_seqpar_workspace_bytes(int B, int H, int dk, int dv, int P)
 hipError_t launch_chunk_fwd_seqpar(const ChunkFwdArgs &a, int P, void *workspace, hipStream_t stream)
 {
     (void)hipGetLastError();
-    if (P < 1 || a.T % P != 0 || !a.qkv_bf16 || a.lengths || a.A_log || a.dv % 8) return hipErrorInvalidValue;
+    if (P < 1 || a.T % P != 0 || !a.qkv_bf16 || a.lengths || a.A_log || a.dv % CW) return hipErrorInvalidValue;
     const size_t n = (size_t)a.B * P * a.H;
     float *N = static_cast<float *>(workspace);
     float *M = N + n * a.dk * a.dv;
