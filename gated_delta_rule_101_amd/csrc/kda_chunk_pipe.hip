@@ -326,11 +326,18 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
             for (int i = 0; i < TILE; ++i) X[i] = (i == r) ? one : 0.f;
             unit_lower_inverse_steps<0>(X, Lc);
-            // lane group gq stores rows 4gq..4gq+3 of column r (row r of the transpose)
+            // lane group gq stores rows 4gq..4gq+3 of column r (row r of the
+            // transpose), chosen by masks from the two bits of gq: a chain of
+            // equality tests on gq compiles to nested branches, and a select
+            // between array elements to a select of addresses (the array then
+            // lives in scratch memory)
             f32x4 part;
+            const unsigned m1 = (gq & 1) ? ~0u : 0u, m2 = (gq & 2) ? ~0u : 0u;
+            auto pick = [](float a, float b, unsigned m) {
+                return __uint_as_float(__float_as_uint(a) ^ ((__float_as_uint(a) ^ __float_as_uint(b)) & m));
+            };
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                part[i] = gq == 0 ? X[i] : gq == 1 ? X[4 + i] : gq == 2 ? X[8 + i] : X[12 + i];
+            for (int i = 0; i < 4; ++i) part[i] = pick(pick(X[i], X[4 + i], m1), pick(X[8 + i], X[12 + i], m1), m2);
             *reinterpret_cast<f16x4 *>(&sm.stage[c & 1].InvT[M][tile_at(r, gq)]) = h16::pack4(part);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             if (lane == 0) __hip_atomic_fetch_add(&sm.inv_posted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
