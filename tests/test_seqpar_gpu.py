@@ -145,3 +145,17 @@ def test_seqpar_segment_count_from_the_library(kda, orc):
     torch.cuda.synchronize()
     o_ref, S_ref = orc.fwd(*[x[n].f64() for n in ("q", "k", "v", "g", "beta")], x["S0"].f64())
     assert err_ratio(f64(o), o_ref) <= 2e-2 and err_ratio(f64(S), S_ref) <= 2e-2
+
+
+def test_seqpar_without_final_state(kda, orc):
+    """output_final_state=False: no S_final is written (the combine skips it) and
+    o is unchanged."""
+    w = H8.scaled(H=2, T=640, name="no_final_state")
+    x = gen.fwd_inputs(w)
+    d = {n: to_dev(x[n]) for n in x}
+    o, S = kda.kda_chunk_fwd_seqpar(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], segments=5,
+                                    output_final_state=False)
+    torch.cuda.synchronize()
+    assert S is None
+    o_ref, _ = orc.fwd(*[x[n].f64() for n in ("q", "k", "v", "g", "beta")], x["S0"].f64())
+    assert err_ratio(f64(o), o_ref) <= 2e-2
