@@ -13,8 +13,8 @@
 //   2. the segments' true starting states in order, S_{p+1} = M_p S_p + N_p
 //      (fp32, this file), the last one being the final state;
 //   3. every segment again from its true starting state, writing o.
-// Steps 1 and 3 are each T / P chunks long instead of T; step 2 is P small
-// products.
+// Steps 1 and 3 each carry the state over T / P tokens instead of T; step 2
+// is P small products in sequence.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -33,10 +33,10 @@ constexpr int CW = 4;     // state columns per combine workgroup
 // (R = DK / 4, i = 0..3), all four columns -- over one of KS slices of KL
 // inner indices (lane bits 0 .. log2 KS - 1 are the slice).  Its M_p entries
 // (4 rows x KL) come straight from global memory into registers, loaded two
-// segments ahead into two register sets used in turn; S sits in LDS, double-buffered so that one barrier per
-// segment separates the reads of S_p from the writes of S_{p+1}, with one
-// padding row per slice so that the slices' reads of one instruction fall in
-// distinct banks.  The slices are added by a reduce-scatter of cross-lane
+// segments ahead into two register sets used in turn.  S sits in LDS,
+// double-buffered so that one barrier per segment separates the reads of S_p
+// from the writes of S_{p+1}, with one padding row per slice so that the
+// slices' reads of one instruction fall in distinct banks.  The slices are added by a reduce-scatter of cross-lane
 // shuffles, after which each lane holds 16 / KS of the block's sums.
 template <int DK>
 __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restrict__ M, const float *__restrict__ N,
