@@ -252,9 +252,11 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             const uint32_t off = (uint32_t)t * (uint32_t)(H * DK * 2) + 8u * (uint32_t)gq;
 #pragma unroll
             for (int blk = blk0; blk < blk1; ++blk) {
-                const u32x2 qv = __builtin_amdgcn_raw_buffer_load_b64(qr, off + 32u * blk, 0, 0);
+                if constexpr (!TR) {   // transition passes form no output: no queries
+                    const u32x2 qv = __builtin_amdgcn_raw_buffer_load_b64(qr, off + 32u * blk, 0, 0);
+                    in.q[blk].a = make_uint2(qv.x, qv.y);
+                }
                 const u32x2 kv = __builtin_amdgcn_raw_buffer_load_b64(kr, off + 32u * blk, 0, 0);
-                in.q[blk].a = make_uint2(qv.x, qv.y);
                 in.k[blk].a = make_uint2(kv.x, kv.y);
             }
         };
@@ -358,9 +360,11 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 float f[KT][4];   // f = e^b in [e^-80, 1] (1/f, up to e^80, is recomputed where used)
                 if constexpr (GLDS) {
                     // the gates' LDS-direct loads are complete once at most the 2 KT
-                    // q and k loads issued after them are outstanding
-                    static_assert(2 * KT < 64, "vmcnt field");
-                    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * KT) & 15) | (((2 * KT) >> 4) << 14));
+                    // q and k loads issued after them (KT k loads in a transition
+                    // pass) are outstanding
+                    constexpr int YOUNGER = TR ? KT : 2 * KT;
+                    static_assert(YOUNGER < 64, "vmcnt field");
+                    __builtin_amdgcn_s_waitcnt(0x0F70 | (YOUNGER & 15) | ((YOUNGER >> 4) << 14));
                     // Tri(s, t) = [s <= t], with the rows of tokens past the end zeroed:
                     // identity tokens (g = 0) drop out of every sum
                     i16x4 tri;
@@ -430,14 +434,20 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 // channels 32p + 4gq + (0..3) and 32p + 16 + 4gq + (0..3).
                 f32x4 gq_d = {0.f, 0.f, 0.f, 0.f}, gk_d = {0.f, 0.f, 0.f, 0.f};
                 auto diagonal = [&](const float (&qf)[8], const float (&kf)[8], const float (&ki)[8]) {
-                    BF::frag8 aqh, aql, bih, bil;
-                    BF::split8(qf, aqh, aql);
-                    BF::split8(ki, bih, bil);
-                    const BF::frag8 akh = BF::pack8(kf);
-                    gq_d = BF::mma32(aqh, bih, gq_d);
-                    gq_d = BF::mma32(aqh, bil, gq_d);
-                    gq_d = BF::mma32(aql, bih, gq_d);
-                    gk_d = BF::mma32(akh, bih, gk_d);
+                    if constexpr (!TR) {
+                        BF::frag8 aqh, aql, bih, bil;
+                        BF::split8(qf, aqh, aql);
+                        BF::split8(ki, bih, bil);
+                        const BF::frag8 akh = BF::pack8(kf);
+                        gq_d = BF::mma32(aqh, bih, gq_d);
+                        gq_d = BF::mma32(aqh, bil, gq_d);
+                        gq_d = BF::mma32(aql, bih, gq_d);
+                        gk_d = BF::mma32(akh, bih, gk_d);
+                    } else {   // no output: only the key-key block
+                        BF::frag8 bih, bil;
+                        BF::split8(ki, bih, bil);
+                        gk_d = BF::mma32(BF::pack8(kf), bih, gk_d);
+                    }
                 };
 
                 if constexpr (M < NT - 1) {
@@ -462,7 +472,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                         for (int hh = 0; hh < 2; ++hh) {
                             float qv[4], kv[4];
-                            in.q[2 * p + hh].to_f32(qv);
+                            if constexpr (!TR) in.q[2 * p + hh].to_f32(qv);
+                            else qv[0] = qv[1] = qv[2] = qv[3] = 0.f;
                             in.k[2 * p + hh].to_f32(kv);
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
@@ -516,7 +527,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             if constexpr (M == 0)
                                 if (r == 0) *reinterpret_cast<f32x4 *>(&st.GamC[ch]) = dma;
                             float qv[4], kv[4];
-                            in.q[blk].to_f32(qv);
+                            if constexpr (!TR) in.q[blk].to_f32(qv);
+                            else qv[0] = qv[1] = qv[2] = qv[3] = 0.f;
                             in.k[blk].to_f32(kv);
                             f32x4 qt, kt, kb;
 #pragma unroll
@@ -533,7 +545,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                                 kb[i] = ik * dma[i];   // decayed to the chunk end, <= |k|
                             }
                             const int row = (TILE * M + r) * LDK + ch;
-                            *reinterpret_cast<f16x4 *>(&st.Qt[row]) = h16::pack4(qt);
+                            if constexpr (!TR) *reinterpret_cast<f16x4 *>(&st.Qt[row]) = h16::pack4(qt);
                             *reinterpret_cast<f16x4 *>(&st.Kt[row]) = h16::pack4(kt);
                             *reinterpret_cast<f16x4 *>(&st.Kb[(TILE * M + r) * LDKB + ch]) = h16::pack4(kb);
                         }
@@ -543,7 +555,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                         const int kh_off = r * LDK + 32 * p + 4 * gq;
                         if constexpr (M >= 1) {
                             const f16x8 bk = h16::lds4x2(&sm.Kh[M - 1][kh_off], &sm.Kh[M - 1][kh_off + 16]);
-                            gq_o[0] = h16::mma32(h16::pack8(qf), bk, gq_o[0]);
+                            if constexpr (!TR) gq_o[0] = h16::mma32(h16::pack8(qf), bk, gq_o[0]);
                             gk_o[0] = h16::mma32(h16::pack8(kf), bk, gk_o[0]);
                         }
                         if constexpr (M >= 2) {
@@ -551,7 +563,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             float a[8], e[8];
 #pragma unroll
                             for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v2[i]; e[i] = kf[i] * v2[i]; }
-                            gq_o[1] = h16::mma32(h16::pack8(a), bk, gq_o[1]);
+                            if constexpr (!TR) gq_o[1] = h16::mma32(h16::pack8(a), bk, gq_o[1]);
                             gk_o[1] = h16::mma32(h16::pack8(e), bk, gk_o[1]);
                         }
                         if constexpr (M >= 3) {
@@ -559,7 +571,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             float a[8], e[8];
 #pragma unroll
                             for (int i = 0; i < 8; ++i) { a[i] = qf[i] * v3[i]; e[i] = kf[i] * v3[i]; }
-                            gq_o[2] = h16::mma32(h16::pack8(a), bk, gq_o[2]);
+                            if constexpr (!TR) gq_o[2] = h16::mma32(h16::pack8(a), bk, gq_o[2]);
                             gk_o[2] = h16::mma32(h16::pack8(e), bk, gk_o[2]);
                         }
                         // this block pair's q and k are consumed: fetch the next chunk's
@@ -578,14 +590,15 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                             aq[i] = (r > row) ? 0.f : gq_d[i];             // keep s <= t
                             ak[i] = (r >= row) ? 0.f : gk_d[i] * bet[i];   // keep s <  t
                         }
-                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, M)][tile_at(r, gq)]) = h16::pack4(aq);
+                        if constexpr (!TR) *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, M)][tile_at(r, gq)]) = h16::pack4(aq);
                         *reinterpret_cast<f32x4 *>(&sm.LdT[M][r][4 * gq]) = ak;
                     }
 #pragma unroll
                     for (int d = 1; d <= M; ++d) {
                         const int n = M - d;
-                        *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, n)][tile_at(r, gq)]) =
-                            h16::pack4(gq_o[d - 1]);
+                        if constexpr (!TR)
+                            *reinterpret_cast<f16x4 *>(&st.AqkT[lower_index(M, n)][tile_at(r, gq)]) =
+                                h16::pack4(gq_o[d - 1]);
                         *reinterpret_cast<f16x4 *>(&st.LT[strict_index(M, n)][tile_at(r, gq)]) =
                             h16::pack4(gk_o[d - 1] * bet);
                     }
@@ -709,7 +722,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
 #pragma unroll
                 for (int j = 0; j < KB; ++j) {
                     const int ch = row + 32 * j + 4 * gq;
-                    q8[j] = h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]);
+                    if constexpr (!TR) q8[j] = h16::lds4x2(&st.Qt[ch], &st.Qt[ch + 16]);   // (no output: no Gamma.Q)
                     k8[j] = h16::lds4x2(&st.Kt[ch], &st.Kt[ch + 16]);
                 }
             };
@@ -732,7 +745,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
                 f32x4 aQ = {0.f, 0.f, 0.f, 0.f}, aK = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < KB; ++j) {
-                    aQ = h16::mma32(Sh[j], aq[mm & 1][j], aQ);
+                    if constexpr (!TR) aQ = h16::mma32(Sh[j], aq[mm & 1][j], aQ);
                     aK = h16::mma32(ak[mm & 1][j], Sh[j], aK);
                 }
                 accQ[mm] = aQ;
@@ -745,7 +758,8 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             // ---- A_qk tiles, read while the solve runs
             f16x4 aqk[NLOWER];
 #pragma unroll
-            for (int i = 0; i < NLOWER; ++i) aqk[i] = h16::tr4(&st.AqkT[i][tro]);
+            for (int i = 0; i < NLOWER; ++i)
+                if constexpr (!TR) aqk[i] = h16::tr4(&st.AqkT[i][tro]);
 
             // ---- the diagonal inverses of this chunk: the producers store them at
             // the start of this period (four per chunk, counted from the first
@@ -803,7 +817,7 @@ kda_chunk_pipe_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict
             // ---- O^T = ((Gamma.Q) S)^T + U^T A_qk^T (U as the A operand, the A_qk
             // tiles as B): lane (g, r) holds four consecutive columns of token r,
             // one wide store per row tile
-            if (o_head) {
+            if (!TR && o_head) {
                 const auto orr = rsrc(o_head + (size_t)c * C * Hdv);
                 const uint32_t o_lane = (uint32_t)r * o_stride + (uint32_t)(4 * gq) * (uint32_t)sizeof(OT);
 #pragma unroll
