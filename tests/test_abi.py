@@ -314,10 +314,10 @@ def test_seqpar_segment_choice(lib):
     pass in two rounds) and one long head (64); shapes whose plain grid already fills the device, and
     invalid shapes, take 1; the count always divides T."""
     f = lib.kda_chunk_fwd_seqpar_segments
-    assert f(1, 4096, 8, 128, 128, 256) == 8            # 0.133 ms (16: 0.136, 4: 0.201, plain 0.329)
-    assert f(1, 4096, 2, 128, 128, 256) == 16           # 0.105 ms (8: 0.127, 32: 0.114)
-    assert f(1, 16384, 8, 128, 128, 256) == 16          # 0.314 ms (8: 0.375)
-    assert f(1, 32768, 1, 128, 128, 256) == 64          # 0.228 ms (32: 0.248, plain 2.442)
+    assert f(1, 4096, 8, 128, 128, 256) == 8            # 0.119 ms (16: 0.122, 4: 0.177, plain 0.317)
+    assert f(1, 4096, 2, 128, 128, 256) == 16           # 0.096 ms (8: 0.113, 32: 0.108)
+    assert f(1, 16384, 8, 128, 128, 256) == 16          # 0.267 ms (8: 0.326)
+    assert f(1, 32768, 1, 128, 128, 256) == 64          # 0.215 ms (32: 0.224, plain 2.379)
     assert f(4, 16384, 32, 128, 128, 256) == 1          # training shape: 256 workgroups already
     assert f(1, 131072, 96, 128, 128, 256) == 1         # long sequence: 2 segments would need 768
     assert f(1, 64, 8, 128, 128, 256) == 1              # one chunk: nothing to gain
