@@ -321,14 +321,14 @@ int kda_chunk_fwd_seqpar_segments(int B, int T, int H, int dk, int dv, int cus)
     return pick;
 }
 
-kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, const void *g,
-                                  const void *beta, const float *S0, void *o, float *S_final,
-                                  void *workspace, size_t workspace_bytes,
-                                  int B, int T, int H, int dk, int dv, int segments,
-                                  kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
-                                  void *stream)
+namespace {
+// kda_chunk_fwd_seqpar and kda_chunk_fwd_gate_seqpar (gate logits with A_log)
+kda_status_t run_seqpar(const void *q, const void *k, const void *v, const void *g, const float *A_log,
+                        const void *beta, const float *S0, void *o, float *S_final, void *workspace,
+                        size_t workspace_bytes, int B, int T, int H, int dk, int dv, int segments,
+                        kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype, void *stream)
 {
-    const kda_status_t st = check_chunk(q, k, v, g, beta, S0, o, S_final, nullptr, nullptr, B, T, H, dk, dv,
+    const kda_status_t st = check_chunk(q, k, v, g, beta, S0, o, S_final, A_log, nullptr, B, T, H, dk, dv,
                                         qkv_dtype, gate_dtype, out_dtype, true, true);
     if (st != KDA_OK) return st;
     if (segments < 1 || segments > KDA_SEQPAR_MAX_SEGMENTS || (T > 0 && T % segments)) return KDA_ERR_INVALID_ARG;
@@ -337,6 +337,7 @@ kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, c
     if (B == 0 || H == 0) return KDA_OK;
     kda::ChunkFwdArgs a = chunk_args(q, k, v, g, beta, S0, o, S_final, B, T, H, dk, dv,
                                      qkv_dtype, gate_dtype, out_dtype);
+    a.A_log = A_log;
     if (T == 0) return run_chunk(a, stream);
     const size_t need = kda::chunk_seqpar_workspace_bytes(B, H, dk, dv, segments);
     if (!workspace || !aligned16(workspace) || workspace_bytes < need) return KDA_ERR_INVALID_ARG;
@@ -347,7 +348,8 @@ kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, c
         const Span sp_w = span(workspace, workspace_bytes);
         const Span others[] = {span(q, tok * dk * sq), span(k, tok * dk * sq), span(v, tok * dv * sq),
                                span(g, tok * dk * sg), span(beta, tok * sg), span(o, tok * dv * so),
-                               span(S0, S0 ? state_bytes : 0), span(S_final, S_final ? state_bytes : 0)};
+                               span(S0, S0 ? state_bytes : 0), span(S_final, S_final ? state_bytes : 0),
+                               span(A_log, A_log ? (size_t)H * sizeof(float) : 0)};
         for (const Span &x : others)
             if (overlap(sp_w, x)) return KDA_ERR_INVALID_ARG;
     }
@@ -355,6 +357,30 @@ kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, c
     // S_final may alias S0 as in kda_chunk_fwd
     return kda::launch_chunk_fwd_seqpar(a, segments, workspace, (hipStream_t)stream) == hipSuccess ? KDA_OK
                                                                                           : KDA_ERR_LAUNCH;
+}
+}  // namespace
+
+kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, const float *S0, void *o, float *S_final,
+                                  void *workspace, size_t workspace_bytes,
+                                  int B, int T, int H, int dk, int dv, int segments,
+                                  kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                  void *stream)
+{
+    return run_seqpar(q, k, v, g, nullptr, beta, S0, o, S_final, workspace, workspace_bytes, B, T, H, dk, dv,
+                      segments, qkv_dtype, gate_dtype, out_dtype, stream);
+}
+
+kda_status_t kda_chunk_fwd_gate_seqpar(const void *q, const void *k, const void *v, const void *z,
+                                       const float *A_log, const void *beta, const float *S0, void *o,
+                                       float *S_final, void *workspace, size_t workspace_bytes,
+                                       int B, int T, int H, int dk, int dv, int segments,
+                                       kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype, kda_dtype_t out_dtype,
+                                       void *stream)
+{
+    if (!A_log && B > 0 && H > 0) return KDA_ERR_INVALID_ARG;
+    return run_seqpar(q, k, v, z, A_log, beta, S0, o, S_final, workspace, workspace_bytes, B, T, H, dk, dv,
+                      segments, qkv_dtype, gate_dtype, out_dtype, stream);
 }
 
 unsigned kda_debug_set_spin_limit(unsigned limit) { return kda::set_spin_limit(limit); }

@@ -912,19 +912,27 @@ hipError_t launch(const ChunkFwdArgs &a, hipStream_t stream)
 }
 
 // The value slabs' final states from a zero start (a.S_final) and the chunk
-// sequence's linear map (M_out), no outputs; bf16 gates or fp32 gates, no
-// logits, no per-sequence lengths.
-template <int DK, bool GBF>
+// sequence's linear map (M_out), no outputs; bf16 or fp32 gates, or gate
+// logits with a.A_log; no per-sequence lengths.
+template <int DK, bool GBF, bool GL>
 hipError_t launch_trans(const ChunkFwdArgs &a, float *M_out, hipStream_t stream)
 {
     typedef typename Store<GBF>::type GT;
     const int nslab_v = a.dv / WV, nslab = nslab_v + DK / WV;
     const unsigned grid = (unsigned)(a.B * a.H * nslab);
-    kda_chunk_pipe_kernel<DK, GBF, false, false, true><<<grid, NTHREADS, 0, stream>>>(
+    kda_chunk_pipe_kernel<DK, GBF, false, GL, true><<<grid, NTHREADS, 0, stream>>>(
         (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, (const GT *)a.g,
-        (const GT *)a.beta, nullptr, nullptr, a.S_final, nullptr, nullptr, a.B, a.T, a.H, a.dv, nslab, nslab_v,
+        (const GT *)a.beta, nullptr, nullptr, a.S_final, nullptr, a.A_log, a.B, a.T, a.H, a.dv, nslab, nslab_v,
         M_out, spin_limit());
     return hipGetLastError();
+}
+
+template <int DK>
+hipError_t dispatch_trans(const ChunkFwdArgs &a, float *M_out, hipStream_t s)
+{
+    if (a.A_log)
+        return a.gate_bf16 ? launch_trans<DK, true, true>(a, M_out, s) : launch_trans<DK, false, true>(a, M_out, s);
+    return a.gate_bf16 ? launch_trans<DK, true, false>(a, M_out, s) : launch_trans<DK, false, false>(a, M_out, s);
 }
 
 template <int DK, bool GL>
@@ -947,9 +955,8 @@ hipError_t launch_chunk_fwd_bf16_trans(const ChunkFwdArgs &a, float *M_out, hipS
     (void)hipGetLastError();
     if ((uint64_t)C * a.H * a.dv * 4 + (uint64_t)a.H * a.dv * 4 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
     if ((uint64_t)C * a.H * a.dk * 2 + (uint64_t)a.H * a.dk * 2 >= ((uint64_t)1 << 31)) return hipErrorInvalidValue;
-    if (a.lengths || a.A_log || !M_out) return hipErrorInvalidValue;
-    if (a.dk == 64) return a.gate_bf16 ? launch_trans<64, true>(a, M_out, stream) : launch_trans<64, false>(a, M_out, stream);
-    return a.gate_bf16 ? launch_trans<128, true>(a, M_out, stream) : launch_trans<128, false>(a, M_out, stream);
+    if (a.lengths || !M_out) return hipErrorInvalidValue;
+    return a.dk == 64 ? dispatch_trans<64>(a, M_out, stream) : dispatch_trans<128>(a, M_out, stream);
 }
 
 hipError_t launch_chunk_fwd_bf16(const ChunkFwdArgs &a, hipStream_t stream)

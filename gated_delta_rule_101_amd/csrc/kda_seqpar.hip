@@ -172,7 +172,7 @@ size_t chunk_seqpar_workspace_bytes(int B, int H, int dk, int dv, int P)
 hipError_t launch_chunk_fwd_seqpar(const ChunkFwdArgs &a, int P, void *workspace, hipStream_t stream)
 {
     (void)hipGetLastError();
-    if (P < 1 || a.T % P != 0 || !a.qkv_bf16 || a.lengths || a.A_log || a.dv % CW) return hipErrorInvalidValue;
+    if (P < 1 || a.T % P != 0 || !a.qkv_bf16 || a.lengths || a.dv % CW) return hipErrorInvalidValue;
     const size_t n = (size_t)a.B * P * a.H;
     float *N = static_cast<float *>(workspace);
     float *M = N + n * a.dk * a.dv;

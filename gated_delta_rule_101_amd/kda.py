@@ -32,7 +32,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_SCRATC
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_gate", "kda_chunk_fwd_ws", "kda_chunk_fwd_gate_ws",
            "kda_chunk_fwd_noalloc", "kda_chunk_fwd_seqpar", "kda_chunk_fwd_seqpar_workspace_bytes",
-           "kda_chunk_fwd_seqpar_segments",
+           "kda_chunk_fwd_seqpar_segments", "kda_chunk_fwd_gate_seqpar",
            "kda_chunk_fwd_workspace_bytes", "kda_debug_set_spin_limit", "kda_verify_step", "kda_commit_step",
            "kda_decode_step", "kda_decode_step_gate", "kda_decode_step_gated", "kda_output_gate",
            "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_status_string", "kda_abi_version")
@@ -72,6 +72,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_chunk_fwd_workspace_bytes.argtypes = [i] * 5
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd_seqpar.argtypes = [vp] * 9 + [sz] + [i] * 9 + [vp]
+    lib.kda_chunk_fwd_gate_seqpar.argtypes = [vp] * 10 + [sz] + [i] * 9 + [vp]
+    lib.kda_chunk_fwd_gate_seqpar.restype = i
     lib.kda_chunk_fwd_seqpar.restype = i
     lib.kda_chunk_fwd_seqpar_workspace_bytes.argtypes = [i] * 6
     lib.kda_chunk_fwd_seqpar_workspace_bytes.restype = sz
@@ -284,6 +286,46 @@ def kda_chunk_fwd_seqpar(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: t
                                   int(segments), _dtype_code(q), _dtype_code(g), _dtype_code(o),
                                   _stream_handle(stream, dev))
     _raise(st, "kda_chunk_fwd_seqpar")
+    return o, S_final
+
+
+def kda_chunk_fwd_gate_seqpar(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, z: torch.Tensor,
+                              A_log: torch.Tensor, beta: torch.Tensor, S0: Optional[torch.Tensor] = None, *,
+                              segments: Optional[int] = None, output_final_state: bool = True,
+                              o: Optional[torch.Tensor] = None, S_final: Optional[torch.Tensor] = None,
+                              out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                              stream: Optional[torch.cuda.Stream] = None
+                              ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_chunk_fwd_gate_seqpar: kda_chunk_fwd_seqpar with the log-decay formed in
+    the kernels from gate logits z [B,T,H,dk] and A_log [H] float32."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or z.shape != q.shape or v.shape != (B, T, H, dv) or beta.shape != (B, T, H):
+        raise ValueError("shape mismatch between q, k, v, z, beta")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != z.dtype:
+        raise TypeError("q, k, v share one dtype; z and beta share one dtype")
+    if A_log.shape != (H,) or A_log.dtype != torch.float32:
+        raise ValueError("A_log must be float32 [H]")
+    if S0 is not None and (S0.shape != (B, H, dk, dv) or S0.dtype != torch.float32):
+        raise ValueError("S0 must be float32 [B,H,dk,dv]")
+    if segments is None:
+        segments = int(lib.kda_chunk_fwd_seqpar_segments(B, T, H, dk, dv, 0))
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype or torch.float32, device=q.device)
+    elif o.shape != (B, T, H, dv):
+        raise ValueError("o must be [B,T,H,dv]")
+    if S_final is None and output_final_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if workspace is None and T > 0:
+        need = int(lib.kda_chunk_fwd_seqpar_workspace_bytes(B, T, H, dk, dv, int(segments)))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dev = _check_dev(q, k, v, z, A_log, beta, S0, o, S_final, workspace)
+    st = lib.kda_chunk_fwd_gate_seqpar(_ptr(q), _ptr(k), _ptr(v), _ptr(z), _ptr(A_log), _ptr(beta), _ptr(S0),
+                                       _ptr(o), _ptr(S_final), _ptr(workspace), _nbytes(workspace), B, T, H, dk,
+                                       dv, int(segments), _dtype_code(q), _dtype_code(z), _dtype_code(o),
+                                       _stream_handle(stream, dev))
+    _raise(st, "kda_chunk_fwd_gate_seqpar")
     return o, S_final
 
 

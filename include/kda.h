@@ -300,6 +300,22 @@ kda_status_t kda_chunk_fwd_seqpar(const void *q, const void *k, const void *v,
                                   kda_dtype_t out_dtype, void *stream);
 
 /*
+ * kda_chunk_fwd_gate_seqpar -- kda_chunk_fwd_seqpar with the log-decay formed
+ * in the kernels from gate logits z and per-head A_log, as kda_chunk_fwd_gate
+ * does ("Kimi K3 - Lesson 3 of 14 - Sequence axis", the scaled-sigmoid
+ * mapping).  Arguments as kda_chunk_fwd_seqpar with z in place of g and A_log
+ * ([H] float32, device) added; a NULL A_log is KDA_ERR_INVALID_ARG.  The
+ * workspace size is kda_chunk_fwd_seqpar_workspace_bytes'.
+ */
+kda_status_t kda_chunk_fwd_gate_seqpar(const void *q, const void *k, const void *v,
+                                       const void *z, const float *A_log, const void *beta,
+                                       const float *S0, void *o, float *S_final,
+                                       void *workspace, size_t workspace_bytes,
+                                       int B, int T, int H, int dk, int dv, int segments,
+                                       kda_dtype_t qkv_dtype, kda_dtype_t gate_dtype,
+                                       kda_dtype_t out_dtype, void *stream);
+
+/*
  * kda_debug_set_spin_limit -- test hook: the bound (sleeps between polls) on
  * every wait inside the chunk kernels launched after the call, process-wide;
  * returns the previous bound (default 2^20).  A small bound makes the waits

@@ -305,6 +305,9 @@ def test_seqpar_workspace_bytes_and_validation(lib):
     assert call(0) == INV and call(65) == INV and call(3) == INV          # range, not dividing T
     assert call(4, qkv=kda.KDA_F32) == kda.KDA_ERR_UNSUPPORTED
     assert call(4, nbytes=1024) == INV                                     # short workspace
+    # the gate-logit form: a NULL A_log is an argument error before anything else
+    assert lib.kda_chunk_fwd_gate_seqpar(q, k, v, g, None, beta, None, o, None, ws, 1 << 30, 1, 256, 2, 128, 128, 4,
+                                         kda.KDA_BF16, kda.KDA_F32, kda.KDA_F32, None) == INV
 
 
 def test_seqpar_segment_choice(lib):

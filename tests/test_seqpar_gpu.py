@@ -159,3 +159,28 @@ def test_seqpar_without_final_state(kda, orc):
     assert S is None
     o_ref, _ = orc.fwd(*[x[n].f64() for n in ("q", "k", "v", "g", "beta")], x["S0"].f64())
     assert err_ratio(f64(o), o_ref) <= 2e-2
+
+
+GATE_CASES = [
+    (H8.scaled(H=2, T=1024, gate="bf16", name="gate_logits_bf16_T1024"), 8),
+    (H8.scaled(H=3, T=390, name="gate_logits_f32_T390_S0"), 5),
+    (T.scaled(B=2, H=2, T=256, dk=64, dv=128, name="gate_logits_dk64_T256"), 4),
+]
+
+
+@pytest.mark.parametrize("w,P", GATE_CASES, ids=[f"{w.name}_P{P}" for w, P in GATE_CASES])
+def test_seqpar_with_gate_logits(kda, orc, w, P):
+    """kda_chunk_fwd_gate_seqpar against the oracle's gate mapping followed by
+    its forward, as the plain gate-logit forward is checked."""
+    from oracle import gate_log_decay
+    x = gen.gate_logit_inputs(w)
+    d = {n: to_dev(x[n]) for n in x}
+    say(f"[seqpar gate] {w.name} B={w.B} T={w.T} H={w.H} dk={w.dk} gate={w.gate} segments={P}")
+    o, S = kda.kda_chunk_fwd_gate_seqpar(d["q"], d["k"], d["v"], d["z"], d["A_log"], d["beta"], d["S0"], segments=P)
+    torch.cuda.synchronize()
+    g = gate_log_decay(x["z"].f64(), x["A_log"].f64())
+    S0 = x["S0"].f64() if x["S0"] is not None else None
+    o_ref, S_ref = orc.fwd(x["q"].f64(), x["k"].f64(), x["v"].f64(), g, x["beta"].f64(), S0)
+    eo, es = err_ratio(f64(o), o_ref), err_ratio(f64(S), S_ref)
+    say(f"      err/rms  o={eo:.3e}  S={es:.3e}")
+    assert eo <= tau_for(w.qkv) and es <= tau_for(w.qkv), (eo, es)
