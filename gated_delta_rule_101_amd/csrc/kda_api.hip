@@ -304,7 +304,9 @@ int kda_chunk_fwd_seqpar_segments(int B, int T, int H, int dk, int dv, int cus)
     // (n + 1) x 5 us per round of workgroups (one workgroup per CU; the extra
     // period is the producers' head start) plus 3 us; the combine about
     // 6 + 1.9 P us; the three launches of the sequence-parallel call about
-    // 10 us more than one.
+    // 10 us more than one.  (The sequence-parallel first pass, which skips the
+    // query side, runs nearer 4.1 us per period; counting it so tips near
+    // ties the wrong way on the shapes measured, so both passes count 5.)
     const auto chunks = [](int t) { return (int64_t)(t + 63) / 64; };
     const auto pass = [cus](int64_t workgroups, int64_t n) {
         return (double)((workgroups + cus - 1) / cus) * (double)(n + 1) * 5.0 + 3.0;
