@@ -12,7 +12,8 @@ tokens, commit 8 of them) is reported under "speculative", the output
 epilogue (alone over the training-shape reads, and fused into decode) under
 "epilogue", the chunkwise backward under "backward", and two secondary
 forward workloads (one head group B1 H8 T4096, a latency figure; the long
-sequence B1 H96 T131072; the first also sequence-parallel) under
+sequence B1 H96 T131072, and one GPU's share of it under 8-way head sharding,
+B1 H12 T131072; the first and the third also sequence-parallel) under
 "forward_secondary", and the forward and decode with the log-decay formed
 in the kernel from gate logits under "gate_prologue".  Each carries a
 roofline object for its kernel, with the kernel's average duration measured
@@ -341,8 +342,10 @@ def bench_fwd_secondary(kda, w, steps, warmup):
     forward kernels are timed: the pipelined one (kda_chunk_fwd) and the ring
     one (kda_chunk_fwd_ws, its workspace allocated before timing), and, where
     the plain grid has at most 64 workgroups, the sequence-parallel forward
-    (kda_chunk_fwd_seqpar) at 4, 8 and 16 segments; the figures at the top of
-    the record are the fastest one's."""
+    (kda_chunk_fwd_seqpar) at 4, 8 and 16 segments and at the count
+    kda_chunk_fwd_seqpar_segments picks; the figures at the top of the record
+    are the fastest one's.  The third workload is one GPU's share of the long
+    sequence under 8-way head sharding (B1 H12 T131072)."""
     import torch
     from kda_workloads import gen_torch
     log(f"[bench] generating {w.name} on the device")
@@ -376,7 +379,8 @@ def bench_fwd_secondary(kda, w, steps, warmup):
     # sequence-parallel forward where the plain grid leaves most CUs idle
     # (the three launches of one call timed together)
     if w.B * w.H * (w.dv // 64) <= 64:
-        for P in (4, 8, 16):
+        picked = kda.kda_chunk_fwd_seqpar_segments(w.B, w.T, w.H, w.dk, w.dv)
+        for P in sorted({4, 8, 16, picked} - {1}):
             if w.T % P:
                 continue
             wsp = torch.empty(kda.kda_chunk_fwd_seqpar_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, P),
@@ -846,7 +850,8 @@ def main():
     if not args.no_decode:
         from kda_workloads import configs
         out["forward_secondary"] = [bench_fwd_secondary(kda, configs.HEADGROUP_BF16, 20, 3),
-                                    bench_fwd_secondary(kda, configs.LONG_BF16, 3, 1)]
+                                    bench_fwd_secondary(kda, configs.LONG_BF16, 3, 1),
+                                    bench_fwd_secondary(kda, configs.LONG_SHARE_BF16, 5, 1)]
         out["decode"] = bench_decode(kda, args.decode_reps)
         out["speculative"] = bench_speculative(kda, 10)
         out["epilogue"] = bench_epilogue(kda)

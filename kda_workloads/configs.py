@@ -91,6 +91,10 @@ LONG_BF16 = Workload(
     z_mu=0.0, z_sd=1.0, s0_sd=None,
 )
 
+# One GPU's share of LONG_BF16 under 8-way head sharding (12 of its 96 heads):
+# 24 workgroups of the plain forward for 256 CUs, the sequence-parallel case.
+LONG_SHARE_BF16 = LONG_BF16.scaled(H=12, name="kda_fwd_B1_H12_T131072_d128_bf16")
+
 # Batched single-token decode: 256 sequences x 96 heads of fp32 128x128 state.
 DECODE_BF16 = Workload(
     name="kda_decode_B256_H96_d128_bf16_x64", kind="decode",

@@ -184,3 +184,21 @@ def test_seqpar_with_gate_logits(kda, orc, w, P):
     eo, es = err_ratio(f64(o), o_ref), err_ratio(f64(S), S_ref)
     say(f"      err/rms  o={eo:.3e}  S={es:.3e}")
     assert eo <= tau_for(w.qkv) and es <= tau_for(w.qkv), (eo, es)
+
+
+def test_seqpar_long_sequence_share(kda, orc):
+    """One GPU's share of the long sequence under 8-way head sharding (B1 H12
+    T131072) at the library's segment count, the first and the last head
+    against the oracle over all 131072 tokens."""
+    w = configs.LONG_SHARE_BF16
+    P = kda.kda_chunk_fwd_seqpar_segments(w.B, w.T, w.H, w.dk, w.dv)
+    d = gen_torch.fwd_inputs(w)
+    say(f"[seqpar long share] {w.name} segments={P}")
+    o, S = kda.kda_chunk_fwd_seqpar(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], segments=P)
+    torch.cuda.synchronize()
+    heads = spread_heads(w.B, w.H, 2)
+    o_ref, S_ref = oracle_heads(orc, d, heads)
+    og, Sg = gpu_heads(o, S, heads)
+    eo, es = err_ratio(og, o_ref), err_ratio(Sg, S_ref)
+    say(f"      err/rms  o={eo:.3e}  S_final={es:.3e}")
+    assert P > 1 and eo <= 2e-2 and es <= 2e-2
