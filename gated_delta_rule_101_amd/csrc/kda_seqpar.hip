@@ -36,8 +36,23 @@ constexpr int CW = 4;     // state columns per combine workgroup
 // segments ahead into two register sets used in turn.  S sits in LDS,
 // double-buffered so that one barrier per segment separates the reads of S_p
 // from the writes of S_{p+1}, with one padding row per slice so that the
-// slices' reads of one instruction fall in distinct banks.  The slices are added by a reduce-scatter of cross-lane
-// shuffles, after which each lane holds 16 / KS of the block's sums.
+// slices' reads of one instruction fall in distinct banks.  The slices are
+// added by a reduce-scatter over DPP row patterns, after which each lane holds
+// 16 / KS of the block's sums.
+template <int L> struct Level { static constexpr int value = L; };
+
+// Reduce-scatter level k over the 16 lanes of a DPP row: lane x pairs with
+// x ^ 15 (row mirror), x ^ 7 within its half (half-row mirror), x ^ 1 or x ^ 2
+// (quad permutations).  The masks span the four slice bits, and the slice bit
+// that decides which half a lane keeps, {3, 2, 0, 1}, is one in which the pair
+// differs and which every later level's pairs share.
+constexpr int dpp_ctrl(int k) { return k == 0 ? 0x140 : k == 1 ? 0x141 : k == 2 ? 0xB1 : 0x4E; }
+constexpr int dpp_bit(int k) { return k == 0 ? 3 : k == 1 ? 2 : k == 2 ? 0 : 1; }
+template <int CTRL> __device__ __forceinline__ float dpp_from(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 template <int DK>
 __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restrict__ M, const float *__restrict__ N,
                                                             const float *S0, float *__restrict__ S_start,
@@ -50,6 +65,7 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
     constexpr int NOUT = 16 / KS;            // sums per lane after the reduce-scatter
     constexpr int SROWS = DK + KS;           // S rows in LDS, one padding row per slice
     static_assert(KS * R == CT && (1 << LOGKS) == KS && KL % 4 == 0 && NOUT >= 1 && DK * CW % CT == 0, "thread layout");
+    static_assert(LOGKS == 3 || LOGKS == 4, "the slices of a group lie in one 16-lane DPP row");
     __shared__ alignas(16) float sS[2][SROWS][CW];
     const int ncg = dv / CW;
     const int bh = blockIdx.x / ncg, j0 = (blockIdx.x % ncg) * CW;
@@ -59,14 +75,16 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
     auto seg = [&](int p) { return (size_t)(b * P + p) * H + h; };   // (sequence, head) of segment p
     auto srow = [](int k) { return k + k / KL; };                     // LDS row of state row k
 
-    // this lane's sums after the reduce-scatter: block index o = 8 b0 + 4 b1 + 2 b2 (+ b3) (+ j),
-    // b the lane's slice bits: row rg + R (o / 4), column o % 4
+    // this lane's sums after the reduce-scatter: level l fixes bit 3 - l of the
+    // block index o (row rg + R (o / 4), column o % 4) from slice bit
+    // dpp_bit(l + FIRST); the last 16 / KS bits of o are j
+    constexpr int FIRST = 4 - LOGKS;   // dk = 128 (8 slices) starts at the half-row mirror
     int out_row[NOUT], out_col[NOUT];
 #pragma unroll
     for (int j = 0; j < NOUT; ++j) {
         int o = 0;
 #pragma unroll
-        for (int L = 0; L < LOGKS; ++L) o |= ((slice >> L) & 1) << (3 - L);
+        for (int L = 0; L < LOGKS; ++L) o |= ((slice >> dpp_bit(L + FIRST)) & 1) << (3 - L);
         o |= j;
         out_row[j] = rg + R * (o / 4);
         out_col[j] = o % 4;
@@ -122,21 +140,23 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
 #pragma unroll
         for (int j = 0; j < NOUT; ++j) nn[j] = n[j];
         fetch(p + 2, m, n);
-        // reduce-scatter over the slice bits: at level L a lane keeps the half of
-        // its sums whose index bit 3 - L equals its slice bit L
-        int cnt = 16;
+        // reduce-scatter: at level L a lane keeps the half of its sums whose
+        // index bit 3 - L equals its slice bit dpp_bit(L + FIRST) and adds the
+        // partner's copy of that half
+        auto level = [&](auto lv) __attribute__((always_inline)) {
+            constexpr int L = decltype(lv)::value, K = L + FIRST, cnt = 8 >> L;
+            const bool hi = (slice >> dpp_bit(K)) & 1;
 #pragma unroll
-        for (int L = 0; L < LOGKS; ++L) {
-            const bool hi = (slice >> L) & 1;
-            cnt /= 2;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (j >= cnt) break;
+            for (int j = 0; j < cnt; ++j) {
                 const float send = hi ? acc[j] : acc[j + cnt];
                 const float keep = hi ? acc[j + cnt] : acc[j];
-                acc[j] = keep + __shfl_xor(send, 1 << L);
+                acc[j] = keep + dpp_from<dpp_ctrl(K)>(send);
             }
-        }
+        };
+        level(Level<0>{});
+        level(Level<1>{});
+        level(Level<2>{});
+        if constexpr (LOGKS == 4) level(Level<3>{});
         float *nxt = &sS[cur ^ 1][0][0];
 #pragma unroll
         for (int j = 0; j < NOUT; ++j) nxt[srow(out_row[j]) * CW + out_col[j]] = acc[j] + nn[j];
