@@ -24,13 +24,13 @@ namespace {
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int CT = 256;   // threads per combine workgroup
-constexpr int CW = 4;     // state columns per combine workgroup
+constexpr int CW_MIN = 4; // state columns per combine workgroup: 4, or 8 where 4 would overfill the device
 
-// One workgroup per (b, h, 4 state columns): S <- S0 (or 0); for each segment
+// One workgroup per (b, h, CW state columns): S <- S0 (or 0); for each segment
 // p, S_start[p] = S and S <- M_p S + N_p; S_final <- S.  fp32 throughout.
 //
-// Thread (slice, rg) computes a 4 x 4 block of each product -- rows rg + R i
-// (R = DK / 4, i = 0..3), all four columns -- over one of KS slices of KL
+// Thread (slice, rg) computes a 4 x CW block of each product -- rows rg + R i
+// (R = DK / 4, i = 0..3), all CW columns -- over one of KS slices of KL
 // inner indices (lane bits 0 .. log2 KS - 1 are the slice).  Its M_p entries
 // (4 rows x KL) come straight from global memory into registers, loaded two
 // segments ahead into two register sets used in turn.  S sits in LDS,
@@ -38,7 +38,7 @@ constexpr int CW = 4;     // state columns per combine workgroup
 // from the writes of S_{p+1}, with one padding row per slice so that the
 // slices' reads of one instruction fall in distinct banks.  The slices are
 // added by a reduce-scatter over DPP row patterns, after which each lane holds
-// 16 / KS of the block's sums.
+// 4 CW / KS of the block's sums.
 template <int L> struct Level { static constexpr int value = L; };
 
 // Reduce-scatter level k over the 16 lanes of a DPP row: lane x pairs with
@@ -53,7 +53,7 @@ template <int CTRL> __device__ __forceinline__ float dpp_from(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-template <int DK>
+template <int DK, int CW>
 __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restrict__ M, const float *__restrict__ N,
                                                             const float *S0, float *__restrict__ S_start,
                                                             float *S_final, int H, int P, int dv)
@@ -62,9 +62,12 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
     constexpr int KS = CT / R;               // slices of the inner index
     constexpr int KL = DK / KS;              // inner indices per slice
     constexpr int LOGKS = KS == 8 ? 3 : 4;
-    constexpr int NOUT = 16 / KS;            // sums per lane after the reduce-scatter
+    constexpr int NACC = 4 * CW;             // sums per thread before the reduce-scatter
+    constexpr int LOGO = CW == 4 ? 4 : 5;    // bits of a block index
+    constexpr int NOUT = NACC / KS;          // sums per lane after it
     constexpr int SROWS = DK + KS;           // S rows in LDS, one padding row per slice
-    static_assert(KS * R == CT && (1 << LOGKS) == KS && KL % 4 == 0 && NOUT >= 1 && DK * CW % CT == 0, "thread layout");
+    static_assert(KS * R == CT && (1 << LOGKS) == KS && KL % 4 == 0 && NOUT >= 1 && DK * CW % CT == 0 &&
+                  (1 << LOGO) == NACC, "thread layout");
     static_assert(LOGKS == 3 || LOGKS == 4, "the slices of a group lie in one 16-lane DPP row");
     __shared__ alignas(16) float sS[2][SROWS][CW];
     const int ncg = dv / CW;
@@ -75,19 +78,19 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
     auto seg = [&](int p) { return (size_t)(b * P + p) * H + h; };   // (sequence, head) of segment p
     auto srow = [](int k) { return k + k / KL; };                     // LDS row of state row k
 
-    // this lane's sums after the reduce-scatter: level l fixes bit 3 - l of the
-    // block index o (row rg + R (o / 4), column o % 4) from slice bit
-    // dpp_bit(l + FIRST); the last 16 / KS bits of o are j
+    // this lane's sums after the reduce-scatter: level l fixes bit LOGO - 1 - l
+    // of the block index o (row rg + R (o / CW), column o % CW) from slice bit
+    // dpp_bit(l + FIRST); the remaining low bits of o are j
     constexpr int FIRST = 4 - LOGKS;   // dk = 128 (8 slices) starts at the half-row mirror
     int out_row[NOUT], out_col[NOUT];
 #pragma unroll
     for (int j = 0; j < NOUT; ++j) {
         int o = 0;
 #pragma unroll
-        for (int L = 0; L < LOGKS; ++L) o |= ((slice >> dpp_bit(L + FIRST)) & 1) << (3 - L);
+        for (int L = 0; L < LOGKS; ++L) o |= ((slice >> dpp_bit(L + FIRST)) & 1) << (LOGO - 1 - L);
         o |= j;
-        out_row[j] = rg + R * (o / 4);
-        out_col[j] = o % 4;
+        out_row[j] = rg + R * (o / CW);
+        out_col[j] = o % CW;
     }
 
     f32x4v mx[4][KL / 4], my[4][KL / 4];
@@ -122,18 +125,22 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
             const int e = tid + CT * u, r = e / CW, j = e % CW;
             S_start[(seg(p) * DK + r) * dv + j0 + j] = sS[cur][srow(r)][j];
         }
-        float acc[16];
+        float acc[NACC];
 #pragma unroll
-        for (int o = 0; o < 16; ++o) acc[o] = 0.f;
+        for (int o = 0; o < NACC; ++o) acc[o] = 0.f;
 #pragma unroll
         for (int u = 0; u < KL / 4; ++u) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const f32x4v s4 = *reinterpret_cast<const f32x4v *>(&sS[cur][srow(KL * slice + 4 * u + kk)][0]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int c4 = 0; c4 < CW / 4; ++c4) {
+                    const f32x4v s4 = *reinterpret_cast<const f32x4v *>(&sS[cur][srow(KL * slice + 4 * u + kk)][4 * c4]);
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[4 * i + c] = fmaf(m[i][u][kk], s4[c], acc[4 * i + c]);
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            acc[CW * i + 4 * c4 + c] = fmaf(m[i][u][kk], s4[c], acc[CW * i + 4 * c4 + c]);
+                }
             }
         }
         float nn[NOUT];
@@ -141,10 +148,10 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
         for (int j = 0; j < NOUT; ++j) nn[j] = n[j];
         fetch(p + 2, m, n);
         // reduce-scatter: at level L a lane keeps the half of its sums whose
-        // index bit 3 - L equals its slice bit dpp_bit(L + FIRST) and adds the
-        // partner's copy of that half
+        // index bit LOGO - 1 - L equals its slice bit dpp_bit(L + FIRST) and
+        // adds the partner's copy of that half
         auto level = [&](auto lv) __attribute__((always_inline)) {
-            constexpr int L = decltype(lv)::value, K = L + FIRST, cnt = 8 >> L;
+            constexpr int L = decltype(lv)::value, K = L + FIRST, cnt = (NACC / 2) >> L;
             const bool hi = (slice >> dpp_bit(K)) & 1;
 #pragma unroll
             for (int j = 0; j < cnt; ++j) {
@@ -173,12 +180,18 @@ __global__ void __launch_bounds__(CT) seqpar_combine_kernel(const float *__restr
         }
 }
 
+// 8 columns per workgroup where 4 would give more workgroups than the device
+// has compute units: the workgroups of a head each read all of M_p, so fewer of
+// them read less of it
 template <int DK>
 void launch_combine(const float *M, const float *N, const float *S0, float *S_start, float *S_final, int B, int H,
-                    int P, int dv, hipStream_t stream)
+                    int P, int dv, int cus, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)((size_t)B * H * (dv / CW));
-    seqpar_combine_kernel<DK><<<grid, CT, 0, stream>>>(M, N, S0, S_start, S_final, H, P, dv);
+    const size_t groups4 = (size_t)B * H * (dv / 4);
+    if (dv % 8 == 0 && groups4 > (size_t)cus)
+        seqpar_combine_kernel<DK, 8><<<(unsigned)(groups4 / 2), CT, 0, stream>>>(M, N, S0, S_start, S_final, H, P, dv);
+    else
+        seqpar_combine_kernel<DK, 4><<<(unsigned)groups4, CT, 0, stream>>>(M, N, S0, S_start, S_final, H, P, dv);
 }
 
 }  // namespace
@@ -192,7 +205,11 @@ size_t chunk_seqpar_workspace_bytes(int B, int H, int dk, int dv, int P)
 hipError_t launch_chunk_fwd_seqpar(const ChunkFwdArgs &a, int P, void *workspace, hipStream_t stream)
 {
     (void)hipGetLastError();
-    if (P < 1 || a.T % P != 0 || !a.qkv_bf16 || a.lengths || a.dv % CW) return hipErrorInvalidValue;
+    if (P < 1 || a.T % P != 0 || !a.qkv_bf16 || a.lengths || a.dv % CW_MIN) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
     const size_t n = (size_t)a.B * P * a.H;
     float *N = static_cast<float *>(workspace);
     float *M = N + n * a.dk * a.dv;
@@ -205,14 +222,14 @@ hipError_t launch_chunk_fwd_seqpar(const ChunkFwdArgs &a, int P, void *workspace
     e.S0 = nullptr;
     e.o = nullptr;
     e.S_final = N;
-    hipError_t err = launch_chunk_fwd_bf16_trans(e, M, stream);
+    err = launch_chunk_fwd_bf16_trans(e, M, stream);
     if (err != hipSuccess) return err;
 
     // 2. the segments' starting states and the final state
     if (a.dk == 64)
-        launch_combine<64>(M, N, a.S0, S_start, a.S_final, a.B, a.H, P, a.dv, stream);
+        launch_combine<64>(M, N, a.S0, S_start, a.S_final, a.B, a.H, P, a.dv, cus, stream);
     else
-        launch_combine<128>(M, N, a.S0, S_start, a.S_final, a.B, a.H, P, a.dv, stream);
+        launch_combine<128>(M, N, a.S0, S_start, a.S_final, a.B, a.H, P, a.dv, cus, stream);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
 
